@@ -1,0 +1,20 @@
+"""Oracle -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct CPU reference for small-window paged attention.
+Only `tests/`, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code, header, table or constant generator with the
+HIP library and never imports it.
+
+  attention.c   fp64 attention over the gathered pages (C, OpenMP)
+  _lib.py       builds and loads attention.c through ctypes
+  ref.py        the split planner restated from its written specification,
+                the log-sum-exp combine, the per-unit page gather and the
+                closed-form work and byte counts
+"""
+from ._lib import attention, decode_bf16, decode_e4m3, build_oracle, oracle_threads
+from .ref import (PLAN_MIN_PAGES, attention_pairs, gather_unit_pages, kv_bytes, lse_combine,
+                  plan, plan_export, split_pages)
+
+__all__ = ["attention", "decode_bf16", "decode_e4m3", "build_oracle", "oracle_threads",
+           "PLAN_MIN_PAGES", "attention_pairs", "gather_unit_pages", "kv_bytes", "lse_combine",
+           "plan", "plan_export", "split_pages"]

@@ -1,0 +1,139 @@
+"""Oracle (test infrastructure only): integer planning, page gather, combine, counts.
+
+Everything here is restated from written definitions, in plain Python/numpy:
+
+* The split planner follows the library's written planner specification
+  (the pages give no split formula; key splitting and its reduce kernel are
+  only named in "ChunkedSmallT re-streams full KV per query chunk", section
+  Finding).  It is an independent restatement, never a call into the library.
+* The log-sum-exp combine is the exact merge of softmax partials over disjoint
+  key ranges (the "reduce kernel" of the same section).
+* kv_bytes follows the same page's section Measurement: GB/s there is the KV
+  bytes of one sweep over the visible context divided by the call time.
+* attention_pairs follows "DFlash2 leaves the paged graph fast path ...",
+  section The cost (its work-per-draft-step table).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PAGE = 16
+PLAN_MIN_PAGES = 8          # a split never holds fewer pages than this (auto mode)
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None):
+    """Split plan for one call.
+
+    n_pg(p)     = ceil(L_p / 16)
+    slots       = num_cus * (1 if a K page-head (16*D*elt bytes) >= 8 KiB else 2)
+    total       = Hkv * sum_p n_pg(p)
+    ppu         = max(8, ceil(total / slots))          pages per split
+    S_p         = 1                         if n_pg(p) == 0
+                = min(force_splits, n_pg)   if force_splits > 0
+                = ceil(n_pg(p) / ppu)       otherwise
+    unit_off[p] = Hkv * sum_{q<p} S_q;  unit u = unit_off[p] + kvh*S_p + s
+    split s covers logical pages [floor(s*n/S), floor((s+1)*n/S))
+    """
+    seq = [int(x) for x in seq_lens]
+    assert len(seq) == P
+    elt = 1 if kv_fp8 else 2
+    n_pg = [_ceil_div(L, PAGE) for L in seq]
+    slots = num_cus * (1 if PAGE * D * elt >= 8192 else 2)
+    total = Hkv * sum(n_pg)
+    ppu = max(PLAN_MIN_PAGES, _ceil_div(total, slots))
+    splits = []
+    for n in n_pg:
+        if n == 0:
+            splits.append(1)
+        elif force_splits > 0:
+            splits.append(min(force_splits, n))
+        else:
+            splits.append(_ceil_div(n, ppu))
+    unit_off = [0]
+    for s in splits:
+        unit_off.append(unit_off[-1] + Hkv * s)
+    units = []
+    for p in range(P):
+        S, n = splits[p], n_pg[p]
+        for kvh in range(Hkv):
+            for s in range(S):
+                pb, pe = split_pages(n, S, s)
+                units.append((p, kvh, s, pb, pe))
+    return {"P": P, "Hkv": Hkv, "n_pg": n_pg, "splits": splits, "unit_off": unit_off,
+            "units": units, "U": unit_off[-1], "any_split": any(s > 1 for s in splits)}
+
+
+def split_pages(n: int, S: int, s: int):
+    return (s * n) // S, ((s + 1) * n) // S
+
+
+def plan_export(pl, R: int) -> np.ndarray:
+    """Integer export layout: [P, Hkv, U, R] + S_p[P] + unit_off[P+1] + U*(p,kvh,s,pb,pe)."""
+    head = [pl["P"], pl["Hkv"], pl["U"], R]
+    flat = head + list(pl["splits"]) + list(pl["unit_off"])
+    for u in pl["units"]:
+        flat.extend(u)
+    return np.asarray(flat, dtype=np.int32)
+
+
+def gather_unit_pages(pl, block_table: np.ndarray) -> list[list[int]]:
+    """Physical page ids each work unit streams, in logical order."""
+    out = []
+    for (p, _kvh, _s, pb, pe) in pl["units"]:
+        out.append([int(block_table[p, n]) for n in range(pb, pe)])
+    return out
+
+
+def lse_combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge partials over disjoint key ranges.
+
+    o_parts [S][..., D] (each normalised by its own sum), lse_parts [S][...].
+    M = max_s lse_s; lse = M + ln sum_s exp(lse_s - M); o = sum_s exp(lse_s - lse) o_s.
+    A part with lse_s = -inf has weight 0; all parts -inf gives o = 0, lse = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    M = lse_parts.max(axis=0)
+    Ms = np.where(np.isfinite(M), M, 0.0)
+    w = np.exp(lse_parts - Ms)                      # exp(-inf) = 0
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(tot > 0, Ms + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    wn = np.where(tot > 0, w / np.where(tot > 0, tot, 1.0), 0.0)
+    o = (wn[..., None] * o_parts).sum(axis=0)
+    return o, lse
+
+
+def kv_bytes(seq_lens, Hkv: int, D: int, kv_fp8: bool = False) -> int:
+    """Bytes of one sweep over every visible K and V element (plus fp8 scales)."""
+    tokens = int(sum(int(L) for L in seq_lens))
+    elt = 1 if kv_fp8 else 2
+    per_token_head = 2 * D * elt + (2 * 4 if kv_fp8 else 0)
+    return tokens * Hkv * per_token_head
+
+
+def attention_pairs(seq_lens, W: int, Hq: int, causal: bool) -> int:
+    """(query row, key) pairs the exact method scores: sum over rows of visible keys."""
+    total = 0
+    for L in seq_lens:
+        L = int(L)
+        for i in range(W):
+            n = (L - W + i + 1) if causal else L
+            total += max(n, 0)
+    return total * Hq
+
+
+def materialised_pairs(ctxs, k: int) -> int:
+    """Pairs of the fallback that attends every context row too: sum_r (ctx_r+1+k)^2."""
+    return sum((int(c) + 1 + k) ** 2 for c in ctxs)
+
+
+def paged_pairs(ctxs, k: int) -> int:
+    """Pairs of the block-only route: (1+k) * C, C = sum of contexts."""
+    return (1 + k) * sum(int(c) for c in ctxs)

@@ -1,0 +1,401 @@
+"""Pins for the oracle: each test ties it to something other than itself.
+
+* brute force: a dense numpy/torch formulation (vectorised gather, torch's own
+  bf16 / float8_e4m3fn decoders, an explicit mask matrix) and torch's
+  scaled_dot_product_attention in float64;
+* closed forms (Q = 0, equal keys, constant V, one key, W = 1);
+* invariants (window split, page relabelling, GQA = replicated MHA, batch =
+  singles, NaN poison, split partials + log-sum-exp combine);
+* format tables (all bf16 and e4m3fn codes against torch);
+* numbers the pages print (tests/golden/).
+"""
+import dataclasses
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_workload, to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(P=1, Hq=4, Hkv=2, D=8, ctx=(20,), W=3, causal=True, kv="bf16", seed=1, pool=None,
+         poison=True, **kw):
+    npg = sum(math.ceil((c + W) / 16) for c in ctx)
+    return make_workload(None, P=P, Hq=Hq, Hkv=Hkv, D=D, ctx=tuple(ctx), W=W, causal=causal,
+                         kv=kv, placement="permuted", pool_pages=pool or npg + 5, seed=seed,
+                         poison=poison, **kw)
+
+
+# ---------------------------------------------------------------- brute force
+def dense_kv(w):
+    """Dense K, V [P][Hkv][Lmax][D] in float64 via vectorised gather + torch decoders."""
+    Lmax = max(1, int(w.seq_lens.max()))
+    K = np.zeros((w.P, w.Hkv, Lmax, w.D))
+    V = np.zeros((w.P, w.Hkv, Lmax, w.D))
+    for p in range(w.P):
+        L = int(w.seq_lens[p])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        phys = w.block_table[p, t // 16]
+        slot = t % 16
+        kc = w.k_pool[phys, :, slot, :]                  # [L][Hkv][D]
+        vc = w.v_pool[phys, :, :, slot]                  # [L][Hkv][D]
+        if w.kv == "fp8":
+            kd = torch.from_numpy(np.ascontiguousarray(kc)).view(torch.float8_e4m3fn).double()
+            vd = torch.from_numpy(np.ascontiguousarray(vc)).view(torch.float8_e4m3fn).double()
+            kd = kd * torch.from_numpy(w.k_scale[phys, :, slot]).double()[..., None]
+            vd = vd * torch.from_numpy(w.v_scale[phys, :, slot]).double()[..., None]
+        else:
+            kd = torch.from_numpy(np.ascontiguousarray(kc).view(np.int16)).view(torch.bfloat16).double()
+            vd = torch.from_numpy(np.ascontiguousarray(vc).view(np.int16)).view(torch.bfloat16).double()
+        K[p, :, :L] = kd.numpy().transpose(1, 0, 2)
+        V[p, :, :L] = vd.numpy().transpose(1, 0, 2)
+    return K, V
+
+
+def q_f64(w):
+    return torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def mask_matrix(L, W, causal, Lmax):
+    i = np.arange(W)[:, None]
+    j = np.arange(Lmax)[None, :]
+    vis = np.broadcast_to(j < L, (W, Lmax))
+    if causal:
+        vis = vis & (j <= (L - W + i))
+    return vis
+
+
+def brute(w):
+    K, V = dense_kv(w)
+    Q = q_f64(w)
+    G = w.G
+    Lmax = K.shape[2]
+    out = np.zeros((w.P, w.W, w.Hq, w.D))
+    lse = np.full((w.P, w.W, w.Hq), -np.inf)
+    for p in range(w.P):
+        M = mask_matrix(int(w.seq_lens[p]), w.W, w.causal, Lmax)
+        for h in range(w.Hq):
+            S = (Q[p, :, h, :] @ K[p, h // G].T) * w.scale      # [W][Lmax]
+            S = np.where(M, S, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            ok = np.isfinite(m[:, 0])
+            E = np.where(M, np.exp(S - np.where(np.isfinite(m), m, 0.0)), 0.0)
+            l = E.sum(axis=1)
+            out[p, ok, h] = (E[ok] @ V[p, h // G]) / l[ok, None]
+            lse[p, ok, h] = m[ok, 0] + np.log(l[ok])
+    return out, lse
+
+
+CASES = [
+    dict(P=1, Hq=4, Hkv=1, D=64, ctx=(256,), W=4, causal=True),            # the tiny config
+    dict(P=3, Hq=4, Hkv=2, D=8, ctx=(5, 40, 66), W=5, causal=True),
+    dict(P=2, Hq=6, Hkv=3, D=16, ctx=(1, 33), W=2, causal=False),
+    dict(P=2, Hq=4, Hkv=4, D=8, ctx=(15, 16), W=1, causal=True),
+    dict(P=1, Hq=12, Hkv=2, D=64, ctx=(300,), W=16, causal=True),
+    dict(P=2, Hq=4, Hkv=1, D=8, ctx=(17, 31), W=3, causal=True, kv="fp8"),
+    dict(P=2, Hq=8, Hkv=2, D=16, ctx=(50, 9), W=4, causal=False, kv="fp8"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_oracle_matches_dense_brute_force(case):
+    w = tiny(seed=10 + case, **CASES[case])
+    o, l = oracle.attention(w)
+    ob, lb = brute(w)
+    assert np.isfinite(o).all()
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_oracle_matches_torch_sdpa_fp64(case):
+    w = tiny(seed=20 + case, **CASES[case])
+    o, _ = oracle.attention(w)
+    K, V = dense_kv(w)
+    Q = q_f64(w)
+    for p in range(w.P):
+        L = int(w.seq_lens[p])
+        M = torch.from_numpy(mask_matrix(L, w.W, w.causal, K.shape[2]))
+        kk = torch.from_numpy(K[p]).repeat_interleave(w.G, dim=0)[None]     # [1][Hq][L][D]
+        vv = torch.from_numpy(V[p]).repeat_interleave(w.G, dim=0)[None]
+        qq = torch.from_numpy(Q[p]).permute(1, 0, 2)[None]                   # [1][Hq][W][D]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk, vv, attn_mask=M, scale=w.scale)[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(o[p], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_zero_query_gives_log_count_and_mean_value():
+    w = tiny(P=2, Hq=4, Hkv=2, D=16, ctx=(29, 70), W=6, causal=True, seed=3)
+    w.q[...] = 0
+    o, l = oracle.attention(w)
+    _, V = dense_kv(w)
+    for p in range(w.P):
+        L = int(w.seq_lens[p])
+        for i in range(w.W):
+            n = L - w.W + i + 1
+            np.testing.assert_allclose(l[p, i], math.log(n), rtol=0, atol=1e-13)
+            for h in range(w.Hq):
+                np.testing.assert_allclose(o[p, i, h], V[p, h // w.G, :n].mean(axis=0),
+                                           rtol=0, atol=1e-13)
+
+
+def test_equal_keys_give_uniform_weights():
+    w = tiny(P=1, Hq=2, Hkv=1, D=8, ctx=(40,), W=3, causal=True, seed=4)
+    key = to_bf16_bits(np.linspace(-1, 1, 8, dtype=np.float32))
+    for n in range(math.ceil(int(w.seq_lens[0]) / 16)):
+        w.k_pool[w.block_table[0, n], 0, :, :] = key
+    o, l = oracle.attention(w)
+    K, V = dense_kv(w)
+    Q = q_f64(w)
+    for i in range(w.W):
+        n = int(w.seq_lens[0]) - w.W + i + 1
+        for h in range(w.Hq):
+            s = w.scale * float(Q[0, i, h] @ K[0, 0, 0])
+            assert abs(l[0, i, h] - (s + math.log(n))) < 1e-12
+            np.testing.assert_allclose(o[0, i, h], V[0, 0, :n].mean(axis=0), atol=1e-13)
+
+
+def test_constant_value_rows_return_the_constant():
+    w = tiny(P=2, Hq=4, Hkv=2, D=8, ctx=(21, 50), W=4, causal=False, seed=5)
+    c = 0.375
+    w.v_pool[...] = to_bf16_bits(np.float32(c))
+    o, _ = oracle.attention(w)
+    np.testing.assert_allclose(o, c, rtol=0, atol=1e-15)
+
+
+def test_single_key_returns_its_value_and_score():
+    w = tiny(P=1, Hq=2, Hkv=1, D=8, ctx=(0,), W=1, causal=False, seed=6)
+    o, l = oracle.attention(w)
+    K, V = dense_kv(w)
+    Q = q_f64(w)
+    for h in range(2):
+        np.testing.assert_array_equal(o[0, 0, h], V[0, 0, 0])
+        assert abs(l[0, 0, h] - w.scale * float(Q[0, 0, h] @ K[0, 0, 0])) < 1e-14
+
+
+def test_one_row_causal_equals_non_causal():
+    w = tiny(P=2, Hq=4, Hkv=2, D=8, ctx=(10, 45), W=1, causal=True, seed=7)
+    a = oracle.attention(w)
+    b = oracle.attention(dataclasses.replace(w, causal=False))
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_empty_request_gives_zero_and_minus_inf():
+    w = tiny(P=3, Hq=2, Hkv=1, D=8, ctx=(10, 0, 20), W=2, causal=True, seed=8,
+             seq_lens=(12, 0, 22))
+    o, l = oracle.attention(w)
+    assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
+    ob, lb = brute(w)
+    np.testing.assert_allclose(o, ob, atol=1e-12)
+    np.testing.assert_allclose(l[[0, 2]], lb[[0, 2]], atol=1e-12)
+
+
+def test_causal_shorter_than_window_is_rejected():
+    w = tiny(P=1, Hq=2, Hkv=1, D=8, ctx=(5,), W=4, causal=True, seq_lens=(3,))
+    with pytest.raises(ValueError):
+        oracle.attention(w)
+
+
+# ---------------------------------------------------------------- invariants
+def test_window_rows_equal_single_row_calls():
+    w = tiny(P=2, Hq=6, Hkv=2, D=16, ctx=(37, 80), W=7, causal=True, seed=11)
+    o, l = oracle.attention(w)
+    for i in range(w.W):
+        one = dataclasses.replace(w, W=1, q=np.ascontiguousarray(w.q[:, i:i + 1]),
+                                  seq_lens=(w.seq_lens - w.W + i + 1).astype(np.int32))
+        o1, l1 = oracle.attention(one)
+        np.testing.assert_array_equal(o[:, i], o1[:, 0])
+        np.testing.assert_array_equal(l[:, i], l1[:, 0])
+
+
+def test_sixteen_rows_equal_two_eight_row_calls():
+    w = tiny(P=1, Hq=4, Hkv=1, D=8, ctx=(100,), W=16, causal=True, seed=12)
+    o, l = oracle.attention(w)
+    lo = dataclasses.replace(w, W=8, q=np.ascontiguousarray(w.q[:, :8]),
+                             seq_lens=(w.seq_lens - 8).astype(np.int32))
+    hi = dataclasses.replace(w, W=8, q=np.ascontiguousarray(w.q[:, 8:]))
+    np.testing.assert_array_equal(o[:, :8], oracle.attention(lo)[0])
+    np.testing.assert_array_equal(o[:, 8:], oracle.attention(hi)[0])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_page_relabelling_is_bitwise_invariant(kv):
+    w = tiny(P=2, Hq=4, Hkv=2, D=16, ctx=(50, 77), W=5, causal=True, kv=kv, seed=13, pool=20)
+    perm = np.random.default_rng(0).permutation(w.num_pages)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(w.num_pages)
+    w2 = dataclasses.replace(
+        w, k_pool=np.ascontiguousarray(w.k_pool[inv]), v_pool=np.ascontiguousarray(w.v_pool[inv]),
+        k_scale=None if w.k_scale is None else np.ascontiguousarray(w.k_scale[inv]),
+        v_scale=None if w.v_scale is None else np.ascontiguousarray(w.v_scale[inv]),
+        block_table=np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1)
+        .astype(np.int32))
+    a, b = oracle.attention(w), oracle.attention(w2)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_gqa_equals_replicated_mha():
+    w = tiny(P=2, Hq=6, Hkv=2, D=8, ctx=(30, 47), W=3, causal=True, seed=14)
+    rep = np.repeat(np.arange(w.Hkv), w.G)
+    w2 = dataclasses.replace(w, Hkv=w.Hq, k_pool=np.ascontiguousarray(w.k_pool[:, rep]),
+                             v_pool=np.ascontiguousarray(w.v_pool[:, rep]))
+    a, b = oracle.attention(w), oracle.attention(w2)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_batch_equals_single_requests():
+    w = tiny(P=3, Hq=4, Hkv=2, D=8, ctx=(12, 60, 33), W=4, causal=False, seed=15)
+    o, l = oracle.attention(w)
+    for p in range(w.P):
+        one = dataclasses.replace(w, P=1, q=np.ascontiguousarray(w.q[p:p + 1]),
+                                  block_table=np.ascontiguousarray(w.block_table[p:p + 1]),
+                                  seq_lens=np.ascontiguousarray(w.seq_lens[p:p + 1]))
+        o1, l1 = oracle.attention(one)
+        np.testing.assert_array_equal(o[p], o1[0])
+        np.testing.assert_array_equal(l[p], l1[0])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_nan_in_stale_slots_and_free_pages_is_never_read(kv):
+    a = tiny(P=2, Hq=4, Hkv=2, D=8, ctx=(19, 42), W=3, kv=kv, seed=16, poison=True, pool=12)
+    b = tiny(P=2, Hq=4, Hkv=2, D=8, ctx=(19, 42), W=3, kv=kv, seed=16, poison=False, pool=12)
+    assert np.isnan(oracle.decode_bf16(a.k_pool)).any() if kv == "bf16" else True
+    oa, la = oracle.attention(a)
+    ob, lb = oracle.attention(b)
+    assert np.isfinite(oa).all() and np.isfinite(la).all()
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+@pytest.mark.parametrize("force", [1, 2, 3, 7, 0])
+def test_split_partials_combine_to_the_full_result(force):
+    w = tiny(P=1, Hq=4, Hkv=2, D=16, ctx=(200,), W=6, causal=True, seed=17)
+    n = math.ceil(int(w.seq_lens[0]) / 16)
+    pl = oracle.plan(P=1, Hkv=w.Hkv, D=w.D, kv_fp8=False, seq_lens=w.seq_lens, num_cus=1,
+                     force_splits=force or n)
+    o, l = oracle.attention(w)
+    S = pl["splits"][0]
+    parts_o, parts_l = [], []
+    for s in range(S):
+        pb, pe = oracle.split_pages(n, S, s)
+        po, plse = oracle.attention(w, key_lo=pb * 16, key_hi=pe * 16)
+        parts_o.append(po)
+        parts_l.append(plse)
+    co, cl = oracle.lse_combine(np.stack(parts_o), np.stack(parts_l))
+    np.testing.assert_allclose(co, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(cl, l, rtol=1e-13, atol=1e-12)
+
+
+def test_sampled_rows_equal_full_rows():
+    w = tiny(P=2, Hq=6, Hkv=3, D=16, ctx=(40, 90), W=5, causal=True, seed=18)
+    o, l = oracle.attention(w)
+    rows = np.array([[0, 0, 0], [1, 4, 5], [1, 2, 3], [0, 3, 1]])
+    os_, ls_ = oracle.attention(w, rows=rows)
+    for k, (p, i, h) in enumerate(rows):
+        np.testing.assert_array_equal(os_[k], o[p, i, h])
+        assert ls_[k] == l[p, i, h]
+
+
+# ---------------------------------------------------------------- formats
+def test_bf16_decode_matches_torch_for_every_code():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.decode_bf16(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    mine = oracle.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(mine), nan)
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+    assert np.nanmax(mine) == 448.0 and mine[1] == 2.0 ** -9
+
+
+# ---------------------------------------------------------------- counts and the pages' numbers
+def test_attention_pairs_equal_mask_population():
+    for L, W, causal in [(260, 4, True), (9, 9, True), (1309, 9, False), (70, 16, True)]:
+        M = mask_matrix(L, W, causal, L)
+        assert oracle.attention_pairs([L], W, 3, causal) == 3 * int(M.sum())
+    # closed forms: causal H*(W*L - W(W-1)/2), non-causal H*W*L
+    assert oracle.attention_pairs([100, 50], 5, 2, True) == 2 * (5 * 150 - 2 * 10)
+    assert oracle.attention_pairs([100, 50], 5, 2, False) == 2 * 5 * 150
+
+
+def _rows(fname):
+    rows = []
+    for line in open(os.path.join(GOLDEN, fname)):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append([float(x) for x in line.split()])
+    return rows
+
+
+def test_kv_byte_count_reproduces_the_pages_bandwidth_figures():
+    for ctx, _W, us, gbps in _rows("p1_measurement.txt"):
+        b = oracle.kv_bytes([int(ctx)], Hkv=4, D=256)
+        assert abs(b / (us * 1e-6) / 1e9 - gbps) / gbps < 0.005
+
+
+def test_draft_work_blowup_matches_the_pages_ratio():
+    for ctx, k, ratio, tol in _rows("p2_work.txt"):
+        from oracle.ref import materialised_pairs, paged_pairs
+        r = materialised_pairs([int(ctx)], int(k)) / paged_pairs([int(ctx)], int(k))
+        assert abs(r - ratio) / ratio < tol
+
+
+# ---------------------------------------------------------------- planner specification
+def test_plan_partitions_every_request_into_balanced_splits():
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        P = int(rng.integers(1, 9))
+        seq = [int(x) for x in rng.integers(0, 5000, size=P)]
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128, 256]))
+        fp8 = bool(rng.integers(0, 2))
+        force = int(rng.choice([0, 0, 1, 3, 50]))
+        pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=fp8, seq_lens=seq, num_cus=256,
+                         force_splits=force)
+        assert pl["U"] == Hkv * sum(pl["splits"]) == len(pl["units"])
+        k = 0
+        for p in range(P):
+            n, S = pl["n_pg"][p], pl["splits"][p]
+            assert n == math.ceil(seq[p] / 16)
+            assert 1 <= S <= max(n, 1)
+            for kvh in range(Hkv):
+                edge = 0
+                for s in range(S):
+                    up, ukvh, us, pb, pe = pl["units"][k]
+                    assert (up, ukvh, us) == (p, kvh, s) and pb == edge
+                    assert n // S <= pe - pb <= -(-n // S)
+                    edge = pe
+                    k += 1
+                assert edge == n
+
+
+def test_plan_at_the_long_context_shapes():
+    # 64K verify: total = 4*4097 = 16388 page-heads, 256 slots -> 65 pages per
+    # split -> S = ceil(4097/65) = 64 -> 256 units, one per compute unit.
+    pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[65552], num_cus=256)
+    assert pl["splits"] == [64] and pl["U"] == 256
+    # 16K verify: 4*1025 = 4100 -> 17 pages per split -> S = ceil(1025/17) = 61
+    pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[16400], num_cus=256)
+    assert pl["splits"] == [61]
+    # tiny: 17 pages, one head -> the 8-page floor -> S = 3
+    pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256)
+    assert pl["splits"] == [3] and [u[3:] for u in pl["units"]] == [(0, 5), (5, 11), (11, 17)]
