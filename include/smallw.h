@@ -1,0 +1,187 @@
+/*
+ * smallw.h -- small-window paged attention for speculative-decoding verify and
+ * draft blocks on AMD Instinct MI355X (gfx950).
+ *
+ * One call computes softmax attention for a window of W = 1..16 query rows per
+ * request against that request's paged KV cache, for P requests at once, and
+ * reads every visible K/V byte once for all W rows and all query heads of a
+ * KV group.
+ *
+ * Where the operation is defined:
+ *  - "ChunkedSmallT re-streams full KV per query chunk (DFlash K>=8 verify at
+ *    long context)", section Finding: the W = K+1 verify rows of a speculative
+ *    step attend the visible key range; key splitting plus a reduce step merge
+ *    the partial results.  Section Measurement: the call is timed per layer on
+ *    a cold cache and its bandwidth is the KV bytes of one sweep / time.
+ *  - "DFlash2 leaves the paged graph fast path at every c>1 ...", sections The
+ *    route change and Scope: attention for P x (1+k) block rows only, against
+ *    per-request paged context held in one shared pool, addressed by a batched
+ *    block table and per-request sequence lengths; section The cost: draft
+ *    block rows are non-causal and attend the request's entire span.
+ *  - "perf(dflash): widen the verify window past the compact graph's four-row
+ *    limit", section What changed: only seq_len entries are read, so stale
+ *    slots past a request's length are never touched, and an unsupported width
+ *    must be an error, not a silent refusal.
+ *
+ * Semantics (per request p with length L = seq_lens[p], window row i, query
+ * head h, KV head kvh = h / (Hq/Hkv)):
+ *   visible keys  j < L                       (causal == 0, draft block)
+ *                 j <= L - W + i              (causal == 1, verify window:
+ *                                              L counts the window's own rows,
+ *                                              row i sits at position L-W+i)
+ *   s_j = scale * <q, k_j>;  out = softmax(s) . V;  lse = ln sum_j exp(s_j)
+ *   A row with no visible key (only when L == 0) gets out = 0, lse = -inf.
+ *
+ * Device layouts (all row-major, caller-owned):
+ *   q            bf16   [P][W][Hq][D]
+ *   k_pool       [num_pages][Hkv][16][D]     bf16, or e4m3fn bytes
+ *   v_pool       [num_pages][Hkv][D][16]     bf16, or e4m3fn bytes; each
+ *                                            16-token page-head is stored
+ *                                            transposed (d-major)
+ *   k_scale      fp32 [num_pages][Hkv][16]   fp8 only: value = code * scale
+ *   v_scale      fp32 [num_pages][Hkv][16]   fp8 only
+ *   block_table  int32 [P][max_pages_per_req]; entry n of row p is the pool
+ *                page holding tokens [16n, 16n+16) of request p
+ *   seq_lens     int32 [P]; must equal the host lengths given to the plan
+ *   out          bf16   [P][W][Hq][D]
+ *   lse          fp32   [P][W][Hq]   natural log
+ * Pages are 16 tokens.  e4m3fn is the OCP 8-bit format (bias 7, max 448,
+ * S.1111.111 = NaN, no infinities).
+ *
+ * Status codes: every call returns SMALLW_OK (0) or a negative code; no C++
+ * exception crosses this interface.  All shape and range checks happen in
+ * small_w_attention_plan on the host.  Block-table entries outside
+ * [0, num_pages) are clamped on the device, so they cannot fault, but give
+ * undefined numbers.
+ */
+#ifndef SMALLW_H
+#define SMALLW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMALLW_OK            0
+#define SMALLW_EINVAL       (-1)  /* malformed argument (null, negative, inconsistent) */
+#define SMALLW_EUNSUPPORTED (-2)  /* well-formed but outside what the kernels serve    */
+#define SMALLW_EWORKSPACE   (-3)  /* workspace missing or smaller than required       */
+#define SMALLW_EDEVICE      (-4)  /* a HIP call failed; see small_w_attention_strerror */
+#define SMALLW_ENOMEM       (-5)  /* host allocation failed                            */
+
+#define SMALLW_PAGE_SIZE     16
+#define SMALLW_MAX_WINDOW    16
+#define SMALLW_MAX_REQS      256
+#define SMALLW_MAX_ROWS      128  /* W * (Hq / Hkv) */
+
+typedef enum { SMALLW_KV_BF16 = 0, SMALLW_KV_FP8_E4M3 = 1 } smallw_kv_dtype;
+
+typedef struct smallw_problem {
+    int32_t num_reqs;          /* P, 1..SMALLW_MAX_REQS                              */
+    int32_t window;            /* W, 1..SMALLW_MAX_WINDOW                            */
+    int32_t num_q_heads;       /* Hq >= 1                                            */
+    int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0, W*Hq/Hkv <= 128           */
+    int32_t head_dim;          /* D: 64, 128 or 256                                  */
+    int32_t page_size;         /* must be 16                                         */
+    int32_t num_pages;         /* pool capacity in pages, >= 1                       */
+    int32_t max_pages_per_req; /* block_table row stride, >= 1                       */
+    int32_t causal;            /* 1 = verify window (tail mask), 0 = draft block     */
+    int32_t kv_dtype;          /* smallw_kv_dtype                                    */
+    float   scale;             /* softmax scale; <= 0 selects 1/sqrt(D)              */
+    int32_t num_cus;           /* compute units to plan for; 0 = ask current device  */
+    int32_t force_splits;      /* 0 = automatic; > 0 = this many key splits per
+                                  request (capped at its page count)                 */
+} smallw_problem;
+
+typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
+
+/*
+ * Validate a problem and decide the split-K decomposition for one call.
+ * Plan once per speculative step, then run it for every attention layer.
+ *   seq_lens_host  host int32 [P]: L_p >= 0, L_p <= 16*max_pages_per_req, and
+ *                  for causal calls L_p == 0 or L_p >= W.
+ *   out            receives a new plan; release it with ..._plan_destroy.
+ * Splits: n_p = ceil(L_p/16) pages; slots = num_cus * (1 if 16*D*elt >= 8 KiB
+ * else 2); ppu = max(8, ceil(Hkv * sum n_p / slots)); S_p = ceil(n_p / ppu)
+ * (or min(force_splits, n_p)), S_p = 1 for an empty request.  Work unit
+ * u = unit_off[p] + kvh*S_p + s covers pages [floor(s n/S), floor((s+1) n/S)).
+ * Returns SMALLW_EINVAL / SMALLW_EUNSUPPORTED on bad input (nothing allocated),
+ * SMALLW_EDEVICE if num_cus == 0 and the device query fails, SMALLW_ENOMEM.
+ */
+int small_w_attention_plan(const smallw_problem* problem, const int32_t* seq_lens_host,
+                           smallw_plan** out);
+
+/* Device workspace bytes small_w_attention_run needs (0 when no request is
+ * split).  Holds per-split partial outputs and log-sum-exps. */
+size_t small_w_attention_workspace_bytes(const smallw_plan* plan);
+
+/*
+ * Enqueue the attention for one layer on `stream` (a hipStream_t; NULL = the
+ * default stream).  Launches the split-K sweep kernel and, when any request
+ * is split, the log-sum-exp combine kernel.  No host synchronisation and no
+ * allocation, so the call can be captured in a HIP graph.  All pointers are
+ * device pointers in the layouts above; k_scale / v_scale are required for
+ * fp8 KV and ignored otherwise.  workspace must be 256-byte aligned and hold
+ * small_w_attention_workspace_bytes(plan) bytes (may be NULL when that is 0);
+ * it is scratch owned by the caller and may be reused between calls on the
+ * same stream.  Returns SMALLW_EINVAL (null pointer / plan), SMALLW_EWORKSPACE,
+ * or SMALLW_EDEVICE (launch failure).
+ */
+int small_w_attention_run(const smallw_plan* plan, const void* q, const void* k_pool,
+                          const void* v_pool, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As small_w_attention_run, and additionally records caller-created hipEvent_t
+ * handles on `stream`: ev_start before the sweep kernel, ev_sweep_done after
+ * it, ev_end after the combine (equal to ev_sweep_done's position when there
+ * is no combine).  Any event may be NULL.  For timing the kernels in place.
+ */
+int small_w_attention_run_events(const smallw_plan* plan, const void* q, const void* k_pool,
+                                 const void* v_pool, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 const int32_t* seq_lens, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* ev_start, void* ev_sweep_done, void* ev_end);
+
+/*
+ * Export the plan's integer decomposition into host int32 `buf` of `cap`
+ * entries; *needed receives the entry count.  Layout:
+ *   [P, Hkv, U, R]  R = W*Hq/Hkv rows per work unit
+ *   S_p           x P
+ *   unit_off      x (P+1)
+ *   (p, kvh, s, page_begin, page_end) x U
+ * Returns SMALLW_EINVAL if buf is too small (with *needed set).
+ */
+int small_w_attention_plan_export(const smallw_plan* plan, int32_t* buf, size_t cap,
+                                  size_t* needed);
+
+/*
+ * Debug index export: on `stream`, write the physical pool page of every page
+ * each work unit streams, in the order the sweep kernel streams them, using
+ * the sweep kernel's own unit-decode and page-addressing device code.
+ * pages_out is device int32 [U][max_unit_pages] (unused tail entries = -1);
+ * max_unit_pages comes from small_w_attention_plan_max_unit_pages.
+ */
+int small_w_attention_trace_pages(const smallw_plan* plan, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t* pages_out,
+                                  size_t max_unit_pages, void* stream);
+
+/* Largest page count of any work unit of the plan (host lengths). */
+size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan);
+
+/* Release a plan (NULL is allowed). */
+void small_w_attention_plan_destroy(smallw_plan* plan);
+
+/* Static description of a status code; for SMALLW_EDEVICE, the last HIP
+ * error seen by this library on the calling thread. */
+const char* small_w_attention_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMALLW_H */

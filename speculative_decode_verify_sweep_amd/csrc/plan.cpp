@@ -1,0 +1,153 @@
+// Split-K planner: validates a call and decides its work decomposition.
+//
+// The pages name key splitting with a reduce step ("ChunkedSmallT re-streams
+// full KV per query chunk", section Finding) and a capacity function that
+// throws past the tile width (section Why no PR yet); they give no formula.
+// This planner sizes the splits so that the work units of one call fill the
+// GPU's compute units once, with an 8-page floor per split so the per-split
+// pipeline start and the partial traffic stay small against the KV stream:
+//   n_p   = ceil(L_p / 16)
+//   slots = num_cus * (1 if a K page-head (16*D*elt bytes) >= 8 KiB else 2)
+//   ppu   = max(8, ceil(Hkv * sum_p n_p / slots))
+//   S_p   = 1 (empty request) | min(force_splits, n_p) | ceil(n_p / ppu)
+//   unit  u = unit_off[p] + kvh*S_p + s,  pages [floor(s n/S), floor((s+1) n/S))
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "plan_internal.h"
+
+namespace {
+
+constexpr int kMinPagesPerSplit = 8;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int validate(const smallw_problem& pr, const int32_t* seq) {
+    if (pr.num_reqs < 1 || pr.window < 1 || pr.num_q_heads < 1 || pr.num_kv_heads < 1 ||
+        pr.head_dim < 1 || pr.page_size < 1 || pr.num_pages < 1 || pr.max_pages_per_req < 1 ||
+        pr.num_cus < 0 || pr.force_splits < 0)
+        return SMALLW_EINVAL;
+    if (pr.causal != 0 && pr.causal != 1) return SMALLW_EINVAL;
+    if (pr.kv_dtype != SMALLW_KV_BF16 && pr.kv_dtype != SMALLW_KV_FP8_E4M3) return SMALLW_EINVAL;
+    if (std::isnan(pr.scale) || std::isinf(pr.scale)) return SMALLW_EINVAL;
+    if (pr.num_q_heads % pr.num_kv_heads != 0) return SMALLW_EINVAL;
+    if (pr.num_reqs > SMALLW_MAX_REQS) return SMALLW_EUNSUPPORTED;
+    if (pr.window > SMALLW_MAX_WINDOW) return SMALLW_EUNSUPPORTED;
+    if (pr.page_size != SMALLW_PAGE_SIZE) return SMALLW_EUNSUPPORTED;
+    if (pr.head_dim != 64 && pr.head_dim != 128 && pr.head_dim != 256) return SMALLW_EUNSUPPORTED;
+    const int64_t rows = int64_t(pr.window) * (pr.num_q_heads / pr.num_kv_heads);
+    if (rows > SMALLW_MAX_ROWS) return SMALLW_EUNSUPPORTED;
+    if (!seq) return SMALLW_EINVAL;
+    const int64_t cap = int64_t(pr.max_pages_per_req) * SMALLW_PAGE_SIZE;
+    for (int p = 0; p < pr.num_reqs; ++p) {
+        if (seq[p] < 0 || seq[p] > cap) return SMALLW_EINVAL;
+        if (pr.causal && seq[p] > 0 && seq[p] < pr.window) return SMALLW_EINVAL;
+    }
+    return SMALLW_OK;
+}
+
+}  // namespace
+
+namespace smallw {
+
+int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) {
+    int rc = validate(in, seq);
+    if (rc != SMALLW_OK) return rc;
+    smallw_plan* pl = new (std::nothrow) smallw_plan();
+    if (!pl) return SMALLW_ENOMEM;
+    try {
+        pl->prob = in;
+        if (!(pl->prob.scale > 0.f)) pl->prob.scale = 1.0f / std::sqrt(float(in.head_dim));
+        const int P = in.num_reqs, Hkv = in.num_kv_heads, D = in.head_dim;
+        const int elt = in.kv_dtype == SMALLW_KV_FP8_E4M3 ? 1 : 2;
+        pl->G = in.num_q_heads / Hkv;
+        pl->R = in.window * pl->G;
+        pl->seq.assign(seq, seq + P);
+        pl->npg.resize(P);
+        int64_t total = 0;
+        for (int p = 0; p < P; ++p) {
+            pl->npg[p] = int32_t(ceil_div(seq[p], SMALLW_PAGE_SIZE));
+            total += pl->npg[p];
+        }
+        total *= Hkv;
+        const int64_t slots = int64_t(in.num_cus) * (SMALLW_PAGE_SIZE * D * elt >= 8192 ? 1 : 2);
+        int64_t ppu = ceil_div(total, slots);
+        if (ppu < kMinPagesPerSplit) ppu = kMinPagesPerSplit;
+        pl->splits.resize(P);
+        pl->unit_off.assign(P + 1, 0);
+        for (int p = 0; p < P; ++p) {
+            const int64_t n = pl->npg[p];
+            int64_t S;
+            if (n == 0) S = 1;
+            else if (in.force_splits > 0) S = in.force_splits < n ? in.force_splits : n;
+            else S = ceil_div(n, ppu);
+            pl->splits[p] = int32_t(S);
+            if (S > 1) pl->any_split = true;
+            const int64_t next = int64_t(pl->unit_off[p]) + Hkv * S;
+            if (next > INT32_MAX / 2) { delete pl; return SMALLW_EUNSUPPORTED; }
+            pl->unit_off[p + 1] = int32_t(next);
+            const int64_t biggest = ceil_div(n, S);
+            if (size_t(biggest) > pl->max_unit_pages) pl->max_unit_pages = size_t(biggest);
+        }
+        pl->U = pl->unit_off[P];
+        if (pl->any_split) {
+            const size_t po = size_t(pl->U) * pl->R * D * sizeof(float);
+            const size_t pls = size_t(pl->U) * pl->R * sizeof(float);
+            pl->part_o_off = 0;
+            pl->part_lse_off = align256(po);
+            pl->ws_bytes = pl->part_lse_off + align256(pls);
+        }
+    } catch (...) {
+        delete pl;
+        return SMALLW_ENOMEM;
+    }
+    *out = pl;
+    return SMALLW_OK;
+}
+
+}  // namespace smallw
+
+extern "C" {
+
+size_t small_w_attention_workspace_bytes(const smallw_plan* plan) {
+    return plan ? plan->ws_bytes : 0;
+}
+
+size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan) {
+    return plan ? plan->max_unit_pages : 0;
+}
+
+int small_w_attention_plan_export(const smallw_plan* plan, int32_t* buf, size_t cap,
+                                  size_t* needed) {
+    if (!plan) return SMALLW_EINVAL;
+    const int P = plan->prob.num_reqs, Hkv = plan->prob.num_kv_heads;
+    const size_t n = 4 + size_t(P) + size_t(P + 1) + 5 * size_t(plan->U);
+    if (needed) *needed = n;
+    if (!buf || cap < n) return SMALLW_EINVAL;
+    size_t k = 0;
+    buf[k++] = P;
+    buf[k++] = Hkv;
+    buf[k++] = plan->U;
+    buf[k++] = plan->R;
+    for (int p = 0; p < P; ++p) buf[k++] = plan->splits[p];
+    for (int p = 0; p <= P; ++p) buf[k++] = plan->unit_off[p];
+    for (int p = 0; p < P; ++p) {
+        const int64_t npg = plan->npg[p], S = plan->splits[p];
+        for (int kvh = 0; kvh < Hkv; ++kvh)
+            for (int64_t s = 0; s < S; ++s) {
+                buf[k++] = p;
+                buf[k++] = kvh;
+                buf[k++] = int32_t(s);
+                buf[k++] = int32_t(s * npg / S);
+                buf[k++] = int32_t((s + 1) * npg / S);
+            }
+    }
+    return SMALLW_OK;
+}
+
+void small_w_attention_plan_destroy(smallw_plan* plan) { delete plan; }
+
+}  // extern "C"

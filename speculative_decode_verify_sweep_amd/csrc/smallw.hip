@@ -1,0 +1,649 @@
+// Small-window paged attention for MI355X (gfx950): split-K sweep, log-sum-exp
+// combine, page-trace export, and the C entry points that launch them.
+//
+// Method (see "ChunkedSmallT re-streams full KV per query chunk", section
+// Finding): all W window rows of a request attend its visible keys; the key
+// range is split across work units and the partial softmax results are merged
+// by a reduce step.  Unlike the chunked route that page describes, one work
+// unit holds ALL W*G query rows of its KV head, so every K/V byte of the
+// visible context is streamed from HBM exactly once per call.
+//
+// Work unit u = (request p, KV head kvh, key split s), one 256-thread
+// workgroup (4 wave64s).  The unit walks its pages two at a time ("chunks" of
+// 32 tokens) through an NSTAGE-deep ring of LDS buffers that the four waves
+// fill with 16-byte global->LDS DMA loads, each load instruction moving 1 KiB
+// of one page-head.  Rows are the N side of the MFMAs:
+//   S^T[token][row]  = K[token][:] . Q[row][:]       (v_mfma_f32_16x16x32_bf16)
+//   O^T[d][row]     += V^T[d][token] . P^T[token][row]
+// In this orientation a lane's accumulator registers all belong to one query
+// row, so the online-softmax max/sum and the rescale factor are per-lane
+// scalars, and the S^T accumulator registers of two 16-token tiles are
+// exactly the B operand of the PV MFMA (no shuffle through LDS).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "plan_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPage = SMALLW_PAGE_SIZE;
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Params {
+    const uint16_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* bt;
+    const int32_t* seq;
+    uint16_t* out;
+    float* lse;
+    float* part_o;
+    float* part_lse;
+    int32_t P, W, Hq, Hkv, G, R, bt_stride, num_pages, causal;
+    float scale_log2;  // softmax scale * log2(e): scores are kept in base 2
+    int32_t unit_off[SMALLW_MAX_REQS + 1];
+};
+
+struct Unit {
+    int p, kvh, s, S, L;
+    int pb, pe;  // logical page range [pb, pe)
+};
+
+// Work unit u -> (p, kvh, s) and its page range.  Shared by the sweep and the
+// page-trace kernel so the trace shows exactly what the sweep addresses.
+__device__ __forceinline__ Unit decode_unit(const Params& a, int u) {
+    int lo = 0, hi = a.P;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.unit_off[mid] <= u) lo = mid;
+        else hi = mid;
+    }
+    Unit r;
+    r.p = lo;
+    r.S = (a.unit_off[lo + 1] - a.unit_off[lo]) / a.Hkv;
+    const int rem = u - a.unit_off[lo];
+    r.kvh = rem / r.S;
+    r.s = rem - r.kvh * r.S;
+    int L = a.seq[lo];
+    const int cap = a.bt_stride * kPage;
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    r.L = L;
+    const int64_t n = (L + kPage - 1) / kPage;
+    r.pb = int((int64_t(r.s) * n) / r.S);
+    r.pe = int((int64_t(r.s + 1) * n) / r.S);
+    return r;
+}
+
+// Pool page holding logical page n of request p; clamped so a bad table
+// entry can never address outside the pool.
+__device__ __forceinline__ int phys_page(const Params& a, int p, int n) {
+    int pg = a.bt[int64_t(p) * a.bt_stride + n];
+    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+    return pg;
+}
+
+// 16-byte global -> LDS DMA.  Lane l's 16 bytes land at lds_addr + 16*l.
+// Issued through inline asm so the compiler does not guard every later LDS
+// read with a full vmcnt(0) wait; completion is tracked by hand with vmcnt.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gaddr), "s"(lds_addr)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Wait until at most k*LPW of this wave's DMA loads are still in flight.
+template <int LPW>
+__device__ __forceinline__ void wait_stages(int k) {
+    if (k <= 0) wait_vmcnt<0>();
+    else if (k == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<2 * LPW>();
+}
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// ----------------------------------------------------------------------------
+// Split-K sweep kernel, bf16 KV.
+//   D    head dim (64/128/256)
+//   TPW  16-row MFMA tiles per wave (rows are spread over the 4 waves)
+//   NS   LDS ring depth in chunks (2 pages each)
+// LDS chunk layout (bytes):  [K page0 | K page1 | V^T page0 | V^T page1],
+// each page-head 32*D bytes.  Wave w DMAs region w.
+// K rows are 16-byte-chunk swizzled: token row tau stores global chunk c at
+// slot c ^ h(tau), h(tau) = ((tau>>1)&12)|(tau&3) (masked to the row), so the
+// 16 lanes of one MFMA operand read hit distinct banks.  V^T rows (32 bytes)
+// swap their two halves when bit 2 xor bit 3 of d is set, for the same reason.
+// ----------------------------------------------------------------------------
+template <int D, int TPW, int NS>
+__global__ __launch_bounds__(kThreads, 1) void sweep_bf16(Params a) {
+    constexpr int KS = D / 32;              // MFMA k-steps over the head dim
+    constexpr int DT = D / 16;              // 16-wide d tiles of the output
+    constexpr int PAGE_BYTES = 32 * D;      // one page-head of K (or V^T), bf16
+    constexpr int STAGE = 4 * PAGE_BYTES;   // K0 K1 V0 V1
+    constexpr int LPW = PAGE_BYTES / 1024;  // DMA instructions per wave per chunk
+    constexpr int CPR = D / 8;              // 16-byte chunks per K token row
+    static_assert(LPW >= 1 && NS >= 2 && NS <= 4, "config");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int g = l >> 4;   // lane group: MFMA k-slot group
+    const int ln = l & 15;  // MFMA row/column index within a 16-tile
+
+    const Unit un = decode_unit(a, blockIdx.x);
+    const int u = blockIdx.x;
+    const int p = un.p, kvh = un.kvh, L = un.L;
+    const int npages = un.pe - un.pb;
+    const int nchunks = (npages + 1) >> 1;
+    const int jend = min(L, un.pe * kPage);                    // keys past this: not in unit
+    const int lim_lo = a.causal ? (L - a.W + 1) : L;          // first key any row may not see
+    const int first_masked = min(jend, lim_lo);
+
+    // ---- DMA addressing for this wave's region: per-lane offsets inside a page-head
+    const int region_pg = w & 1;
+    const bool region_v = (w >> 1) != 0;
+    uint32_t goff[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int qc = 64 * i + l;  // 16-byte chunk index inside the page-head (LDS order)
+        if (!region_v) {
+            const int tr = qc / CPR, slot = qc % CPR;
+            const int tau = 16 * region_pg + tr;
+            const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
+            goff[i] = uint32_t(tr * (2 * D) + (slot ^ hsw) * 16);
+        } else {
+            const int d = qc >> 1, slot = qc & 1;
+            const int sv = ((d >> 2) ^ (d >> 3)) & 1;
+            goff[i] = uint32_t(d * 32 + (slot ^ sv) * 16);
+        }
+    }
+    const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
+    const uint8_t* const pool = region_v ? a.v : a.k;
+    const int64_t head_stride = int64_t(PAGE_BYTES);
+
+    auto issue_chunk = [&](int c) {
+        int n = un.pb + 2 * c + region_pg;
+        if (n >= un.pe) n = un.pb + 2 * c;  // absent second page: reload the first, masked later
+        const int phys = phys_page(a, p, n);
+        const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * head_stride;
+        const uint32_t lds = smem_base + uint32_t((c % NS) * STAGE + w * PAGE_BYTES);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            dma16(base + goff[i], __builtin_amdgcn_readfirstlane(lds + 1024u * i));
+    };
+
+    // ---- prologue: start streaming before touching Q
+    const int pro = min(NS - 1, nchunks);
+    for (int c = 0; c < pro; ++c) issue_chunk(c);
+
+    // ---- rows owned by this wave: global tiles w, w+4, ...
+    const int T = (a.R + 15) >> 4;
+    int ntile = 0;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+        if (w + 4 * tt < T) ntile = tt + 1;
+
+    bf16x8_t qf[TPW][KS];
+    int hi_tok[TPW];  // last key position this lane's row may see (inclusive)
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int r = 16 * (w + 4 * tt) + ln;
+        const int i = r / a.G;
+        const int gq = r - i * a.G;
+        const bool valid = tt < ntile && r < a.R;
+        const int lim = a.causal ? (L - a.W + i) : (L - 1);
+        hi_tok[tt] = min(jend - 1, lim);
+        const uint16_t* qrow =
+            a.q + ((int64_t(p) * a.W + (valid ? i : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (valid) {
+                const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+                qf[tt][ks] = __builtin_bit_cast(bf16x8_t, raw);
+            } else {
+                qf[tt][ks] = __builtin_bit_cast(bf16x8_t, u32x4{0u, 0u, 0u, 0u});
+            }
+        }
+    }
+
+    // ---- LDS read addressing (per lane, constant over chunks)
+    // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
+    // so lane group g of the S^T accumulators covers chunk tokens 8g+4t+j and the PV
+    // B operand of lane group g is chunk tokens 8g..8g+7 -- one 16-byte V^T read.
+    uint32_t kaddr[2][4];
+    {
+        const int mh = (ln >> 2) & (KS - 1 < 3 ? KS - 1 : 3);
+        const int ml = ln & 3;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
+            const int row_base = (tau >> 4) * PAGE_BYTES + (tau & 15) * (2 * D);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                kaddr[t][b] = uint32_t(row_base + 64 * ((b ^ mh) & (KS - 1)) + 16 * (g ^ ml));
+        }
+    }
+    uint32_t vaddr;
+    {
+        const int sv = ((ln >> 2) ^ (ln >> 3)) & 1;
+        vaddr = uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES + (2 * ln + ((g & 1) ^ sv)) * 16);
+    }
+
+    f32x4 acc[TPW][DT];
+    float m_run[TPW], l_run[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        m_run[tt] = -INFINITY;
+        l_run[tt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- main loop over chunks
+    for (int c = 0; c < nchunks; ++c) {
+        wait_stages<LPW>(min(NS - 2, nchunks - 1 - c));
+        __syncthreads();
+        if (c + NS - 1 < nchunks) issue_chunk(c + NS - 1);
+        if (ntile == 0) continue;
+
+        const uint8_t* st = smem + (c % NS) * STAGE;
+        const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
+
+        f32x4 s[TPW][2];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) s[tt][0] = s[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(
+                    st + kaddr[t][ks & 3] + 256 * (ks >> 2));
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt)
+                    if (tt < ntile)
+                        s[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[tt][ks],
+                                                                            s[tt][t], 0, 0, 0);
+            }
+        }
+
+        const bool masked = j0 + 32 > first_masked;
+        bf16x8_t pf[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            if (tt >= ntile) continue;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = s[tt][e >> 2][e & 3] * a.scale_log2;
+            if (masked) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tok = j0 + 8 * g + e;
+                    x[e] = tok <= hi_tok[tt] ? x[e] : -INFINITY;
+                }
+            }
+            float mx = x[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+            mx = wave_max_groups(mx);
+            const float m_new = fmaxf(m_run[tt], mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[tt] - m_use);
+            m_run[tt] = m_new;
+            float psum = 0.f;
+            __bf16 pb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
+                psum += pe;
+                pb[e] = (__bf16)pe;
+            }
+            l_run[tt] = l_run[tt] * alpha + psum;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[tt][dt] *= alpha;
+            pf[tt] = bf16x8_t{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
+        }
+
+        // valid tokens of this lane group's 8-token V^T slice (stale / absent -> zero)
+        const int vcnt = min(max(jend - (j0 + 8 * g), 0), 8);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+            if (vcnt < 8) {
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    const uint32_t keep = (2 * k2 + 1 < vcnt) ? 0xffffffffu
+                                        : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
+                    raw[k2] &= keep;
+                }
+            }
+            const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+                if (tt < ntile)
+                    acc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pf[tt], acc[tt][dt],
+                                                                          0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: normalise, write final output or the split partial
+    const bool direct = un.S == 1;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        if (tt >= ntile) continue;
+        const int r = 16 * (w + 4 * tt) + ln;
+        const float lsum = wave_sum_groups(l_run[tt]);
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const float lse_v = lsum > 0.f ? (m_run[tt] + __log2f(lsum)) * kLn2 : -INFINITY;
+        if (r >= a.R) continue;
+        const int i = r / a.G;
+        const int h = kvh * a.G + (r - i * a.G);
+        if (direct) {
+            uint16_t* orow = a.out + ((int64_t(p) * a.W + i) * a.Hq + h) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o = acc[tt][dt] * inv;
+                uint2 pk;
+                pk.x = uint32_t(f32_to_bf16_bits(o[0])) | (uint32_t(f32_to_bf16_bits(o[1])) << 16);
+                pk.y = uint32_t(f32_to_bf16_bits(o[2])) | (uint32_t(f32_to_bf16_bits(o[3])) << 16);
+                *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pk;
+            }
+            if (g == 0) a.lse[(int64_t(p) * a.W + i) * a.Hq + h] = lse_v;
+        } else {
+            float* orow = a.part_o + (int64_t(u) * a.R + r) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = acc[tt][dt] * inv;
+            if (g == 0) a.part_lse[int64_t(u) * a.R + r] = lse_v;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Log-sum-exp combine over the S_p key splits of every (p, kvh, row).
+// One workgroup per row; threads split the D/4 float4 columns x split groups.
+//   M = max_s lse_s;  lse = M + ln sum_s exp(lse_s - M);  o = sum_s exp(lse_s - lse) o_s
+// Fixed reduction order, so repeated calls are bitwise identical.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
+    constexpr int NQ = D / 4;
+    constexpr int NGRP = kThreads / NQ;
+    __shared__ float red[kWaves];
+    __shared__ f32x4 part[kThreads];
+
+    const int b = blockIdx.x;
+    const int r = b % a.R;
+    const int pk = b / a.R;
+    const int kvh = pk % a.Hkv;
+    const int p = pk / a.Hkv;
+    const int S = (a.unit_off[p + 1] - a.unit_off[p]) / a.Hkv;
+    if (S <= 1) return;
+    const int64_t u0 = a.unit_off[p] + int64_t(kvh) * S;
+    const int tid = threadIdx.x;
+
+    float mx = -INFINITY;
+    for (int s = tid; s < S; s += kThreads) mx = fmaxf(mx, a.part_lse[(u0 + s) * a.R + r]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+
+    float sum = 0.f;
+    if (mx != -INFINITY)
+        for (int s = tid; s < S; s += kThreads) sum += expf(a.part_lse[(u0 + s) * a.R + r] - mx);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if ((tid & 63) == 0) red[tid >> 6] = sum;
+    __syncthreads();
+    sum = (red[0] + red[1]) + (red[2] + red[3]);
+    const float lse = (mx == -INFINITY || !(sum > 0.f)) ? -INFINITY : mx + logf(sum);
+
+    const int d4 = tid % NQ, grp = tid / NQ;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (lse != -INFINITY) {
+        for (int s = grp; s < S; s += NGRP) {
+            const float wgt = expf(a.part_lse[(u0 + s) * a.R + r] - lse);
+            const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + ((u0 + s) * a.R + r) * D + 4 * d4);
+            acc += wgt * o;
+        }
+    }
+    part[tid] = acc;
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+        for (int gg = 1; gg < NGRP; ++gg) acc += part[gg * NQ + d4];
+        const int i = r / a.G;
+        const int h = kvh * a.G + (r - i * a.G);
+        uint16_t* orow = a.out + ((int64_t(p) * a.W + i) * a.Hq + h) * D;
+        uint2 pkd;
+        pkd.x = uint32_t(f32_to_bf16_bits(acc[0])) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
+        pkd.y = uint32_t(f32_to_bf16_bits(acc[2])) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
+        *reinterpret_cast<uint2*>(orow + 4 * d4) = pkd;
+        if (tid == 0) a.lse[(int64_t(p) * a.W + i) * a.Hq + h] = lse;
+    }
+}
+
+// Page-trace export: the pool pages each work unit streams, in order.
+__global__ void trace_kernel(Params a, int32_t* out, int64_t maxp) {
+    const int u = blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= a.unit_off[a.P]) return;
+    const Unit un = decode_unit(a, u);
+    int64_t k = 0;
+    for (int n = un.pb; n < un.pe && k < maxp; ++n, ++k) out[u * maxp + k] = phys_page(a, un.p, n);
+    for (; k < maxp; ++k) out[u * maxp + k] = -1;
+}
+
+// ----------------------------------------------------------------------------
+thread_local char g_err[256] = "";
+
+}  // namespace
+
+namespace smallw {
+void set_device_error(const char* what, int hip_status) {
+    snprintf(g_err, sizeof g_err, "%s: %s", what, hipGetErrorString(hipError_t(hip_status)));
+}
+}  // namespace smallw
+
+namespace {
+
+int check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        smallw::set_device_error(what, int(e));
+        return SMALLW_EDEVICE;
+    }
+    return SMALLW_OK;
+}
+
+void fill_params(Params& a, const smallw_plan* pl) {
+    const smallw_problem& pr = pl->prob;
+    a.P = pr.num_reqs;
+    a.W = pr.window;
+    a.Hq = pr.num_q_heads;
+    a.Hkv = pr.num_kv_heads;
+    a.G = pl->G;
+    a.R = pl->R;
+    a.bt_stride = pr.max_pages_per_req;
+    a.num_pages = pr.num_pages;
+    a.causal = pr.causal;
+    a.scale_log2 = pr.scale * kLog2e;
+    for (int p = 0; p <= pr.num_reqs; ++p) a.unit_off[p] = pl->unit_off[p];
+}
+
+template <int D>
+int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st) {
+    const int T = (pl->R + 15) / 16;
+    constexpr int NS = (D == 256) ? 4 : 4;
+    if (T <= 4) hipLaunchKernelGGL((sweep_bf16<D, 1, NS>), dim3(pl->U), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((sweep_bf16<D, 2, NS>), dim3(pl->U), dim3(kThreads), 0, st, a);
+    return check_launch("sweep kernel launch");
+}
+
+template <int D>
+int launch_combine(const smallw_plan* pl, const Params& a, hipStream_t st) {
+    const int64_t blocks = int64_t(pl->prob.num_reqs) * pl->prob.num_kv_heads * pl->R;
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, a);
+    return check_launch("combine kernel launch");
+}
+
+int record(void* ev, hipStream_t st) {
+    if (!ev) return SMALLW_OK;
+    const hipError_t e = hipEventRecord(hipEvent_t(ev), st);
+    if (e != hipSuccess) {
+        smallw::set_device_error("hipEventRecord", int(e));
+        return SMALLW_EDEVICE;
+    }
+    return SMALLW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int small_w_attention_plan(const smallw_problem* problem, const int32_t* seq_lens_host,
+                           smallw_plan** out) {
+    if (!problem || !out) return SMALLW_EINVAL;
+    *out = nullptr;
+    smallw_problem pr = *problem;
+    if (pr.num_cus < 0) return SMALLW_EINVAL;
+    if (pr.num_cus == 0) {
+        int dev = 0, n = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || n <= 0) {
+            smallw::set_device_error("compute-unit query", int(e));
+            return SMALLW_EDEVICE;
+        }
+        pr.num_cus = n;
+    }
+    return smallw::build_plan(pr, seq_lens_host, out);
+}
+
+int small_w_attention_run_events(const smallw_plan* pl, const void* q, const void* k_pool,
+                                 const void* v_pool, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 const int32_t* seq_lens, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* ev_start, void* ev_sweep_done, void* ev_end) {
+    if (!pl || !q || !k_pool || !v_pool || !block_table || !seq_lens || !out || !lse)
+        return SMALLW_EINVAL;
+    const bool fp8 = pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3;
+    if (fp8 && (!k_scale || !v_scale)) return SMALLW_EINVAL;
+    if (fp8) return SMALLW_EUNSUPPORTED;  // fp8 kernels are not built yet
+    if (pl->ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl->ws_bytes) return SMALLW_EWORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SMALLW_EWORKSPACE;
+    }
+    Params a;
+    memset(&a, 0, sizeof a);
+    fill_params(a, pl);
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint8_t*>(k_pool);
+    a.v = static_cast<const uint8_t*>(v_pool);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.bt = block_table;
+    a.seq = seq_lens;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    if (pl->ws_bytes > 0) {
+        a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl->part_o_off);
+        a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl->part_lse_off);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = record(ev_start, st);
+    if (rc) return rc;
+    switch (pl->prob.head_dim) {
+        case 64: rc = launch_sweep<64>(pl, a, st); break;
+        case 128: rc = launch_sweep<128>(pl, a, st); break;
+        case 256: rc = launch_sweep<256>(pl, a, st); break;
+        default: return SMALLW_EUNSUPPORTED;
+    }
+    if (rc) return rc;
+    if ((rc = record(ev_sweep_done, st))) return rc;
+    if (pl->any_split) {
+        switch (pl->prob.head_dim) {
+            case 64: rc = launch_combine<64>(pl, a, st); break;
+            case 128: rc = launch_combine<128>(pl, a, st); break;
+            default: rc = launch_combine<256>(pl, a, st); break;
+        }
+        if (rc) return rc;
+    }
+    return record(ev_end, st);
+}
+
+int small_w_attention_run(const smallw_plan* pl, const void* q, const void* k_pool,
+                          const void* v_pool, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    return small_w_attention_run_events(pl, q, k_pool, v_pool, k_scale, v_scale, block_table,
+                                        seq_lens, out, lse, workspace, workspace_bytes, stream,
+                                        nullptr, nullptr, nullptr);
+}
+
+int small_w_attention_trace_pages(const smallw_plan* pl, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t* pages_out,
+                                  size_t max_unit_pages, void* stream) {
+    if (!pl || !block_table || !seq_lens || !pages_out || max_unit_pages == 0)
+        return SMALLW_EINVAL;
+    Params a;
+    memset(&a, 0, sizeof a);
+    fill_params(a, pl);
+    a.bt = block_table;
+    a.seq = seq_lens;
+    const int blocks = (pl->U + 255) / 256;
+    hipLaunchKernelGGL(trace_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       a, pages_out, int64_t(max_unit_pages));
+    return check_launch("trace kernel launch");
+}
+
+const char* small_w_attention_strerror(int status) {
+    switch (status) {
+        case SMALLW_OK: return "ok";
+        case SMALLW_EINVAL: return "invalid argument";
+        case SMALLW_EUNSUPPORTED: return "unsupported problem (head_dim, window, rows, page size or request count)";
+        case SMALLW_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case SMALLW_EDEVICE: return g_err[0] ? g_err : "HIP device error";
+        case SMALLW_ENOMEM: return "host allocation failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

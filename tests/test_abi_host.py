@@ -1,0 +1,174 @@
+"""Host-side checks of the C-ABI library: no GPU needed.
+
+* libsmallw.so loads and exports every function include/smallw.h declares;
+* small_w_attention_plan rejects each malformed or unsupported problem with
+  the documented status code (all checks run on the host);
+* the integer plan export is bit-exact against the oracle's restatement of
+  the written split specification, over a seeded sweep of problems;
+* small_w_attention_run rejects null pointers and short or misaligned
+  workspaces before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import speculative_decode_verify_sweep_amd as sw
+from speculative_decode_verify_sweep_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smallw.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(small_w_attention_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "small_w_attention_plan" in names and "small_w_attention_run" in names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def base_problem(**kw):
+    d = dict(num_reqs=1, window=4, num_q_heads=4, num_kv_heads=1, head_dim=64, num_pages=32,
+             max_pages_per_req=32, causal=1, kv_dtype=0, scale=0.0, num_cus=256,
+             force_splits=0)
+    d.update(kw)
+    return B.make_problem(**d)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_reqs", 0, B.SMALLW_EINVAL),
+    ("num_reqs", 257, B.SMALLW_EUNSUPPORTED),
+    ("window", 0, B.SMALLW_EINVAL),
+    ("window", 17, B.SMALLW_EUNSUPPORTED),
+    ("num_q_heads", 6, B.SMALLW_EINVAL),            # 6 % 4 kv heads != 0 (set below)
+    ("num_kv_heads", 0, B.SMALLW_EINVAL),
+    ("head_dim", 96, B.SMALLW_EUNSUPPORTED),
+    ("head_dim", 0, B.SMALLW_EINVAL),
+    ("page_size", 32, B.SMALLW_EUNSUPPORTED),
+    ("num_pages", 0, B.SMALLW_EINVAL),
+    ("max_pages_per_req", 0, B.SMALLW_EINVAL),
+    ("causal", 2, B.SMALLW_EINVAL),
+    ("kv_dtype", 7, B.SMALLW_EINVAL),
+    ("scale", float("nan"), B.SMALLW_EINVAL),
+    ("num_cus", -1, B.SMALLW_EINVAL),
+    ("force_splits", -2, B.SMALLW_EINVAL),
+])
+def test_plan_rejects_bad_problems(field, value, code):
+    kw = {field: value}
+    if field == "num_q_heads":
+        kw["num_kv_heads"] = 4
+    pr = base_problem(**kw)
+    with pytest.raises(B.SmallwError) as e:
+        sw.small_w_attention_plan(pr, [260])
+    assert e.value.code == code
+
+
+def test_plan_rejects_bad_lengths_and_too_many_rows():
+    with pytest.raises(B.SmallwError) as e:      # causal window longer than the request
+        sw.small_w_attention_plan(base_problem(), [3])
+    assert e.value.code == B.SMALLW_EINVAL
+    with pytest.raises(B.SmallwError) as e:      # longer than the block-table row
+        sw.small_w_attention_plan(base_problem(max_pages_per_req=2), [33])
+    assert e.value.code == B.SMALLW_EINVAL
+    with pytest.raises(B.SmallwError) as e:
+        sw.small_w_attention_plan(base_problem(), [-1])
+    assert e.value.code == B.SMALLW_EINVAL
+    with pytest.raises(B.SmallwError) as e:      # W * G = 16 * 9 = 144 rows > 128
+        sw.small_w_attention_plan(base_problem(window=16, num_q_heads=9, num_kv_heads=1), [260])
+    assert e.value.code == B.SMALLW_EUNSUPPORTED
+    # empty request is a valid idle slot, W * G = 128 is the limit
+    sw.small_w_attention_plan(base_problem(num_reqs=2, window=16, num_q_heads=8), [0, 16])
+
+
+def test_plan_export_matches_oracle_plan_bit_exactly():
+    rng = np.random.default_rng(2024)
+    for trial in range(300):
+        P = int(rng.integers(1, 12))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 6]))
+        W = int(rng.integers(1, 17))
+        if W * G > 128:
+            W = 128 // G
+        D = int(rng.choice([64, 128, 256]))
+        fp8 = int(rng.integers(0, 2))
+        causal = int(rng.integers(0, 2))
+        force = int(rng.choice([0, 0, 0, 1, 2, 5, 64]))
+        cus = int(rng.choice([1, 8, 80, 256, 304]))
+        hi = int(rng.choice([40, 3000, 70000]))
+        seq = rng.integers(W if causal else 0, hi, size=P).astype(np.int32)
+        if rng.integers(0, 4) == 0:
+            seq[rng.integers(0, P)] = 0
+        maxp = int(-(-int(seq.max()) // 16)) + int(rng.integers(0, 3)) or 1
+        pr = B.make_problem(num_reqs=P, window=W, num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                            head_dim=D, num_pages=100000, max_pages_per_req=maxp, causal=causal,
+                            kv_dtype=fp8, num_cus=cus, force_splits=force)
+        plan = sw.small_w_attention_plan(pr, seq)
+        mine = sw.small_w_attention_plan_export(plan)
+        ref = oracle.plan_export(
+            oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=bool(fp8), seq_lens=seq, num_cus=cus,
+                        force_splits=force), R=W * G)
+        np.testing.assert_array_equal(mine, ref)
+        pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=bool(fp8), seq_lens=seq, num_cus=cus,
+                         force_splits=force)
+        biggest = max(pe - pb for (_, _, _, pb, pe) in pl["units"])
+        assert sw.small_w_attention_plan_max_unit_pages(plan) == biggest
+        # workspace: fp32 partial outputs and lse per unit and row, 256-byte aligned
+        U, R = pl["U"], W * G
+        a256 = lambda x: (x + 255) // 256 * 256
+        want = a256(U * R * D * 4) + a256(U * R * 4) if pl["any_split"] else 0
+        assert sw.small_w_attention_workspace_bytes(plan) == want
+
+
+def test_run_rejects_null_pointers_and_bad_workspace_before_any_launch():
+    pr = base_problem(force_splits=3)
+    plan = sw.small_w_attention_plan(pr, [260])
+    need = sw.small_w_attention_workspace_bytes(plan)
+    assert need > 0
+    lib = B.lib()
+    fake = 1 << 40  # never dereferenced: every check below fails before a launch
+    args = [plan.handle, fake, fake, fake, None, None, fake, fake, fake, fake, fake, need, None]
+    for k in (1, 2, 3, 6, 7, 8, 9):
+        bad = list(args)
+        bad[k] = None
+        assert lib.small_w_attention_run(*bad) == B.SMALLW_EINVAL
+    short = list(args)
+    short[11] = need - 1
+    assert lib.small_w_attention_run(*short) == B.SMALLW_EWORKSPACE
+    noptr = list(args)
+    noptr[10] = None
+    assert lib.small_w_attention_run(*noptr) == B.SMALLW_EWORKSPACE
+    misaligned = list(args)
+    misaligned[10] = fake + 16
+    assert lib.small_w_attention_run(*misaligned) == B.SMALLW_EWORKSPACE
+    assert lib.small_w_attention_run(None, *args[1:]) == B.SMALLW_EINVAL
+
+
+def test_fp8_run_requires_scales():
+    plan = sw.small_w_attention_plan(base_problem(kv_dtype=1), [260])
+    fake = 1 << 40
+    rc = B.lib().small_w_attention_run(plan.handle, fake, fake, fake, None, None, fake, fake,
+                                       fake, fake, None, 0, None)
+    assert rc == B.SMALLW_EINVAL
+
+
+def test_strerror_names_every_code():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert len(sw.small_w_attention_strerror(code)) >= 2
+    assert "unknown" in sw.small_w_attention_strerror(-99)
+
+
+def test_package_has_no_fallback_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(OSError):
+        B.lib()
