@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark the small-window verify attention on one MI355X.
+
+Workload: one request, 24 query heads / 4 KV heads, head_dim 256, 64K context
+plus a W-row causal verify window, bf16 KV in 16-token pages placed by a
+seeded permutation of a 5000-page pool; Q, K, V ~ N(0, 1).  One step is one
+layer call (sweep kernel + log-sum-exp combine).  Each timed call starts from
+a cold cache: a 2 GiB buffer (8x the 256 MB Infinity Cache) is READ before it,
+outside the timed span (the pages' op bench measures cold).  The flush reads
+rather than writes so that it leaves no dirty lines whose write-back would be
+charged to the timed call.  Per-call times come from HIP events the
+library records on the stream it launches on.
+
+Prints one JSON line: microseconds per layer call at W=16 (value), the KV
+bandwidth (one sweep's K and V bytes / time, the pages' own definition) and
+its fraction of the 8 TB/s HBM peak, the W = 1, 8, 12 times and the W=16/W=1
+ratio, the two-sweep foil (W=16 served as two W=8 calls), a roofline block for
+the sweep kernel and the fp64 CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+CTX = 65536
+WINDOWS = (1, 8, 12, 16)
+COUNTERS = os.path.join(ROOT, "profiles", "sweep_verify64k_w16_counters.json")
+SWEEP_SRC = os.path.join(ROOT, "speculative_decode_verify_sweep_amd", "csrc", "smallw.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kv_bytes(seq_lens, hkv, d, elt=2):
+    """K and V bytes of one sweep over every visible token (the pages' GB/s numerator)."""
+    return int(sum(int(x) for x in seq_lens)) * hkv * 2 * d * elt
+
+
+def source_hash():
+    with open(SWEEP_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Call:
+    """One prepared layer call: plan, device buffers, workspace."""
+
+    def __init__(self, dv, B, torch, base, q, seq_lens, W):
+        import dataclasses
+        import numpy as np
+        self.w = dataclasses.replace(base, W=W, q=q, seq_lens=np.asarray(seq_lens, np.int32))
+        self.plan = dv.plan_for(self.w)
+        self.ws = dv.workspace_for(self.plan)
+        self.t = dict(base_tensors)
+        self.t["q"] = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+        self.t["seq_lens"] = torch.from_numpy(self.w.seq_lens).cuda()
+        self.t["out"] = torch.empty((1, W, base.Hq, base.D), dtype=torch.bfloat16, device="cuda")
+        self.t["lse"] = torch.empty((1, W, base.Hq), dtype=torch.float32, device="cuda")
+        self.dv = dv
+
+    def __call__(self, events=None):
+        self.dv.run(self.plan, self.t, self.ws, events=events)
+
+
+base_tensors = {}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--flush-mib", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-w16", action="store_true", help="time the W=16 call only")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB fp32 copy kernel three times (for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a counter run)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) into the traffic record the roofline block reads")
+    args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention call of one layer runs on a "
+              "single MI355X; rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from speculative_decode_verify_sweep_amd import binding as B
+    from speculative_decode_verify_sweep_amd import device as dv
+    from workloads import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()  # fails loudly if the HIP library is missing
+    t0 = time.time()
+    base = make_workload("verify64k", W=16)
+    log(f"workload generated in {time.time() - t0:.1f}s")
+    dev = dv.upload(base)
+    base_tensors.update({k: dev[k] for k in ("k_pool", "v_pool", "k_scale", "v_scale",
+                                             "block_table")})
+    calls = {}
+    for W in WINDOWS:
+        if args.only_w16 and W != 16:
+            continue
+        q = np.ascontiguousarray(base.q[:, :W])
+        calls[W] = Call(dv, B, torch, base, q, [CTX + W], W)
+    # two-sweep foil: rows 0..7 at length L-8, rows 8..15 at length L
+    foil = [Call(dv, B, torch, base, np.ascontiguousarray(base.q[:, :8]), [CTX + 8], 8),
+            Call(dv, B, torch, base, np.ascontiguousarray(base.q[:, 8:]), [CTX + 16], 8)]
+
+    flush_buf = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def flush():
+        """Evict L2 and the Infinity Cache with a read-only pass over flush_buf."""
+        flush_buf.amax()
+
+    def timed(fn_list, steps, warmup):
+        """Cold-cache per-call timing: returns list of (total_ms, sweep_ms) per step."""
+        for i in range(warmup):
+            flush()
+            for fn in fn_list:
+                fn()
+        torch.cuda.synchronize()
+        evs = [[B.hip_event_create() for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            flush()
+            if len(fn_list) == 1:
+                fn_list[0](events=evs[i])
+            else:
+                fn_list[0](events=(evs[i][0], evs[i][1], None))
+                for fn in fn_list[1:-1]:
+                    fn()
+                fn_list[-1](events=(None, None, evs[i][2]))
+        torch.cuda.synchronize()
+        res = []
+        for e in evs:
+            tot = B.hip_event_elapsed_ms(e[0], e[2])
+            sweep = B.hip_event_elapsed_ms(e[0], e[1]) if len(fn_list) == 1 else float("nan")
+            res.append((tot, sweep))
+            for x in e:
+                B.hip_event_destroy(x)
+        return res
+
+    # --- the contract's timed region: K cold steps of the W=16 call, barrier + sync around
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    main_res = timed([calls[16]], args.steps, args.warmup)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    tot16 = [r[0] for r in main_res]
+    sw16 = [r[1] for r in main_res]
+    us16 = statistics.median(tot16) * 1e3
+    sweep_us = statistics.mean(sw16) * 1e3
+    log(f"W=16 cold: median {us16:.1f} us, mean {statistics.mean(tot16)*1e3:.1f} us, "
+        f"sweep kernel mean {sweep_us:.1f} us")
+
+    per_w = {}
+    for W, c in calls.items():
+        if W == 16:
+            per_w[W] = us16
+            continue
+        r = timed([c], args.steps, args.warmup)
+        per_w[W] = statistics.median([x[0] for x in r]) * 1e3
+        log(f"W={W} cold: median {per_w[W]:.1f} us")
+    foil_us = None
+    if not args.only_w16:
+        r = timed(foil, args.steps, args.warmup)
+        foil_us = statistics.median([x[0] for x in r]) * 1e3
+        log(f"two W=8 calls (two sweeps): median {foil_us:.1f} us")
+
+    # warm back-to-back rate of the W=16 call (no flush between calls)
+    e0, e1 = B.hip_event_create(), B.hip_event_create()
+    for _ in range(args.warmup):
+        calls[16]()
+    B.hip_event_record(e0, stream)
+    for _ in range(args.steps):
+        calls[16]()
+    B.hip_event_record(e1, stream)
+    warm_us = B.hip_event_elapsed_ms(e0, e1) * 1e3 / args.steps
+    B.hip_event_destroy(e0)
+    B.hip_event_destroy(e1)
+
+    kvb = kv_bytes([CTX + 16], base.Hkv, base.D)
+    gbps = kvb / (us16 * 1e-6) / 1e9
+    sweep_gbps = kvb / (sweep_us * 1e-6) / 1e9
+
+    traffic = None
+    if os.path.exists(COUNTERS):
+        cnt = json.load(open(COUNTERS))
+        if cnt.get("source_sha256_16") == source_hash():
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        w = calls[16].w
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            oracle.attention(w)
+            times.append(time.perf_counter() - t)
+        cpu = {"value": round(statistics.median(times) * 1e6, 1), "unit": "us/layer-call",
+               "cores": oracle.oracle_threads(), "kind": "oracle",
+               "sample": "the full 64K W=16 layer call (all 16 rows x 24 heads), fp64, "
+                         "median of 3 runs"}
+        log(f"oracle: {cpu['value']/1e3:.1f} ms on {cpu['cores']} threads")
+
+    line = {
+        "metric": "µs/layer-call and KV HBM GB/s (% of peak) at W=16, 64K ctx, bf16",
+        "value": round(us16, 2),
+        "unit": "us/layer-call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(statistics.mean(tot16), 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal verify, 64K context, W=16, 24 q / 4 KV heads, "
+                               "head_dim 256, bf16 KV, 16-token pages permuted in a "
+                               "5000-page pool, batch 1, cold cache",
+                   "context": CTX, "window": 16, "num_q_heads": 24, "num_kv_heads": 4,
+                   "head_dim": 256, "page_size": 16, "pool_pages": 5000, "batch": 1},
+        "kv_GBps": round(gbps, 1),
+        "kv_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "kv_bytes_per_call": kvb,
+        "us_per_layer_call_by_W": {str(k): round(v, 2) for k, v in per_w.items()},
+        "ratio_W16_over_W1": round(us16 / per_w[1], 3) if 1 in per_w else None,
+        "two_sweep_foil_us": round(foil_us, 2) if foil_us else None,
+        "warm_back_to_back_us": round(warm_us, 2),
+        "wall_s_timed_region_incl_flush": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "sweep_bf16<256,2,4>",
+                     "achieved": round(sweep_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(sweep_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "sweep_us_mean": round(sweep_us, 2),
+                     "bytes_per_launch": kvb},
+        "cpu_baseline": cpu,
+        "reference_context": {"pages_gpu_unnamed_64K_bf16": {"W8_us": 201, "W8_GBps": 1338,
+                                                             "W16_us": 393, "W16_GBps": 683}},
+    }
+    print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("copy calibration kernels done")
+
+
+COPY_BYTES = 256 << 20
+
+
+def _counter_rows(path):
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    return rows
+
+
+def _per_kernel(rows, counter):
+    """{kernel name: [per-dispatch value]} for one counter (values in KiB)."""
+    out = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv):
+    fetch = _per_kernel(_counter_rows(fetch_csv), "FETCH_SIZE")
+    write = _per_kernel(_counter_rows(write_csv), "WRITE_SIZE")
+
+    def pick(d, needle):
+        ks = [k for k in d if needle in k]
+        assert ks, f"no kernel matching {needle!r} in {list(d)[:8]}"
+        vals = [v for k in ks for v in d[k]]
+        return statistics.mean(vals), len(vals)
+
+    copy_f, _ = pick(fetch, "MulFunctor")
+    copy_w, _ = pick(write, "MulFunctor")
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    sw_f, n_f = pick(fetch, "sweep_bf16")
+    sw_w, n_w = pick(write, "sweep_bf16")
+    fetch_b = sw_f * 1024.0 * f_scale
+    write_b = sw_w * 1024.0 * w_scale
+    rec = {"source_sha256_16": source_hash(),
+           "kernel": "sweep_bf16 (64K, W=16)",
+           "fetch_KiB_per_dispatch": sw_f, "write_KiB_per_dispatch": sw_w,
+           "dispatches": [n_f, n_w],
+           "copy_fetch_KiB": copy_f, "copy_write_KiB": copy_w,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+           "hbm_bytes_per_launch": fetch_b + write_b,
+           "algorithmic_kv_bytes": kv_bytes([CTX + 16], 4, 256)}
+    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()

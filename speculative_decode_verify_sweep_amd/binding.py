@@ -189,6 +189,7 @@ def _hip_rt():
                                              ctypes.c_void_p]
         _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return _hip
 
 
@@ -207,6 +208,12 @@ def hip_event_elapsed_ms(a: int, b: int) -> float:
     if rc != 0:
         raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
     return float(ms.value)
+
+
+def hip_event_record(ev: int, stream) -> None:
+    rc = _hip_rt().hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(_stream(stream)))
+    if rc != 0:
+        raise RuntimeError(f"hipEventRecord failed ({rc})")
 
 
 def hip_event_destroy(ev: int) -> None:

@@ -25,6 +25,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "plan_internal.h"
 
@@ -39,6 +40,16 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Page-table window staged in LDS (pool page ids of one work unit).
+constexpr int kPtab = 512;
+// Lazy rescale: the running max is only moved when a chunk's max exceeds it
+// by more than this (base-2 units), so exp2(s - m) <= 2^8 stays well inside
+// fp32/bf16 range; final normalisation by the same sum keeps the result exact.
+constexpr float kRescaleSlack = 8.0f;
+// s_waitcnt immediate for gfx9: vmcnt(0), expcnt/lgkmcnt untouched.  The
+// compiler's wait-count pass understands this builtin, so after it no
+// compiler-issued vector load is considered in flight.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct Params {
     const uint16_t* q;
@@ -136,31 +147,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 // ----------------------------------------------------------------------------
-// Split-K sweep kernel, bf16 KV.
+// Split-K sweep kernel, bf16 KV.  512 threads = 8 wave64s; wave w owns the
+// 16-row MFMA tile w of the unit's W*G rows (W*G <= 128), and all 8 waves
+// share the DMA work.
 //   D    head dim (64/128/256)
-//   TPW  16-row MFMA tiles per wave (rows are spread over the 4 waves)
 //   NS   LDS ring depth in chunks (2 pages each)
 // LDS chunk layout (bytes):  [K page0 | K page1 | V^T page0 | V^T page1],
-// each page-head 32*D bytes.  Wave w DMAs region w.
+// each page-head 32*D bytes.  Region (w & 3), half (w >> 2) is DMA'd by wave w.
 // K rows are 16-byte-chunk swizzled: token row tau stores global chunk c at
 // slot c ^ h(tau), h(tau) = ((tau>>1)&12)|(tau&3) (masked to the row), so the
 // 16 lanes of one MFMA operand read hit distinct banks.  V^T rows (32 bytes)
 // swap their two halves when bit 2 xor bit 3 of d is set, for the same reason.
 // ----------------------------------------------------------------------------
-template <int D, int TPW, int NS>
-__global__ __launch_bounds__(kThreads, 1) void sweep_bf16(Params a) {
-    constexpr int KS = D / 32;              // MFMA k-steps over the head dim
-    constexpr int DT = D / 16;              // 16-wide d tiles of the output
-    constexpr int PAGE_BYTES = 32 * D;      // one page-head of K (or V^T), bf16
-    constexpr int STAGE = 4 * PAGE_BYTES;   // K0 K1 V0 V1
-    constexpr int LPW = PAGE_BYTES / 1024;  // DMA instructions per wave per chunk
-    constexpr int CPR = D / 8;              // 16-byte chunks per K token row
+constexpr int kSweepWaves = 8;
+constexpr int kSweepThreads = 64 * kSweepWaves;
+
+template <int D, int NS>
+__global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
+    constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
+    constexpr int DT = D / 16;                     // 16-wide d tiles of the output
+    constexpr int PAGE_BYTES = 32 * D;             // one page-head of K (or V^T), bf16
+    constexpr int STAGE = 4 * PAGE_BYTES;          // K0 K1 V0 V1
+    constexpr int LPW = PAGE_BYTES / 1024 / 2;     // DMA instructions per wave per chunk
+    constexpr int CPR = D / 8;                     // 16-byte chunks per K token row
     static_assert(LPW >= 1 && NS >= 2 && NS <= 4, "config");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+    __shared__ int32_t ptab[kPtab];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int l = tid & 63;
     const int g = l >> 4;   // lane group: MFMA k-slot group
     const int ln = l & 15;  // MFMA row/column index within a 16-tile
@@ -170,17 +186,50 @@ __global__ __launch_bounds__(kThreads, 1) void sweep_bf16(Params a) {
     const int p = un.p, kvh = un.kvh, L = un.L;
     const int npages = un.pe - un.pb;
     const int nchunks = (npages + 1) >> 1;
-    const int jend = min(L, un.pe * kPage);                    // keys past this: not in unit
-    const int lim_lo = a.causal ? (L - a.W + 1) : L;          // first key any row may not see
+    const int jend = min(L, un.pe * kPage);            // keys past this: not in the unit
+    const int lim_lo = a.causal ? (L - a.W + 1) : L;  // first key some row may not see
     const int first_masked = min(jend, lim_lo);
 
-    // ---- DMA addressing for this wave's region: per-lane offsets inside a page-head
-    const int region_pg = w & 1;
-    const bool region_v = (w >> 1) != 0;
+    // ---- this wave's query rows (tile w).  Q is loaded before the DMA ring
+    // starts so that no compiler-visible vector load is pending inside the loop.
+    const int T = (a.R + 15) >> 4;
+    const bool has_tile = w < T;
+    const int r = 16 * w + ln;
+    const int qi = r / a.G;
+    const int hi_tok = min(jend - 1, a.causal ? (L - a.W + qi) : (L - 1));
+    bf16x8_t qf[KS];
+    {
+        const bool valid = has_tile && r < a.R;
+        const int gq = r - qi * a.G;
+        const uint16_t* qrow =
+            a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
+        }
+    }
+
+    // ---- pool page ids of this unit, staged in LDS (window of kPtab pages)
+    int tbase = 0;  // unit-relative page index of ptab[0]
+    auto fill_ptab = [&](int base) {
+        for (int k = tid; k < kPtab; k += kSweepThreads)
+            if (base + k < npages) ptab[k] = phys_page(a, p, un.pb + base + k);
+    };
+    fill_ptab(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    // ---- DMA addressing: wave w moves half (w>>2) of region (w&3) of each chunk
+    const int region = w & 3;
+    const int region_pg = region & 1;
+    const bool region_v = region >= 2;
+    const int ibase = (w >> 2) * LPW;
     uint32_t goff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int qc = 64 * i + l;  // 16-byte chunk index inside the page-head (LDS order)
+        const int qc = 64 * (ibase + i) + l;  // 16-byte chunk index inside the page-head
         if (!region_v) {
             const int tr = qc / CPR, slot = qc % CPR;
             const int tau = 16 * region_pg + tr;
@@ -194,52 +243,21 @@ __global__ __launch_bounds__(kThreads, 1) void sweep_bf16(Params a) {
     }
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
     const uint8_t* const pool = region_v ? a.v : a.k;
-    const int64_t head_stride = int64_t(PAGE_BYTES);
 
     auto issue_chunk = [&](int c) {
-        int n = un.pb + 2 * c + region_pg;
-        if (n >= un.pe) n = un.pb + 2 * c;  // absent second page: reload the first, masked later
-        const int phys = phys_page(a, p, n);
-        const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * head_stride;
-        const uint32_t lds = smem_base + uint32_t((c % NS) * STAGE + w * PAGE_BYTES);
+        int n = 2 * c + region_pg;
+        if (n >= npages) n = 2 * c;  // absent second page: reload the first, masked later
+        const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
+        const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * int64_t(PAGE_BYTES);
+        const uint32_t lds = smem_base + uint32_t((c % NS) * STAGE + region * PAGE_BYTES + ibase * 1024);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
             dma16(base + goff[i], __builtin_amdgcn_readfirstlane(lds + 1024u * i));
     };
 
-    // ---- prologue: start streaming before touching Q
+    // ---- prologue: fill the ring
     const int pro = min(NS - 1, nchunks);
     for (int c = 0; c < pro; ++c) issue_chunk(c);
-
-    // ---- rows owned by this wave: global tiles w, w+4, ...
-    const int T = (a.R + 15) >> 4;
-    int ntile = 0;
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-        if (w + 4 * tt < T) ntile = tt + 1;
-
-    bf16x8_t qf[TPW][KS];
-    int hi_tok[TPW];  // last key position this lane's row may see (inclusive)
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int r = 16 * (w + 4 * tt) + ln;
-        const int i = r / a.G;
-        const int gq = r - i * a.G;
-        const bool valid = tt < ntile && r < a.R;
-        const int lim = a.causal ? (L - a.W + i) : (L - 1);
-        hi_tok[tt] = min(jend - 1, lim);
-        const uint16_t* qrow =
-            a.q + ((int64_t(p) * a.W + (valid ? i : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (valid) {
-                const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
-                qf[tt][ks] = __builtin_bit_cast(bf16x8_t, raw);
-            } else {
-                qf[tt][ks] = __builtin_bit_cast(bf16x8_t, u32x4{0u, 0u, 0u, 0u});
-            }
-        }
-    }
 
     // ---- LDS read addressing (per lane, constant over chunks)
     // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
@@ -258,138 +276,132 @@ __global__ __launch_bounds__(kThreads, 1) void sweep_bf16(Params a) {
                 kaddr[t][b] = uint32_t(row_base + 64 * ((b ^ mh) & (KS - 1)) + 16 * (g ^ ml));
         }
     }
-    uint32_t vaddr;
-    {
-        const int sv = ((ln >> 2) ^ (ln >> 3)) & 1;
-        vaddr = uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES + (2 * ln + ((g & 1) ^ sv)) * 16);
-    }
+    const uint32_t vaddr = uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES +
+                                    (2 * ln + ((g & 1) ^ (((ln >> 2) ^ (ln >> 3)) & 1))) * 16);
 
-    f32x4 acc[TPW][DT];
-    float m_run[TPW], l_run[TPW];
+    f32x4 acc[DT];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        m_run[tt] = -INFINITY;
-        l_run[tt] = 0.f;
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto process = [&](const uint8_t* st, int j0, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
+        // independent accumulation chains for MFMA pipelining
+        f32x4 s4[2][2];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // ---- main loop over chunks
-    for (int c = 0; c < nchunks; ++c) {
-        wait_stages<LPW>(min(NS - 2, nchunks - 1 - c));
-        __syncthreads();
-        if (c + NS - 1 < nchunks) issue_chunk(c + NS - 1);
-        if (ntile == 0) continue;
-
-        const uint8_t* st = smem + (c % NS) * STAGE;
-        const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
-
-        f32x4 s[TPW][2];
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) s[tt][0] = s[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t) s4[t][0] = s4[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(
-                    st + kaddr[t][ks & 3] + 256 * (ks >> 2));
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt)
-                    if (tt < ntile)
-                        s[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[tt][ks],
-                                                                            s[tt][t], 0, 0, 0);
+                const bf16x8_t kop =
+                    *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
+                s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[ks], s4[t][ks & 1],
+                                                                          0, 0, 0);
             }
         }
-
-        const bool masked = j0 + 32 > first_masked;
-        bf16x8_t pf[TPW];
+        float x[8];
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            if (tt >= ntile) continue;
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = s[tt][e >> 2][e & 3] * a.scale_log2;
-            if (masked) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tok = j0 + 8 * g + e;
-                    x[e] = tok <= hi_tok[tt] ? x[e] : -INFINITY;
-                }
-            }
-            float mx = x[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-            mx = wave_max_groups(mx);
-            const float m_new = fmaxf(m_run[tt], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[tt] - m_use);
-            m_run[tt] = m_new;
-            float psum = 0.f;
-            __bf16 pb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
-                psum += pe;
-                pb[e] = (__bf16)pe;
-            }
-            l_run[tt] = l_run[tt] * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[tt][dt] *= alpha;
-            pf[tt] = bf16x8_t{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
+        for (int e = 0; e < 8; ++e) {
+            const int t = e >> 2, j = e & 3;
+            x[e] = (s4[t][0][j] + s4[t][1][j]) * a.scale_log2;
+            if (TAIL) x[e] = (j0 + 8 * g + e <= hi_tok) ? x[e] : -INFINITY;
         }
-
-        // valid tokens of this lane group's 8-token V^T slice (stale / absent -> zero)
-        const int vcnt = min(max(jend - (j0 + 8 * g), 0), 8);
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = wave_max_groups(mx);
+        // row-uniform: the four lanes of a row hold the same mx and m_run
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__any(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+            m_run = grow ? mx : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+        l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        const bf16x8_t pf = bf16x8_t{(__bf16)pe[0], (__bf16)pe[1], (__bf16)pe[2], (__bf16)pe[3],
+                                     (__bf16)pe[4], (__bf16)pe[5], (__bf16)pe[6], (__bf16)pe[7]};
+        // O^T += V^T . P^T; stale slots past the unit's keys may hold anything
+        // (even NaN), so the tail path zeroes them in the V^T operand
+        uint32_t vkeep[4] = {~0u, ~0u, ~0u, ~0u};
+        if (TAIL) {
+            const int vcnt = min(max(jend - (j0 + 8 * g), 0), 8);
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2)
+                vkeep[k2] = (2 * k2 + 1 < vcnt) ? 0xffffffffu : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
-            if (vcnt < 8) {
+            if (TAIL) {
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) {
-                    const uint32_t keep = (2 * k2 + 1 < vcnt) ? 0xffffffffu
-                                        : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
-                    raw[k2] &= keep;
-                }
+                for (int k2 = 0; k2 < 4; ++k2) raw[k2] &= vkeep[k2];
             }
-            const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, raw);
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
-                if (tt < ntile)
-                    acc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pf[tt], acc[tt][dt],
-                                                                          0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, raw), pf,
+                                                              acc[dt], 0, 0, 0);
         }
+    };
+
+    // ---- ring step: wait for chunk c, then refill the slot freed by chunk c-1
+    auto ring_step = [&](int c) {
+        wait_stages<LPW>(min(NS - 2, nchunks - 1 - c));
+        __syncthreads();
+        const int cn = c + NS - 1;
+        if (cn < nchunks) {
+            if (2 * cn - tbase >= kPtab) {  // slide the page-table window (long units only)
+                tbase = 2 * cn;
+                fill_ptab(tbase);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __syncthreads();
+            }
+            issue_chunk(cn);
+        }
+    };
+    // Chunks that need no mask come first: the masked ones (keys past the
+    // unit's end, or past some row's causal limit) are always a suffix.
+    int c_tail = nchunks;
+    while (c_tail > 0 && (un.pb + 2 * (c_tail - 1)) * kPage + 32 > first_masked) --c_tail;
+
+    int c = 0;
+    for (; c < c_tail; ++c) {
+        ring_step(c);
+        if (has_tile) process(smem + (c % NS) * STAGE, (un.pb + 2 * c) * kPage, std::false_type{});
+    }
+    for (; c < nchunks; ++c) {
+        ring_step(c);
+        if (has_tile) process(smem + (c % NS) * STAGE, (un.pb + 2 * c) * kPage, std::true_type{});
     }
 
-    // ---- epilogue: normalise, write final output or the split partial
-    const bool direct = un.S == 1;
+    // ---- epilogue: normalise, write the final output or the split partial
+    if (!has_tile) return;
+    const float lsum = wave_sum_groups(l_run);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float lse_v = lsum > 0.f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+    if (r >= a.R) return;
+    const int h = kvh * a.G + (r - qi * a.G);
+    if (un.S == 1) {
+        uint16_t* orow = a.out + ((int64_t(p) * a.W + qi) * a.Hq + h) * D;
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        if (tt >= ntile) continue;
-        const int r = 16 * (w + 4 * tt) + ln;
-        const float lsum = wave_sum_groups(l_run[tt]);
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        const float lse_v = lsum > 0.f ? (m_run[tt] + __log2f(lsum)) * kLn2 : -INFINITY;
-        if (r >= a.R) continue;
-        const int i = r / a.G;
-        const int h = kvh * a.G + (r - i * a.G);
-        if (direct) {
-            uint16_t* orow = a.out + ((int64_t(p) * a.W + i) * a.Hq + h) * D;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f32x4 o = acc[tt][dt] * inv;
-                uint2 pk;
-                pk.x = uint32_t(f32_to_bf16_bits(o[0])) | (uint32_t(f32_to_bf16_bits(o[1])) << 16);
-                pk.y = uint32_t(f32_to_bf16_bits(o[2])) | (uint32_t(f32_to_bf16_bits(o[3])) << 16);
-                *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pk;
-            }
-            if (g == 0) a.lse[(int64_t(p) * a.W + i) * a.Hq + h] = lse_v;
-        } else {
-            float* orow = a.part_o + (int64_t(u) * a.R + r) * D;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = acc[tt][dt] * inv;
-            if (g == 0) a.part_lse[int64_t(u) * a.R + r] = lse_v;
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 o = acc[dt] * inv;
+            uint2 pk;
+            pk.x = uint32_t(f32_to_bf16_bits(o[0])) | (uint32_t(f32_to_bf16_bits(o[1])) << 16);
+            pk.y = uint32_t(f32_to_bf16_bits(o[2])) | (uint32_t(f32_to_bf16_bits(o[3])) << 16);
+            *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pk;
         }
+        if (g == 0) a.lse[(int64_t(p) * a.W + qi) * a.Hq + h] = lse_v;
+    } else {
+        float* orow = a.part_o + (int64_t(u) * a.R + r) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = acc[dt] * inv;
+        if (g == 0) a.part_lse[int64_t(u) * a.R + r] = lse_v;
     }
 }
 
@@ -438,6 +450,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
     const int d4 = tid % NQ, grp = tid / NQ;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (lse != -INFINITY) {
+#pragma unroll 4
         for (int s = grp; s < S; s += NGRP) {
             const float wgt = expf(a.part_lse[(u0 + s) * a.R + r] - lse);
             const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + ((u0 + s) * a.R + r) * D + 4 * d4);
@@ -509,10 +522,7 @@ void fill_params(Params& a, const smallw_plan* pl) {
 
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st) {
-    const int T = (pl->R + 15) / 16;
-    constexpr int NS = (D == 256) ? 4 : 4;
-    if (T <= 4) hipLaunchKernelGGL((sweep_bf16<D, 1, NS>), dim3(pl->U), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((sweep_bf16<D, 2, NS>), dim3(pl->U), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((sweep_bf16<D, 4>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
     return check_launch("sweep kernel launch");
 }
 
