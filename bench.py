@@ -246,7 +246,7 @@ def main():
         "two_sweep_foil_us": round(foil_us, 2) if foil_us else None,
         "warm_back_to_back_us": round(warm_us, 2),
         "wall_s_timed_region_incl_flush": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "sweep_bf16<256,2,4>",
+        "roofline": {"bound": "hbm", "kernel": "sweep_bf16<256,4>",
                      "achieved": round(sweep_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(sweep_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "sweep_us_mean": round(sweep_us, 2),
@@ -260,6 +260,7 @@ def main():
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
+            flush()  # the copy's source must come from HBM, as the sweep's KV does
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         log("copy calibration kernels done")
