@@ -37,7 +37,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPage = SMALLW_PAGE_SIZE;
 constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Page-table window staged in LDS (pool page ids of one work unit).
@@ -147,32 +146,72 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 // ----------------------------------------------------------------------------
-// Split-K sweep kernel, bf16 KV.  512 threads = 8 wave64s; wave w owns the
-// 16-row MFMA tile w of the unit's W*G rows (W*G <= 128), and all 8 waves
-// share the DMA work.
+// Split-K sweep kernel.  512 threads = 8 wave64s; wave w owns the 16-row MFMA
+// tile w of the unit's W*G rows (W*G <= 128), and the waves share the DMA work.
 //   D    head dim (64/128/256)
 //   NS   LDS ring depth in chunks (2 pages each)
-// LDS chunk layout (bytes):  [K page0 | K page1 | V^T page0 | V^T page1],
-// each page-head 32*D bytes.  Region (w & 3), half (w >> 2) is DMA'd by wave w.
+//   FP8  K/V stored as OCP e4m3fn codes with per-(token, KV-head) fp32 scales,
+//        dequantised to bf16 in registers (the MFMAs stay bf16)
+// LDS chunk layout (bytes): [K page0 | K page1 | V^T page0 | V^T page1], each a
+// page-head of 16*D*elt bytes; fp8 chunks add 256 bytes of scales (k page0,
+// k page1, v page0, v page1; 16 floats each) in a separate small array.
 // K rows are 16-byte-chunk swizzled: token row tau stores global chunk c at
 // slot c ^ h(tau), h(tau) = ((tau>>1)&12)|(tau&3) (masked to the row), so the
-// 16 lanes of one MFMA operand read hit distinct banks.  V^T rows (32 bytes)
-// swap their two halves when bit 2 xor bit 3 of d is set, for the same reason.
+// 16 lanes of one MFMA operand read hit distinct banks.  bf16 V^T rows (32
+// bytes) swap their halves when bit 2 xor bit 3 of d is set, for the same
+// reason; fp8 V^T rows are a single 16-byte chunk.
 // ----------------------------------------------------------------------------
 constexpr int kSweepWaves = 8;
 constexpr int kSweepThreads = 64 * kSweepWaves;
 
-template <int D, int NS>
-__global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
+__device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gaddr), "s"(lds_addr)
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 24]
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+    switch (n) {
+#define SMALLW_WAIT_CASE(k) case k: wait_vmcnt<k>(); break;
+        SMALLW_WAIT_CASE(0) SMALLW_WAIT_CASE(1) SMALLW_WAIT_CASE(2) SMALLW_WAIT_CASE(3)
+        SMALLW_WAIT_CASE(4) SMALLW_WAIT_CASE(5) SMALLW_WAIT_CASE(6) SMALLW_WAIT_CASE(7)
+        SMALLW_WAIT_CASE(8) SMALLW_WAIT_CASE(9) SMALLW_WAIT_CASE(10) SMALLW_WAIT_CASE(11)
+        SMALLW_WAIT_CASE(12) SMALLW_WAIT_CASE(13) SMALLW_WAIT_CASE(14) SMALLW_WAIT_CASE(15)
+        SMALLW_WAIT_CASE(16) SMALLW_WAIT_CASE(17) SMALLW_WAIT_CASE(18) SMALLW_WAIT_CASE(19)
+        SMALLW_WAIT_CASE(20) SMALLW_WAIT_CASE(21) SMALLW_WAIT_CASE(22) SMALLW_WAIT_CASE(23)
+#undef SMALLW_WAIT_CASE
+        default: wait_vmcnt<24>(); break;
+    }
+}
+
+// 8 e4m3fn codes (one per byte, little-endian order) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int D, int NS, bool FP8>
+__global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
+    constexpr int ELT = FP8 ? 1 : 2;
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
-    constexpr int PAGE_BYTES = 32 * D;             // one page-head of K (or V^T), bf16
+    constexpr int ROW = D * ELT;                   // bytes of one K token row
+    constexpr int PAGE_BYTES = 16 * ROW;           // one page-head of K (or V^T)
     constexpr int STAGE = 4 * PAGE_BYTES;          // K0 K1 V0 V1
-    constexpr int LPW = PAGE_BYTES / 1024 / 2;     // DMA instructions per wave per chunk
-    constexpr int CPR = D / 8;                     // 16-byte chunks per K token row
-    static_assert(LPW >= 1 && NS >= 2 && NS <= 4, "config");
+    constexpr int REG_INST = PAGE_BYTES / 1024;    // DMA instructions per region
+    constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
+    constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
+    constexpr int CPR = ROW / 16;                  // 16-byte chunks per K token row
+    static_assert(REG_INST >= 1 && NS >= 2 && NS <= 4, "config");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+    __shared__ __attribute__((aligned(16))) float scl[FP8 ? NS : 1][64];
     __shared__ int32_t ptab[kPtab];
 
     const int tid = threadIdx.x;
@@ -221,11 +260,15 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
-    // ---- DMA addressing: wave w moves half (w>>2) of region (w&3) of each chunk
+    // ---- DMA work of this wave: part (w>>2) of region (w&3) of each chunk, and
+    // for fp8 wave 7 also the chunk's 64 scales
     const int region = w & 3;
     const int region_pg = region & 1;
     const bool region_v = region >= 2;
-    const int ibase = (w >> 2) * LPW;
+    const bool issues_kv = SPLIT || w < 4;
+    const bool issues_scale = FP8 && w == kSweepWaves - 1;
+    const int nload = (issues_kv ? LPW : 0) + (issues_scale ? 1 : 0);  // per chunk
+    const int ibase = SPLIT ? (w >> 2) * LPW : 0;
     uint32_t goff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -234,7 +277,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
             const int tr = qc / CPR, slot = qc % CPR;
             const int tau = 16 * region_pg + tr;
             const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
-            goff[i] = uint32_t(tr * (2 * D) + (slot ^ hsw) * 16);
+            goff[i] = uint32_t(tr * ROW + (slot ^ hsw) * 16);
+        } else if (FP8) {
+            goff[i] = uint32_t(qc * 16);  // d-row qc: 16 token codes
         } else {
             const int d = qc >> 1, slot = qc & 1;
             const int sv = ((d >> 2) ^ (d >> 3)) & 1;
@@ -242,17 +287,31 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
         }
     }
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
+    const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
     const uint8_t* const pool = region_v ? a.v : a.k;
 
     auto issue_chunk = [&](int c) {
-        int n = 2 * c + region_pg;
-        if (n >= npages) n = 2 * c;  // absent second page: reload the first, masked later
-        const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
-        const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * int64_t(PAGE_BYTES);
-        const uint32_t lds = smem_base + uint32_t((c % NS) * STAGE + region * PAGE_BYTES + ibase * 1024);
+        if (issues_kv) {
+            int n = 2 * c + region_pg;
+            if (n >= npages) n = 2 * c;  // absent second page: reload the first, masked later
+            const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
+            const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * int64_t(PAGE_BYTES);
+            const uint32_t lds =
+                smem_base + uint32_t((c % NS) * STAGE + region * PAGE_BYTES + ibase * 1024);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            dma16(base + goff[i], __builtin_amdgcn_readfirstlane(lds + 1024u * i));
+            for (int i = 0; i < LPW; ++i)
+                dma16(base + goff[i], __builtin_amdgcn_readfirstlane(lds + 1024u * i));
+        }
+        if (issues_scale) {
+            // lane l: array l>>4 (k page0, k page1, v page0, v page1), token l&15
+            const int arr = l >> 4;
+            int n = 2 * c + (arr & 1);
+            if (n >= npages) n = 2 * c;
+            const int phys = ptab[n - tbase];
+            const float* src = (arr < 2 ? a.k_scale : a.v_scale) +
+                               (int64_t(phys) * a.Hkv + kvh) * kPage + (l & 15);
+            dma4(src, __builtin_amdgcn_readfirstlane(scl_base + uint32_t((c % NS) * 256)));
+        }
     };
 
     // ---- prologue: fill the ring
@@ -262,30 +321,40 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
     // ---- LDS read addressing (per lane, constant over chunks)
     // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
     // so lane group g of the S^T accumulators covers chunk tokens 8g+4t+j and the PV
-    // B operand of lane group g is chunk tokens 8g..8g+7 -- one 16-byte V^T read.
-    uint32_t kaddr[2][4];
-    {
-        const int mh = (ln >> 2) & (KS - 1 < 3 ? KS - 1 : 3);
-        const int ml = ln & 3;
+    // B operand of lane group g is chunk tokens 8g..8g+7 -- one V^T row segment.
+    // Row tau's swizzle key h(tau) equals ln for every t.
+    uint32_t kaddr[2][FP8 ? KS : 4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
-            const int row_base = (tau >> 4) * PAGE_BYTES + (tau & 15) * (2 * D);
+    for (int t = 0; t < 2; ++t) {
+        const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
+        const int row_base = (tau >> 4) * PAGE_BYTES + (tau & 15) * ROW;
+        if (FP8) {
+            // element block 32ks+8g: 16-byte chunk 2ks + (g>>1), half g&1
+#pragma unroll
+            for (int ks = 0; ks < (FP8 ? KS : 4); ++ks)
+                kaddr[t][ks] = uint32_t(row_base + (((2 * ks + (g >> 1)) ^ (ln & (CPR - 1))) * 16) +
+                                        8 * (g & 1));
+        } else {
+            const int mh = (ln >> 2) & (KS - 1 < 3 ? KS - 1 : 3);
+            const int ml = ln & 3;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
                 kaddr[t][b] = uint32_t(row_base + 64 * ((b ^ mh) & (KS - 1)) + 16 * (g ^ ml));
         }
     }
-    const uint32_t vaddr = uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES +
-                                    (2 * ln + ((g & 1) ^ (((ln >> 2) ^ (ln >> 3)) & 1))) * 16);
+    const uint32_t vaddr =
+        FP8 ? uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES + ln * 16 + 8 * (g & 1))
+            : uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES +
+                       (2 * ln + ((g & 1) ^ (((ln >> 2) ^ (ln >> 3)) & 1))) * 16);
 
     f32x4 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto process = [&](const uint8_t* st, int j0, auto tail_tag) {
+    auto process = [&](int slot, int j0, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
+        const uint8_t* st = smem + slot * STAGE;
         // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
         // independent accumulation chains for MFMA pipelining
         f32x4 s4[2][2];
@@ -295,17 +364,36 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const bf16x8_t kop =
-                    *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
+                bf16x8_t kop;
+                if constexpr (FP8) {
+                    const uint2 raw = *reinterpret_cast<const uint2*>(st + kaddr[t][ks]);
+                    kop = e4m3x8_to_bf16(raw.x, raw.y);
+                } else {
+                    kop = *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] +
+                                                             256 * (ks >> 2));
+                }
                 s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[ks], s4[t][ks & 1],
                                                                           0, 0, 0);
+            }
+        }
+        float ksc[8], vsc[8];
+        if constexpr (FP8) {
+            // scales of chunk tokens 8g..8g+7: k at [8g], v at [32 + 8g]
+            const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[slot][0]);
+            const f32x4 k0 = sp[2 * g], k1 = sp[2 * g + 1], v0 = sp[8 + 2 * g], v1 = sp[9 + 2 * g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ksc[e] = k0[e] * a.scale_log2;
+                ksc[e + 4] = k1[e] * a.scale_log2;
+                vsc[e] = v0[e];
+                vsc[e + 4] = v1[e];
             }
         }
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = e >> 2, j = e & 3;
-            x[e] = (s4[t][0][j] + s4[t][1][j]) * a.scale_log2;
+            x[e] = (s4[t][0][j] + s4[t][1][j]) * (FP8 ? ksc[e] : a.scale_log2);
             if (TAIL) x[e] = (j0 + 8 * g + e <= hi_tok) ? x[e] : -INFINITY;
         }
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
@@ -325,32 +413,44 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
         l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        // tokens past the unit's keys may hold anything (even NaN): zero their
+        // V^T elements (and, for fp8, their weights, since the scale may be NaN)
+        const int vcnt = TAIL ? min(max(jend - (j0 + 8 * g), 0), 8) : 8;
+        if constexpr (FP8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = (!TAIL || e < vcnt) ? pe[e] * vsc[e] : 0.f;
+        }
         const bf16x8_t pf = bf16x8_t{(__bf16)pe[0], (__bf16)pe[1], (__bf16)pe[2], (__bf16)pe[3],
                                      (__bf16)pe[4], (__bf16)pe[5], (__bf16)pe[6], (__bf16)pe[7]};
-        // O^T += V^T . P^T; stale slots past the unit's keys may hold anything
-        // (even NaN), so the tail path zeroes them in the V^T operand
-        uint32_t vkeep[4] = {~0u, ~0u, ~0u, ~0u};
-        if (TAIL) {
-            const int vcnt = min(max(jend - (j0 + 8 * g), 0), 8);
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2)
-                vkeep[k2] = (2 * k2 + 1 < vcnt) ? 0xffffffffu : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
-        }
+        // O^T += V^T . P^T
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
-            if (TAIL) {
+            bf16x8_t vop;
+            if constexpr (FP8) {
+                uint2 raw = *reinterpret_cast<const uint2*>(st + vaddr + 256 * dt);
+                if constexpr (TAIL) {  // keep the codes of the first vcnt tokens (code 0 is +0)
+                    const uint64_t keep = vcnt >= 8 ? ~0ull : ((1ull << (8 * vcnt)) - 1ull);
+                    raw.x &= uint32_t(keep);
+                    raw.y &= uint32_t(keep >> 32);
+                }
+                vop = e4m3x8_to_bf16(raw.x, raw.y);
+            } else {
+                u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+                if constexpr (TAIL) {
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) raw[k2] &= vkeep[k2];
+                    for (int k2 = 0; k2 < 4; ++k2)
+                        raw[k2] &= (2 * k2 + 1 < vcnt) ? 0xffffffffu
+                                 : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
+                }
+                vop = __builtin_bit_cast(bf16x8_t, raw);
             }
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, raw), pf,
-                                                              acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pf, acc[dt], 0, 0, 0);
         }
     };
 
     // ---- ring step: wait for chunk c, then refill the slot freed by chunk c-1
     auto ring_step = [&](int c) {
-        wait_stages<LPW>(min(NS - 2, nchunks - 1 - c));
+        wait_vmcnt_dyn(min(NS - 2, nchunks - 1 - c) * nload);
         __syncthreads();
         const int cn = c + NS - 1;
         if (cn < nchunks) {
@@ -371,11 +471,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
     int c = 0;
     for (; c < c_tail; ++c) {
         ring_step(c);
-        if (has_tile) process(smem + (c % NS) * STAGE, (un.pb + 2 * c) * kPage, std::false_type{});
+        if (has_tile) process(c % NS, (un.pb + 2 * c) * kPage, std::false_type{});
     }
     for (; c < nchunks; ++c) {
         ring_step(c);
-        if (has_tile) process(smem + (c % NS) * STAGE, (un.pb + 2 * c) * kPage, std::true_type{});
+        if (has_tile) process(c % NS, (un.pb + 2 * c) * kPage, std::true_type{});
     }
 
     // ---- epilogue: normalise, write the final output or the split partial
@@ -401,13 +501,18 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_bf16(Params a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
             *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = acc[dt] * inv;
-        if (g == 0) a.part_lse[int64_t(u) * a.R + r] = lse_v;
+        // split log-sum-exps of one row are contiguous: [unit group][row][split]
+        if (g == 0) a.part_lse[int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s] = lse_v;
     }
 }
 
 // ----------------------------------------------------------------------------
 // Log-sum-exp combine over the S_p key splits of every (p, kvh, row).
-// One workgroup per row; threads split the D/4 float4 columns x split groups.
+// One workgroup per row; thread (d4, grp) owns float4 column d4 and the splits
+// s = grp (mod NGRP).  The row's S split log-sum-exps are contiguous and the
+// same for every thread, so each thread forms the max and the normaliser
+// itself (uniform loads, no block reduction), and all of its partial-output
+// loads are issued together: one memory round trip, one LDS reduction.
 //   M = max_s lse_s;  lse = M + ln sum_s exp(lse_s - M);  o = sum_s exp(lse_s - lse) o_s
 // Fixed reduction order, so repeated calls are bitwise identical.
 // ----------------------------------------------------------------------------
@@ -415,7 +520,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
     constexpr int NQ = D / 4;
     constexpr int NGRP = kThreads / NQ;
-    __shared__ float red[kWaves];
+    constexpr int KPF = 16;  // partial loads in flight per thread
     __shared__ f32x4 part[kThreads];
 
     const int b = blockIdx.x;
@@ -426,35 +531,46 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
     const int S = (a.unit_off[p + 1] - a.unit_off[p]) / a.Hkv;
     if (S <= 1) return;
     const int64_t u0 = a.unit_off[p] + int64_t(kvh) * S;
+    const float* lrow = a.part_lse + u0 * a.R + int64_t(r) * S;
     const int tid = threadIdx.x;
-
-    float mx = -INFINITY;
-    for (int s = tid; s < S; s += kThreads) mx = fmaxf(mx, a.part_lse[(u0 + s) * a.R + r]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-
-    float sum = 0.f;
-    if (mx != -INFINITY)
-        for (int s = tid; s < S; s += kThreads) sum += expf(a.part_lse[(u0 + s) * a.R + r] - mx);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-    if ((tid & 63) == 0) red[tid >> 6] = sum;
-    __syncthreads();
-    sum = (red[0] + red[1]) + (red[2] + red[3]);
-    const float lse = (mx == -INFINITY || !(sum > 0.f)) ? -INFINITY : mx + logf(sum);
-
     const int d4 = tid % NQ, grp = tid / NQ;
+    float lse = -INFINITY;
+
+    const int lane = tid & 63;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (lse != -INFINITY) {
-#pragma unroll 4
-        for (int s = grp; s < S; s += NGRP) {
-            const float wgt = expf(a.part_lse[(u0 + s) * a.R + r] - lse);
-            const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + ((u0 + s) * a.R + r) * D + 4 * d4);
-            acc += wgt * o;
+    for (int s0 = grp; s0 < S; s0 += NGRP * KPF) {
+        // this thread's partials and their log-sum-exps, all loads in flight together
+        f32x4 o[KPF];
+        float ls[KPF];
+#pragma unroll
+        for (int k = 0; k < KPF; ++k) {
+            const int s = s0 + k * NGRP;
+            if (s < S) {
+                o[k] = *reinterpret_cast<const f32x4*>(a.part_o + ((u0 + s) * a.R + r) * D + 4 * d4);
+                ls[k] = lrow[s];
+            } else {
+                o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                ls[k] = -INFINITY;
+            }
+        }
+        // row max and normaliser over all S splits: lane-strided loads, wave reductions
+        // (every wave computes the same values; no cross-wave synchronisation)
+        const float v0 = lane < S ? lrow[lane] : -INFINITY;
+        float mx = v0;
+        for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, lrow[s]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        float sum = 0.f;
+        if (mx != -INFINITY) {
+            sum = v0 == -INFINITY ? 0.f : expf(v0 - mx);
+            for (int s = lane + 64; s < S; s += 64) sum += expf(lrow[s] - mx);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        lse = (mx == -INFINITY || !(sum > 0.f)) ? -INFINITY : mx + logf(sum);
+        if (lse != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < KPF; ++k) acc += expf(ls[k] - lse) * o[k];
         }
     }
     part[tid] = acc;
@@ -522,7 +638,10 @@ void fill_params(Params& a, const smallw_plan* pl) {
 
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st) {
-    hipLaunchKernelGGL((sweep_bf16<D, 4>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
+    if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
+        hipLaunchKernelGGL((sweep_kernel<D, 4, true>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((sweep_kernel<D, 4, false>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
     return check_launch("sweep kernel launch");
 }
 
@@ -576,7 +695,6 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
         return SMALLW_EINVAL;
     const bool fp8 = pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3;
     if (fp8 && (!k_scale || !v_scale)) return SMALLW_EINVAL;
-    if (fp8) return SMALLW_EUNSUPPORTED;  // fp8 kernels are not built yet
     if (pl->ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl->ws_bytes) return SMALLW_EWORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SMALLW_EWORKSPACE;

@@ -211,3 +211,71 @@ def test_trace_pages_match_oracle_gather(name, force):
 
 def _num_cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# ------------------------------------------------------------------ fp8-e4m3 KV
+def test_fp8_verify_batched_contexts():
+    w = make_workload("fp8")
+    announce("fp8 P=4 8K..64K W=16 (sampled rows)")
+    o, l = gpu_run(w)
+    rows = sampled_rows(w, [0, 7, 12, 23])
+    ro, rl = oracle.attention(w, rows=np.array(rows))
+    check(w, o, l, ro, rl, rows=rows)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+FP8_EDGE = [
+    dict(P=1, Hq=4, Hkv=1, D=64, ctx=(256,), W=4, causal=True),
+    dict(P=3, Hq=8, Hkv=1, D=128, ctx=(1, 17, 40), W=16, causal=True),
+    dict(P=2, Hq=12, Hkv=2, D=256, ctx=(33, 100), W=16, causal=False),
+    dict(P=4, Hq=4, Hkv=2, D=128, ctx=(7, 31, 64, 250), W=3, causal=True),
+    dict(P=1, Hq=24, Hkv=4, D=256, ctx=(3000,), W=12, causal=True),
+    dict(P=2, Hq=2, Hkv=1, D=64, ctx=(0, 5), W=1, causal=False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP8_EDGE)))
+@pytest.mark.parametrize("force", [0, 3])
+def test_fp8_edge_shapes(case, force):
+    spec = FP8_EDGE[case]
+    npg = sum(-(-(c + spec["W"]) // 16) for c in spec["ctx"])
+    w = make_workload(None, kv="fp8", placement="permuted", pool_pages=npg + 5,
+                      seed=500 + case, **spec)
+    announce(f"fp8 edge {case} {spec} force={force}")
+    o, l = gpu_run(w, force_splits=force)
+    check(w, o, l, *oracle.attention(w))
+
+
+def test_fp8_poison_and_determinism():
+    kw = dict(P=2, Hq=24, Hkv=4, D=256, ctx=(501, 77), W=16, causal=True, kv="fp8",
+              placement="permuted", pool_pages=60, seed=54)
+    a = make_workload(None, poison=True, **kw)
+    b = make_workload(None, poison=False, **kw)
+    announce("fp8 poison / determinism")
+    (oa, la), (oa2, la2) = gpu_run(a, repeats=2)
+    ob, lb = gpu_run(b)
+    assert np.isfinite(oa).all() and np.isfinite(la).all()
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(oa, oa2)
+    np.testing.assert_array_equal(la, la2)
+    check(a, oa, la, *oracle.attention(a))
+
+
+def test_fp8_every_code_decodes_exactly():
+    """Q = 0 gives uniform weights; with one token of value code c in d-row d and
+    the other 15 tokens 0, out[d] * 16 must equal the code's exact value."""
+    w = make_workload(None, P=1, Hq=1, Hkv=1, D=256, ctx=(0,), W=16, causal=False, kv="fp8",
+                      placement="in_order", pool_pages=1, seed=55, poison=False)
+    assert int(w.seq_lens[0]) == 16
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    codes[[0x7F, 0xFF]] = 0                   # the two NaN codes are never stored
+    w.q[...] = 0
+    w.v_pool[...] = 0
+    w.v_pool[0, 0, :, 0] = codes               # d-row d, token 0
+    w.v_scale[...] = 1.0
+    w.k_scale[...] = 1.0
+    announce("fp8 all codes")
+    o, _ = gpu_run(w)
+    got = o[0, 0, 0] * 16.0
+    want = oracle.decode_e4m3(codes)
+    np.testing.assert_array_equal(got, want)
