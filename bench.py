@@ -74,6 +74,11 @@ class Call:
 base_tensors = {}
 
 
+def sw_export_units(plan):
+    from speculative_decode_verify_sweep_amd import binding as B
+    return B.small_w_attention_plan_export(plan)[2]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,18 +175,49 @@ def main():
         f"sweep kernel mean {sweep_us:.1f} us")
 
     per_w = {}
+    sweep_w = {}
     for W, c in calls.items():
         if W == 16:
             per_w[W] = us16
+            sweep_w[W] = statistics.median(sw16) * 1e3
             continue
         r = timed([c], args.steps, args.warmup)
         per_w[W] = statistics.median([x[0] for x in r]) * 1e3
-        log(f"W={W} cold: median {per_w[W]:.1f} us")
+        sweep_w[W] = statistics.median([x[1] for x in r]) * 1e3
+        log(f"W={W} cold: median {per_w[W]:.1f} us (sweep {sweep_w[W]:.1f} us)")
     foil_us = None
     if not args.only_w16:
         r = timed(foil, args.steps, args.warmup)
         foil_us = statistics.median([x[0] for x in r]) * 1e3
         log(f"two W=8 calls (two sweeps): median {foil_us:.1f} us")
+
+    # the other named workloads, each as one call over its whole batch
+    others = {}
+    if not args.only_w16:
+        specs = [("verify16k W=16", dict(name="verify16k", W=16)),
+                 ("verify16k W=1", dict(name="verify16k", W=1)),
+                 ("draft P=8 W=9 non-causal", dict(name="draft")),
+                 ("fp8 P=4 8K..64K W=16", dict(name="fp8"))]
+        for label, spec in specs:
+            wl = make_workload(spec["name"], W=spec.get("W"))
+            dd = dv.upload(wl)
+            pl = dv.plan_for(wl)
+            wsb = dv.workspace_for(pl)
+
+            def fn(events=None, pl=pl, dd=dd, wsb=wsb):
+                dv.run(pl, dd, wsb, events=events)
+
+            r = timed([fn], args.steps, args.warmup)
+            t_us = statistics.median([x[0] for x in r]) * 1e3
+            s_us = statistics.median([x[1] for x in r]) * 1e3
+            b = kv_bytes(wl.seq_lens, wl.Hkv, wl.D, elt=1 if wl.kv == "fp8" else 2)
+            if wl.kv == "fp8":
+                b += int(sum(int(x) for x in wl.seq_lens)) * wl.Hkv * 8   # k and v scales
+            others[label] = {"us_per_call": round(t_us, 2), "sweep_us": round(s_us, 2),
+                             "kv_bytes": b, "kv_GBps": round(b / (t_us * 1e-6) / 1e9, 1),
+                             "units": int(sw_export_units(pl))}
+            log(f"{label}: {t_us:.1f} us (sweep {s_us:.1f}), {others[label]['kv_GBps']} GB/s")
+            del dd, wsb
 
     # warm back-to-back rate of the W=16 call (no flush between calls)
     e0, e1 = B.hip_event_create(), B.hip_event_create()
@@ -242,6 +278,7 @@ def main():
         "kv_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "kv_bytes_per_call": kvb,
         "us_per_layer_call_by_W": {str(k): round(v, 2) for k, v in per_w.items()},
+        "sweep_us_by_W": {str(k): round(v, 2) for k, v in sweep_w.items()},
         "ratio_W16_over_W1": round(us16 / per_w[1], 3) if 1 in per_w else None,
         "two_sweep_foil_us": round(foil_us, 2) if foil_us else None,
         "warm_back_to_back_us": round(warm_us, 2),
@@ -252,6 +289,7 @@ def main():
                      "sweep_us_mean": round(sweep_us, 2),
                      "bytes_per_launch": kvb},
         "cpu_baseline": cpu,
+        "other_workloads": others,
         "reference_context": {"pages_gpu_unnamed_64K_bf16": {"W8_us": 201, "W8_GBps": 1338,
                                                              "W16_us": 393, "W16_GBps": 683}},
     }

@@ -103,8 +103,9 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  *   seq_lens_host  host int32 [P]: L_p >= 0, L_p <= 16*max_pages_per_req, and
  *                  for causal calls L_p == 0 or L_p >= W.
  *   out            receives a new plan; release it with ..._plan_destroy.
- * Splits: n_p = ceil(L_p/16) pages; slots = num_cus * (1 if 16*D*elt >= 8 KiB
- * else 2); ppu = max(8, ceil(Hkv * sum n_p / slots)); S_p = ceil(n_p / ppu)
+ * Splits: n_p = ceil(L_p/16) pages; slots = num_cus * (1 if D == 256 else 2)
+ * (work units resident per compute unit); ppu = max(8, ceil(Hkv * sum n_p /
+ * slots)); S_p = ceil(n_p / ppu)
  * (or min(force_splits, n_p)), S_p = 1 for an empty request.  Work unit
  * u = unit_off[p] + kvh*S_p + s covers pages [floor(s n/S), floor((s+1) n/S)).
  * Returns SMALLW_EINVAL / SMALLW_EUNSUPPORTED on bad input (nothing allocated),

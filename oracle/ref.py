@@ -31,7 +31,7 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
     """Split plan for one call.
 
     n_pg(p)     = ceil(L_p / 16)
-    slots       = num_cus * (1 if a K page-head (16*D*elt bytes) >= 8 KiB else 2)
+    slots       = num_cus * (1 if D == 256 else 2)          units resident per CU
     total       = Hkv * sum_p n_pg(p)
     ppu         = max(8, ceil(total / slots))          pages per split
     S_p         = 1                         if n_pg(p) == 0
@@ -44,7 +44,7 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
     assert len(seq) == P
     elt = 1 if kv_fp8 else 2
     n_pg = [_ceil_div(L, PAGE) for L in seq]
-    slots = num_cus * (1 if PAGE * D * elt >= 8192 else 2)
+    slots = num_cus * (1 if D == 256 else 2)
     total = Hkv * sum(n_pg)
     ppu = max(PLAN_MIN_PAGES, _ceil_div(total, slots))
     splits = []

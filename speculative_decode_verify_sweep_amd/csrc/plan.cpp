@@ -7,7 +7,8 @@
 // GPU's compute units once, with an 8-page floor per split so the per-split
 // pipeline start and the partial traffic stay small against the KV stream:
 //   n_p   = ceil(L_p / 16)
-//   slots = num_cus * (1 if a K page-head (16*D*elt bytes) >= 8 KiB else 2)
+//   slots = num_cus * (1 if D == 256 else 2)   (units resident per CU: a D=256
+//           unit needs one CU's VGPRs and LDS; smaller heads fit two)
 //   ppu   = max(8, ceil(Hkv * sum_p n_p / slots))
 //   S_p   = 1 (empty request) | min(force_splits, n_p) | ceil(n_p / ppu)
 //   unit  u = unit_off[p] + kvh*S_p + s,  pages [floor(s n/S), floor((s+1) n/S))
@@ -62,7 +63,6 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
         pl->prob = in;
         if (!(pl->prob.scale > 0.f)) pl->prob.scale = 1.0f / std::sqrt(float(in.head_dim));
         const int P = in.num_reqs, Hkv = in.num_kv_heads, D = in.head_dim;
-        const int elt = in.kv_dtype == SMALLW_KV_FP8_E4M3 ? 1 : 2;
         pl->G = in.num_q_heads / Hkv;
         pl->R = in.window * pl->G;
         pl->seq.assign(seq, seq + P);
@@ -73,7 +73,7 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             total += pl->npg[p];
         }
         total *= Hkv;
-        const int64_t slots = int64_t(in.num_cus) * (SMALLW_PAGE_SIZE * D * elt >= 8192 ? 1 : 2);
+        const int64_t slots = int64_t(in.num_cus) * (D == 256 ? 1 : 2);
         int64_t ppu = ceil_div(total, slots);
         if (ppu < kMinPagesPerSplit) ppu = kMinPagesPerSplit;
         pl->splits.resize(P);

@@ -49,7 +49,7 @@ def plan_for(w, *, num_cus: int = 0, force_splits: int = 0) -> B.Plan:
 
 def workspace_for(plan: B.Plan, device: str = "cuda:0"):
     n = B.small_w_attention_workspace_bytes(plan)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device) if n else None
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def run(plan: B.Plan, d: dict, workspace=None, stream=None, events=None) -> None:

@@ -279,3 +279,22 @@ def test_fp8_every_code_decodes_exactly():
     got = o[0, 0, 0] * 16.0
     want = oracle.decode_e4m3(codes)
     np.testing.assert_array_equal(got, want)
+
+
+# ------------------------------------------------------------------ workspace reuse
+def test_one_workspace_shared_by_many_plans():
+    cases = [make_workload("tiny"), make_workload("verify16k", W=16),
+             make_workload("draft"), make_workload("tiny", W=2),
+             make_workload("verify16k", W=3)]
+    plans = [dv.plan_for(w, force_splits=(5 if w.name == "tiny" else 0)) for w in cases]
+    need = max(sw.small_w_attention_workspace_bytes(p) for p in plans)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # NaN-ish garbage
+    announce("shared workspace across plans")
+    for rep in range(2):
+        for w, plan in zip(cases, plans):
+            d = dv.upload(w)
+            dv.run(plan, d, ws)
+            torch.cuda.synchronize()
+            o = d["out"].float().cpu().numpy().astype(np.float64)
+            l = d["lse"].cpu().numpy().astype(np.float64)
+            check(w, o, l, *oracle.attention(w))
