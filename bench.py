@@ -93,6 +93,11 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) into the traffic record the roofline block reads")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="only run NAME (tiny, verify16k, verify64k, draft, fp8; W from "
+                         "--profile-window) --steps times, each after a cold flush, for "
+                         "counter collection; prints nothing else")
+    ap.add_argument("--profile-window", type=int, default=None)
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
@@ -111,6 +116,18 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()  # fails loudly if the HIP library is missing
+    if args.profile_workload:
+        wl = make_workload(args.profile_workload, W=args.profile_window)
+        dd = dv.upload(wl)
+        pl = dv.plan_for(wl)
+        wsb = dv.workspace_for(pl)
+        fbuf = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
+        for _ in range(args.steps):
+            fbuf.amax()
+            dv.run(pl, dd, wsb)
+        torch.cuda.synchronize()
+        log(f"profiled {args.profile_workload} W={wl.W}: {args.steps} cold calls")
+        return
     t0 = time.time()
     base = make_workload("verify64k", W=16)
     log(f"workload generated in {time.time() - t0:.1f}s")

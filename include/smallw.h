@@ -104,9 +104,9 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  *                  for causal calls L_p == 0 or L_p >= W.
  *   out            receives a new plan; release it with ..._plan_destroy.
  * Splits: n_p = ceil(L_p/16) pages; slots = num_cus * (1 if D == 256 else 2)
- * (work units resident per compute unit); ppu = max(8, ceil(Hkv * sum n_p /
- * slots)); S_p = ceil(n_p / ppu)
- * (or min(force_splits, n_p)), S_p = 1 for an empty request.  Work unit
+ * (work units resident per compute unit); S_p = max(1, min(floor(n_p * slots /
+ * (Hkv * sum_q n_q)), floor(n_p / 8))) (or min(force_splits, n_p)), S_p = 1 for
+ * an empty request.  Work unit
  * u = unit_off[p] + kvh*S_p + s covers pages [floor(s n/S), floor((s+1) n/S)).
  * Returns SMALLW_EINVAL / SMALLW_EUNSUPPORTED on bad input (nothing allocated),
  * SMALLW_EDEVICE if num_cus == 0 and the device query fails, SMALLW_ENOMEM.

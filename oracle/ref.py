@@ -33,10 +33,11 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
     n_pg(p)     = ceil(L_p / 16)
     slots       = num_cus * (1 if D == 256 else 2)          units resident per CU
     total       = Hkv * sum_p n_pg(p)
-    ppu         = max(8, ceil(total / slots))          pages per split
     S_p         = 1                         if n_pg(p) == 0
                 = min(force_splits, n_pg)   if force_splits > 0
-                = ceil(n_pg(p) / ppu)       otherwise
+                = max(1, min(floor(n_pg(p) * slots / total), floor(n_pg(p) / 8)))
+                  otherwise (a request's share of the slots, at least 8 pages a split;
+                  the floors keep sum_p Hkv*S_p <= slots whenever P*Hkv <= slots)
     unit_off[p] = Hkv * sum_{q<p} S_q;  unit u = unit_off[p] + kvh*S_p + s
     split s covers logical pages [floor(s*n/S), floor((s+1)*n/S))
     """
@@ -46,7 +47,6 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
     n_pg = [_ceil_div(L, PAGE) for L in seq]
     slots = num_cus * (1 if D == 256 else 2)
     total = Hkv * sum(n_pg)
-    ppu = max(PLAN_MIN_PAGES, _ceil_div(total, slots))
     splits = []
     for n in n_pg:
         if n == 0:
@@ -54,7 +54,7 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
         elif force_splits > 0:
             splits.append(min(force_splits, n))
         else:
-            splits.append(_ceil_div(n, ppu))
+            splits.append(max(1, min((n * slots) // total, n // PLAN_MIN_PAGES)))
     unit_off = [0]
     for s in splits:
         unit_off.append(unit_off[-1] + Hkv * s)

@@ -3,14 +3,15 @@
 // The pages name key splitting with a reduce step ("ChunkedSmallT re-streams
 // full KV per query chunk", section Finding) and a capacity function that
 // throws past the tile width (section Why no PR yet); they give no formula.
-// This planner sizes the splits so that the work units of one call fill the
-// GPU's compute units once, with an 8-page floor per split so the per-split
+// This planner gives each request a share of the GPU's resident work-unit
+// slots proportional to its pages, so one call fills the compute units once
+// without a second round, with at least 8 pages per split so the per-split
 // pipeline start and the partial traffic stay small against the KV stream:
 //   n_p   = ceil(L_p / 16)
 //   slots = num_cus * (1 if D == 256 else 2)   (units resident per CU: a D=256
 //           unit needs one CU's VGPRs and LDS; smaller heads fit two)
-//   ppu   = max(8, ceil(Hkv * sum_p n_p / slots))
-//   S_p   = 1 (empty request) | min(force_splits, n_p) | ceil(n_p / ppu)
+//   S_p   = 1 (empty request) | min(force_splits, n_p) |
+//           max(1, min(floor(n_p * slots / (Hkv * sum_q n_q)), floor(n_p / 8)))
 //   unit  u = unit_off[p] + kvh*S_p + s,  pages [floor(s n/S), floor((s+1) n/S))
 #include <cmath>
 #include <cstring>
@@ -74,8 +75,6 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
         }
         total *= Hkv;
         const int64_t slots = int64_t(in.num_cus) * (D == 256 ? 1 : 2);
-        int64_t ppu = ceil_div(total, slots);
-        if (ppu < kMinPagesPerSplit) ppu = kMinPagesPerSplit;
         pl->splits.resize(P);
         pl->unit_off.assign(P + 1, 0);
         for (int p = 0; p < P; ++p) {
@@ -83,7 +82,11 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             int64_t S;
             if (n == 0) S = 1;
             else if (in.force_splits > 0) S = in.force_splits < n ? in.force_splits : n;
-            else S = ceil_div(n, ppu);
+            else {
+                S = n * slots / total;                       // share of the slots (floor)
+                if (S > n / kMinPagesPerSplit) S = n / kMinPagesPerSplit;
+                if (S < 1) S = 1;
+            }
             pl->splits[p] = int32_t(S);
             if (S > 1) pl->any_split = true;
             const int64_t next = int64_t(pl->unit_off[p]) + Hkv * S;

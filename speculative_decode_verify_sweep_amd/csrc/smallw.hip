@@ -198,19 +198,21 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 template <int D, int NS, bool FP8>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
-    constexpr int ELT = FP8 ? 1 : 2;
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
-    constexpr int ROW = D * ELT;                   // bytes of one K token row
-    constexpr int PAGE_BYTES = 16 * ROW;           // one page-head of K (or V^T)
-    constexpr int STAGE = 4 * PAGE_BYTES;          // K0 K1 V0 V1
-    constexpr int REG_INST = PAGE_BYTES / 1024;    // DMA instructions per region
+    constexpr int BF_PAGE = 32 * D;                // bf16 page-head of K (or V^T) in LDS
+    constexpr int BF_STAGE = 4 * BF_PAGE;          // K0 K1 V0 V1, bf16
+    constexpr int ST_PAGE = FP8 ? 16 * D : BF_PAGE;    // page-head as streamed from HBM
+    constexpr int ST_STAGE = 4 * ST_PAGE;
+    constexpr int RING = NS * ST_STAGE;            // DMA ring
+    constexpr int LDS_BYTES = RING + (FP8 ? 2 * BF_STAGE : 0);  // + fp8 decode staging
+    constexpr int REG_INST = ST_PAGE / 1024;       // DMA instructions per region
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
     constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
-    constexpr int CPR = ROW / 16;                  // 16-byte chunks per K token row
-    static_assert(REG_INST >= 1 && NS >= 2 && NS <= 4, "config");
+    constexpr int CPR = D / 8;                     // 16-byte bf16 chunks per K token row
+    static_assert(REG_INST >= 1 && NS >= (FP8 ? 3 : 2), "config");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
     __shared__ __attribute__((aligned(16))) float scl[FP8 ? NS : 1][64];
     __shared__ int32_t ptab[kPtab];
 
@@ -273,13 +275,13 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int qc = 64 * (ibase + i) + l;  // 16-byte chunk index inside the page-head
-        if (!region_v) {
+        if (FP8) {
+            goff[i] = uint32_t(qc * 16);  // raw codes land unpermuted; the decoder swizzles
+        } else if (!region_v) {
             const int tr = qc / CPR, slot = qc % CPR;
             const int tau = 16 * region_pg + tr;
             const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
-            goff[i] = uint32_t(tr * ROW + (slot ^ hsw) * 16);
-        } else if (FP8) {
-            goff[i] = uint32_t(qc * 16);  // d-row qc: 16 token codes
+            goff[i] = uint32_t(tr * (2 * D) + (slot ^ hsw) * 16);
         } else {
             const int d = qc >> 1, slot = qc & 1;
             const int sv = ((d >> 2) ^ (d >> 3)) & 1;
@@ -295,9 +297,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             int n = 2 * c + region_pg;
             if (n >= npages) n = 2 * c;  // absent second page: reload the first, masked later
             const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
-            const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * int64_t(PAGE_BYTES);
+            const uint8_t* base = pool + (int64_t(phys) * a.Hkv + kvh) * int64_t(ST_PAGE);
             const uint32_t lds =
-                smem_base + uint32_t((c % NS) * STAGE + region * PAGE_BYTES + ibase * 1024);
+                smem_base + uint32_t((c % NS) * ST_STAGE + region * ST_PAGE + ibase * 1024);
 #pragma unroll
             for (int i = 0; i < LPW; ++i)
                 dma16(base + goff[i], __builtin_amdgcn_readfirstlane(lds + 1024u * i));
@@ -314,47 +316,65 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
 
+    // fp8: decode ring chunk c once for the whole workgroup into bf16 staging
+    // buffer (c & 1), in the same swizzled layout the bf16 ring uses
+    auto decode_chunk = [&](int c) {
+        const uint8_t* src = smem + (c % NS) * ST_STAGE;
+        uint8_t* dst = smem + RING + (c & 1) * BF_STAGE;
+        for (int q = tid; q < 4 * D; q += kSweepThreads) {
+            const int reg = q / D, within = q % D, pg = reg & 1;
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(src + reg * ST_PAGE + within * 16);
+            const bf16x8_t lo = e4m3x8_to_bf16(raw[0], raw[1]);
+            const bf16x8_t hi = e4m3x8_to_bf16(raw[2], raw[3]);
+            if (reg < 2) {  // K: 16 codes = elements 16cp .. 16cp+15 of token row tr
+                const int tr = within / (D / 16), cp = within % (D / 16);
+                const int tau = 16 * pg + tr;
+                const int h = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
+                uint8_t* row = dst + pg * BF_PAGE + tr * (2 * D);
+                *reinterpret_cast<bf16x8_t*>(row + ((2 * cp) ^ h) * 16) = lo;
+                *reinterpret_cast<bf16x8_t*>(row + ((2 * cp + 1) ^ h) * 16) = hi;
+            } else {        // V^T: 16 codes = tokens 0..15 of d-row `within`
+                const int sv = ((within >> 2) ^ (within >> 3)) & 1;
+                uint8_t* row = dst + 2 * BF_PAGE + pg * BF_PAGE + within * 32;
+                *reinterpret_cast<bf16x8_t*>(row + sv * 16) = lo;
+                *reinterpret_cast<bf16x8_t*>(row + (sv ^ 1) * 16) = hi;
+            }
+        }
+    };
+
     // ---- prologue: fill the ring
     const int pro = min(NS - 1, nchunks);
     for (int c = 0; c < pro; ++c) issue_chunk(c);
 
-    // ---- LDS read addressing (per lane, constant over chunks)
+    // ---- LDS read addressing (per lane, constant over chunks), bf16 layout
     // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
     // so lane group g of the S^T accumulators covers chunk tokens 8g+4t+j and the PV
-    // B operand of lane group g is chunk tokens 8g..8g+7 -- one V^T row segment.
-    // Row tau's swizzle key h(tau) equals ln for every t.
-    uint32_t kaddr[2][FP8 ? KS : 4];
+    // B operand of lane group g is chunk tokens 8g..8g+7 -- one 16-byte V^T read.
+    uint32_t kaddr[2][4];
+    {
+        const int mh = (ln >> 2) & (KS - 1 < 3 ? KS - 1 : 3);
+        const int ml = ln & 3;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
-        const int row_base = (tau >> 4) * PAGE_BYTES + (tau & 15) * ROW;
-        if (FP8) {
-            // element block 32ks+8g: 16-byte chunk 2ks + (g>>1), half g&1
-#pragma unroll
-            for (int ks = 0; ks < (FP8 ? KS : 4); ++ks)
-                kaddr[t][ks] = uint32_t(row_base + (((2 * ks + (g >> 1)) ^ (ln & (CPR - 1))) * 16) +
-                                        8 * (g & 1));
-        } else {
-            const int mh = (ln >> 2) & (KS - 1 < 3 ? KS - 1 : 3);
-            const int ml = ln & 3;
+        for (int t = 0; t < 2; ++t) {
+            const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
+            const int row_base = (tau >> 4) * BF_PAGE + (tau & 15) * (2 * D);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
                 kaddr[t][b] = uint32_t(row_base + 64 * ((b ^ mh) & (KS - 1)) + 16 * (g ^ ml));
         }
     }
-    const uint32_t vaddr =
-        FP8 ? uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES + ln * 16 + 8 * (g & 1))
-            : uint32_t(2 * PAGE_BYTES + (g >> 1) * PAGE_BYTES +
-                       (2 * ln + ((g & 1) ^ (((ln >> 2) ^ (ln >> 3)) & 1))) * 16);
+    const uint32_t vaddr = uint32_t(2 * BF_PAGE + (g >> 1) * BF_PAGE +
+                                    (2 * ln + ((g & 1) ^ (((ln >> 2) ^ (ln >> 3)) & 1))) * 16);
 
     f32x4 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto process = [&](int slot, int j0, auto tail_tag) {
+    auto process = [&](int c, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        const uint8_t* st = smem + slot * STAGE;
+        const uint8_t* st = FP8 ? smem + RING + (c & 1) * BF_STAGE : smem + (c % NS) * BF_STAGE;
+        const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
         // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
         // independent accumulation chains for MFMA pipelining
         f32x4 s4[2][2];
@@ -364,14 +384,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                bf16x8_t kop;
-                if constexpr (FP8) {
-                    const uint2 raw = *reinterpret_cast<const uint2*>(st + kaddr[t][ks]);
-                    kop = e4m3x8_to_bf16(raw.x, raw.y);
-                } else {
-                    kop = *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] +
-                                                             256 * (ks >> 2));
-                }
+                const bf16x8_t kop =
+                    *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
                 s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[ks], s4[t][ks & 1],
                                                                           0, 0, 0);
             }
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         float ksc[8], vsc[8];
         if constexpr (FP8) {
             // scales of chunk tokens 8g..8g+7: k at [8g], v at [32 + 8g]
-            const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[slot][0]);
+            const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[c % NS][0]);
             const f32x4 k0 = sp[2 * g], k1 = sp[2 * g + 1], v0 = sp[8 + 2 * g], v1 = sp[9 + 2 * g];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -425,32 +439,24 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         // O^T += V^T . P^T
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            bf16x8_t vop;
-            if constexpr (FP8) {
-                uint2 raw = *reinterpret_cast<const uint2*>(st + vaddr + 256 * dt);
-                if constexpr (TAIL) {  // keep the codes of the first vcnt tokens (code 0 is +0)
-                    const uint64_t keep = vcnt >= 8 ? ~0ull : ((1ull << (8 * vcnt)) - 1ull);
-                    raw.x &= uint32_t(keep);
-                    raw.y &= uint32_t(keep >> 32);
-                }
-                vop = e4m3x8_to_bf16(raw.x, raw.y);
-            } else {
-                u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
-                if constexpr (TAIL) {
+            u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+            if constexpr (TAIL) {
 #pragma unroll
-                    for (int k2 = 0; k2 < 4; ++k2)
-                        raw[k2] &= (2 * k2 + 1 < vcnt) ? 0xffffffffu
-                                 : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
-                }
-                vop = __builtin_bit_cast(bf16x8_t, raw);
+                for (int k2 = 0; k2 < 4; ++k2)
+                    raw[k2] &= (2 * k2 + 1 < vcnt) ? 0xffffffffu : (2 * k2 < vcnt ? 0x0000ffffu : 0u);
             }
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pf, acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, raw), pf,
+                                                              acc[dt], 0, 0, 0);
         }
     };
 
-    // ---- ring step: wait for chunk c, then refill the slot freed by chunk c-1
+    // ---- ring step for iteration c.
+    // bf16: wait for chunk c, then refill the slot freed by chunk c-1.
+    // fp8:  chunk c was decoded during iteration c-1; wait for chunk c+1 (to
+    //       decode it now), then refill the ring slot of chunk c-1.
     auto ring_step = [&](int c) {
-        wait_vmcnt_dyn(min(NS - 2, nchunks - 1 - c) * nload);
+        const int need = FP8 ? c + 1 : c;
+        if (need < nchunks) wait_vmcnt_dyn(min(NS - 2 - (FP8 ? 1 : 0), nchunks - 1 - need) * nload);
         __syncthreads();
         const int cn = c + NS - 1;
         if (cn < nchunks) {
@@ -462,7 +468,13 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             }
             issue_chunk(cn);
         }
+        if (FP8 && c + 1 < nchunks) decode_chunk(c + 1);
     };
+    if (FP8 && nchunks > 0) {  // decode chunk 0 ahead of the loop
+        wait_vmcnt_dyn(min(NS - 2, nchunks - 1) * nload);
+        __syncthreads();
+        decode_chunk(0);
+    }
     // Chunks that need no mask come first: the masked ones (keys past the
     // unit's end, or past some row's causal limit) are always a suffix.
     int c_tail = nchunks;
@@ -471,11 +483,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     int c = 0;
     for (; c < c_tail; ++c) {
         ring_step(c);
-        if (has_tile) process(c % NS, (un.pb + 2 * c) * kPage, std::false_type{});
+        if (has_tile) process(c, std::false_type{});
     }
     for (; c < nchunks; ++c) {
         ring_step(c);
-        if (has_tile) process(c % NS, (un.pb + 2 * c) * kPage, std::true_type{});
+        if (has_tile) process(c, std::true_type{});
     }
 
     // ---- epilogue: normalise, write the final output or the split partial
@@ -639,7 +651,7 @@ void fill_params(Params& a, const smallw_plan* pl) {
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st) {
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        hipLaunchKernelGGL((sweep_kernel<D, 4, true>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
+        hipLaunchKernelGGL((sweep_kernel<D, 5, true>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
     else
         hipLaunchKernelGGL((sweep_kernel<D, 4, false>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
     return check_launch("sweep kernel launch");

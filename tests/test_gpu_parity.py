@@ -298,3 +298,17 @@ def test_one_workspace_shared_by_many_plans():
             o = d["out"].float().cpu().numpy().astype(np.float64)
             l = d["lse"].cpu().numpy().astype(np.float64)
             check(w, o, l, *oracle.attention(w))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_long_unit_slides_the_page_table_window(kv):
+    """force_splits=1 at 64K: each unit streams 4097 pages, past the 512-entry
+    LDS page-table window, so the window refill path runs 8 times per unit."""
+    w = make_workload("verify64k", W=8) if kv == "bf16" else \
+        make_workload(None, P=1, Hq=24, Hkv=4, D=256, ctx=(65536,), W=8, causal=True, kv="fp8",
+                      placement="permuted", pool_pages=5000, seed=56)
+    announce(f"long unit {kv} force_splits=1")
+    o, l = gpu_run(w, force_splits=1)
+    rows = sampled_rows(w, [0, 11, 23])
+    ro, rl = oracle.attention(w, rows=np.array(rows))
+    check(w, o, l, ro, rl, rows=rows)

@@ -372,11 +372,15 @@ def test_plan_partitions_every_request_into_balanced_splits():
         pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=fp8, seq_lens=seq, num_cus=256,
                          force_splits=force)
         assert pl["U"] == Hkv * sum(pl["splits"]) == len(pl["units"])
+        if force == 0 and P * Hkv <= 256:
+            assert pl["U"] <= 256 * (1 if D == 256 else 2)   # never a second round
         k = 0
         for p in range(P):
             n, S = pl["n_pg"][p], pl["splits"][p]
             assert n == math.ceil(seq[p] / 16)
             assert 1 <= S <= max(n, 1)
+            if force == 0 and n >= 8:
+                assert n // S >= 8                    # at least 8 pages a split
             for kvh in range(Hkv):
                 edge = 0
                 for s in range(S):
@@ -389,13 +393,18 @@ def test_plan_partitions_every_request_into_balanced_splits():
 
 
 def test_plan_at_the_long_context_shapes():
-    # 64K verify: total = 4*4097 = 16388 page-heads, 256 slots -> 65 pages per
-    # split -> S = ceil(4097/65) = 64 -> 256 units, one per compute unit.
+    # 64K verify: total = 4*4097 = 16388 page-heads, 256 slots (D=256: one per
+    # CU) -> S = floor(4097*256/16388) = 64 -> 256 units, one per compute unit.
     pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[65552], num_cus=256)
     assert pl["splits"] == [64] and pl["U"] == 256
-    # 16K verify: 4*1025 = 4100 -> 17 pages per split -> S = ceil(1025/17) = 61
+    # 16K verify: S = floor(1025*256/4100) = 64, and floor(1025/8) = 128 does not bind
     pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[16400], num_cus=256)
-    assert pl["splits"] == [61]
-    # tiny: 17 pages, one head -> the 8-page floor -> S = 3
+    assert pl["splits"] == [64]
+    # fp8 batch: pages 513/1025/2049/4097 (sum 7684), 4 heads, 256 slots ->
+    # floor(n*256/30736) = 4, 8, 17, 34 -> 252 units, no second round
+    pl = oracle.plan(P=4, Hkv=4, D=256, kv_fp8=True, seq_lens=[8208, 16400, 32784, 65552],
+                     num_cus=256)
+    assert pl["splits"] == [4, 8, 17, 34] and pl["U"] == 252
+    # tiny: 17 pages, one head, 512 slots (D=64) -> the 8-page floor: floor(17/8) = 2
     pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256)
-    assert pl["splits"] == [3] and [u[3:] for u in pl["units"]] == [(0, 5), (5, 11), (11, 17)]
+    assert pl["splits"] == [2] and [u[3:] for u in pl["units"]] == [(0, 8), (8, 17)]
