@@ -376,19 +376,34 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         const uint8_t* st = FP8 ? smem + RING + (c & 1) * BF_STAGE : smem + (c % NS) * BF_STAGE;
         const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
         // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
-        // independent accumulation chains for MFMA pipelining
+        // independent accumulation chains for MFMA pipelining.  All 16 K operand
+        // reads are issued before the first MFMA so LDS latency overlaps.
+        bf16x8_t kop[KS][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                kop[ks][t] =
+                    *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
         f32x4 s4[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) s4[t][0] = s4[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bf16x8_t kop =
-                    *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
-                s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[ks], s4[t][ks & 1],
-                                                                          0, 0, 0);
-            }
+            for (int t = 0; t < 2; ++t)
+                s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks][t], qf[ks],
+                                                                          s4[t][ks & 1], 0, 0, 0);
+        // V^T operands do not depend on the softmax: at D = 256 issue their reads
+        // now so their latency hides behind it (smaller heads and the fp8 path,
+        // which also holds the scales, keep the registers)
+        constexpr bool VPRE = D == 256 && !FP8;
+        u32x4 vraw[VPRE ? DT : 1];
+        if constexpr (VPRE) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                vraw[dt] = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+            __builtin_amdgcn_sched_barrier(0);
         }
         float ksc[8], vsc[8];
         if constexpr (FP8) {
@@ -439,7 +454,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         // O^T += V^T . P^T
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            u32x4 raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+            u32x4 raw;
+            if constexpr (VPRE) raw = vraw[dt];
+            else raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
             if constexpr (TAIL) {
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2)

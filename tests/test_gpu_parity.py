@@ -50,6 +50,11 @@ def check(w, o, l, ro, rl, rows=None):
         groups = None
     assert np.isfinite(o).all(), "non-finite output"
     err = np.abs(o - ro).max()
+    nr = np.sqrt((ro ** 2).sum())
+    rr_all = np.sqrt(((o - ro) ** 2).sum()) / nr if nr > 0 else 0.0
+    fin_ = np.isfinite(rl)
+    lerr_all = np.abs(l[fin_] - rl[fin_]).max() if fin_.any() else 0.0
+    print(f"[err] max|dO|={err:.2e} relRMS={rr_all:.2e} max|dLSE|={lerr_all:.2e}", flush=True)
     assert err <= O_MAX_ABS, f"max |dO| = {err:.3e}"
     for p in range(w.P):
         a = o[groups[p]] if groups is not None else o[p]
