@@ -115,6 +115,17 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
                  : "memory");
 }
 
+// Split partials are written through L2 (sc1): the combine kernel reads them
+// right after, and dirty lines left in the eight L2s would otherwise be written
+// back in one burst when the sweep kernel ends.  Nothing in the sweep kernel
+// reads them, so the stores need no wait; the kernel's end orders them.
+__device__ __forceinline__ void store_wt(float* gaddr, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(gaddr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_wt(float* gaddr, float v) {
+    asm volatile("global_store_dword %0, %1, off sc1" : : "v"(gaddr), "v"(v) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -231,26 +242,13 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const int lim_lo = a.causal ? (L - a.W + 1) : L;  // first key some row may not see
     const int first_masked = min(jend, lim_lo);
 
-    // ---- this wave's query rows (tile w).  Q is loaded before the DMA ring
-    // starts so that no compiler-visible vector load is pending inside the loop.
+    // ---- this wave's query rows (tile w)
     const int T = (a.R + 15) >> 4;
     const bool has_tile = w < T;
     const int r = 16 * w + ln;
     const int qi = r / a.G;
     const int hi_tok = min(jend - 1, a.causal ? (L - a.W + qi) : (L - 1));
     bf16x8_t qf[KS];
-    {
-        const bool valid = has_tile && r < a.R;
-        const int gq = r - qi * a.G;
-        const uint16_t* qrow =
-            a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
-            qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
-        }
-    }
 
     // ---- pool page ids of this unit, staged in LDS (window of kPtab pages)
     int tbase = 0;  // unit-relative page index of ptab[0]
@@ -342,9 +340,24 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
 
-    // ---- prologue: fill the ring
+    // ---- prologue: start the ring, then load Q while the first chunks are in
+    // flight (one memory round trip for both), and wait for all of it here so
+    // that no compiler-visible vector load is pending inside the loop
     const int pro = min(NS - 1, nchunks);
     for (int c = 0; c < pro; ++c) issue_chunk(c);
+    {
+        const bool valid = has_tile && r < a.R;
+        const int gq = r - qi * a.G;
+        const uint16_t* qrow =
+            a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // ---- LDS read addressing (per lane, constant over chunks), bf16 layout
     // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
@@ -528,10 +541,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     } else {
         float* orow = a.part_o + (int64_t(u) * a.R + r) * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = acc[dt] * inv;
+        for (int dt = 0; dt < DT; ++dt) store_wt(orow + 16 * dt + 4 * g, acc[dt] * inv);
         // split log-sum-exps of one row are contiguous: [unit group][row][split]
-        if (g == 0) a.part_lse[int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s] = lse_v;
+        if (g == 0) store_wt(a.part_lse + int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s, lse_v);
     }
 }
 
