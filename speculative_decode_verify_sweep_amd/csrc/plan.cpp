@@ -97,11 +97,13 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
         }
         pl->U = pl->unit_off[P];
         if (pl->any_split) {
-            const size_t po = size_t(pl->U) * pl->R * D * sizeof(float);
-            const size_t pls = size_t(pl->U) * pl->R * sizeof(float);
+            // fp16 partials (16-row tiles, the last one padded), then one
+            // {lse, scale} float pair per (unit, row)
+            const size_t po = size_t(pl->U) * ((pl->R + 15) / 16 * 16) * D * 2;
+            const size_t prec = size_t(pl->U) * pl->R * 2 * sizeof(float);
             pl->part_o_off = 0;
-            pl->part_lse_off = align256(po);
-            pl->ws_bytes = pl->part_lse_off + align256(pls);
+            pl->part_rec_off = align256(po);
+            pl->ws_bytes = pl->part_rec_off + align256(prec);
         }
     } catch (...) {
         delete pl;

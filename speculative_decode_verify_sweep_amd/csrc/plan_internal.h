@@ -16,7 +16,7 @@ struct smallw_plan {
     std::vector<int32_t> npg;     // pages per request
     std::vector<int32_t> splits;  // S_p
     std::vector<int32_t> unit_off;// P + 1 prefix offsets of work units
-    size_t part_o_off = 0, part_lse_off = 0, ws_bytes = 0;
+    size_t part_o_off = 0, part_rec_off = 0, ws_bytes = 0;
     size_t max_unit_pages = 0;
 };
 

@@ -60,8 +60,8 @@ struct Params {
     const int32_t* seq;
     uint16_t* out;
     float* lse;
-    float* part_o;
-    float* part_lse;
+    uint16_t* part_o;  // split partials: fp16, lane-native blocks, rows scaled by 2^-e
+    float2* part_rec;  // per (unit, row): {base-2 lse, 2^e}, [unit group][row][split]
     int32_t P, W, Hq, Hkv, G, R, bt_stride, num_pages, causal;
     float scale_log2;  // softmax scale * log2(e): scores are kept in base 2
     int32_t unit_off[SMALLW_MAX_REQS + 1];
@@ -108,8 +108,9 @@ __device__ __forceinline__ int phys_page(const Params& a, int p, int n) {
 // 16-byte global -> LDS DMA.  Lane l's 16 bytes land at lds_addr + 16*l.
 // Issued through inline asm so the compiler does not guard every later LDS
 // read with a full vmcnt(0) wait; completion is tracked by hand with vmcnt.
+// The s_nop is the wait state an M0 write needs before an LDS DMA reads it.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gaddr), "s"(lds_addr)
                  : "memory");
@@ -118,12 +119,15 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
 // Split partials are written through L2 (sc1): the combine kernel reads them
 // right after, and dirty lines left in the eight L2s would otherwise be written
 // back in one burst when the sweep kernel ends.  Nothing in the sweep kernel
-// reads them, so the stores need no wait; the kernel's end orders them.
-__device__ __forceinline__ void store_wt(float* gaddr, f32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(gaddr), "v"(v) : "memory");
+// reads them, so the stores need no wait; the kernel's end orders them.  A
+// store wider than 8 bytes may still be reading its data registers after it
+// issues, and the compiler does not see stores inside asm, so the s_nop keeps
+// the next instruction from overwriting them too early.
+__device__ __forceinline__ void store_wt(void* gaddr, uint2 v) {
+    asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" : : "v"(gaddr), "v"(v) : "memory");
 }
-__device__ __forceinline__ void store_wt(float* gaddr, float v) {
-    asm volatile("global_store_dword %0, %1, off sc1" : : "v"(gaddr), "v"(v) : "memory");
+__device__ __forceinline__ void store_wt(void* gaddr, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(gaddr), "v"(v) : "memory");
 }
 
 template <int N>
@@ -176,7 +180,7 @@ constexpr int kSweepWaves = 8;
 constexpr int kSweepThreads = 64 * kSweepWaves;
 
 __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(gaddr), "s"(lds_addr)
                  : "memory");
@@ -524,7 +528,14 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     if (!has_tile) return;
     const float lsum = wave_sum_groups(l_run);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const float lse_v = lsum > 0.f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+    const float lse2 = lsum > 0.f ? m_run + __log2f(lsum) : -INFINITY;  // base 2
+    // largest |o| of the row (its four lanes), for the split partial's scale
+    float mabs = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mabs = fmaxf(mabs, fabsf(acc[dt][i]));
+    mabs = wave_max_groups(mabs) * inv;
     if (r >= a.R) return;
     const int h = kvh * a.G + (r - qi * a.G);
     if (un.S == 1) {
@@ -537,97 +548,178 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             pk.y = uint32_t(f32_to_bf16_bits(o[2])) | (uint32_t(f32_to_bf16_bits(o[3])) << 16);
             *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pk;
         }
-        if (g == 0) a.lse[(int64_t(p) * a.W + qi) * a.Hq + h] = lse_v;
+        if (g == 0) a.lse[(int64_t(p) * a.W + qi) * a.Hq + h] = lse2 * kLn2;
     } else {
-        float* orow = a.part_o + (int64_t(u) * a.R + r) * D;
+        // split partial in fp16, the row divided by 2^e (e the exponent of its
+        // largest |o|, so every value lies in (-1, 1) and keeps 11 significant
+        // bits relative to the row's largest); the combine multiplies 2^e back.
+        // Stored lane-native: block (u, tile w, k) is 64 lanes x 8 halves, lane
+        // l = 16g + ln holding d tiles 2k and 2k+1 of its row, so each store
+        // instruction writes 1 KiB of contiguous memory.
+        int e = 0;
+        (void)frexpf(mabs, &e);
+        e = min(max(e, -100), 127);
+        const float c = ldexpf(inv, -e);
+        uint16_t* ob = a.part_o + ((int64_t(u) * T + w) * (DT / 2)) * 512 + l * 8;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) store_wt(orow + 16 * dt + 4 * g, acc[dt] * inv);
-        // split log-sum-exps of one row are contiguous: [unit group][row][split]
-        if (g == 0) store_wt(a.part_lse + int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s, lse_v);
+        for (int k = 0; k < DT / 2; ++k) {
+            const f32x4 x0 = acc[2 * k] * c, x1 = acc[2 * k + 1] * c;
+            uint16_t hb[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hb[i] = __builtin_bit_cast(uint16_t, (_Float16)x0[i]);
+                hb[4 + i] = __builtin_bit_cast(uint16_t, (_Float16)x1[i]);
+            }
+            store_wt(ob + k * 512, u32x4{uint32_t(hb[0]) | (uint32_t(hb[1]) << 16),
+                                         uint32_t(hb[2]) | (uint32_t(hb[3]) << 16),
+                                         uint32_t(hb[4]) | (uint32_t(hb[5]) << 16),
+                                         uint32_t(hb[6]) | (uint32_t(hb[7]) << 16)});
+        }
+        // the S records of one row are contiguous: [unit group][row][split]
+        if (g == 0) {
+            const float2 rec = {lse2, ldexpf(1.f, e)};
+            store_wt(a.part_rec + int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s,
+                     __builtin_bit_cast(uint2, rec));
+        }
     }
 }
 
 // ----------------------------------------------------------------------------
 // Log-sum-exp combine over the S_p key splits of every (p, kvh, row).
-// One workgroup per row; thread (d4, grp) owns float4 column d4 and the splits
-// s = grp (mod NGRP).  The row's S split log-sum-exps are contiguous and the
-// same for every thread, so each thread forms the max and the normaliser
-// itself (uniform loads, no block reduction), and all of its partial-output
-// loads are issued together: one memory round trip, one LDS reduction.
-//   M = max_s lse_s;  lse = M + ln sum_s exp(lse_s - M);  o = sum_s exp(lse_s - lse) o_s
-// Fixed reduction order, so repeated calls are bitwise identical.
+// One workgroup per (p, kvh, 16-row tile t, d block k): the 1 KiB lane-native
+// partial block (t, k) of each split, read whole by one wave.  In base 2, with
+// the stored partial o_s = 2^e_s * h_s:
+//   M = max_s lse_s;  lse = M + log2 sum_s 2^(lse_s - M);
+//   o = sum_s 2^(lse_s - lse) * 2^e_s * h_s
+// Phase 1: the 16 rows' lse, 16 threads per row (online max/sum, shuffles).
+// Phase 2: wave v accumulates the splits s = v (mod 4), all of a lane's loads
+// in flight together.  Phase 3: the four waves' sums meet in LDS.  Fixed
+// reduction order, so repeated calls are bitwise identical.
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
-    constexpr int NQ = D / 4;
-    constexpr int NGRP = kThreads / NQ;
-    constexpr int KPF = 16;  // partial loads in flight per thread
-    __shared__ f32x4 part[kThreads];
+    constexpr int KP = D / 32;   // d blocks of two 16-wide tiles
+    constexpr int KPF = 16;      // partial loads in flight per lane
+    constexpr int RPF = 4;       // record loads in flight per phase-1 thread
+    static_assert(kThreads == 256, "four waves");
+    __shared__ float lse_row[16];
+    __shared__ f32x4 part[3][2][64];
 
-    const int b = blockIdx.x;
-    const int r = b % a.R;
-    const int pk = b / a.R;
-    const int kvh = pk % a.Hkv;
-    const int p = pk / a.Hkv;
+    const int T = (a.R + 15) >> 4;
+    int b = blockIdx.x;
+    const int k = b % KP;
+    b /= KP;
+    const int t = b % T;
+    b /= T;
+    const int kvh = b % a.Hkv;
+    const int p = b / a.Hkv;
     const int S = (a.unit_off[p + 1] - a.unit_off[p]) / a.Hkv;
     if (S <= 1) return;
     const int64_t u0 = a.unit_off[p] + int64_t(kvh) * S;
-    const float* lrow = a.part_lse + u0 * a.R + int64_t(r) * S;
     const int tid = threadIdx.x;
-    const int d4 = tid % NQ, grp = tid / NQ;
-    float lse = -INFINITY;
 
-    const int lane = tid & 63;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = grp; s0 < S; s0 += NGRP * KPF) {
-        // this thread's partials and their log-sum-exps, all loads in flight together
-        f32x4 o[KPF];
-        float ls[KPF];
+    // ---- phase 1: thread (row tid/16, part j) folds records s = j (mod 16)
+    {
+        const int rr = 16 * t + (tid >> 4), j = tid & 15;
+        float m = -INFINITY, sm = 0.f;
+        if (rr < a.R) {
+            const float2* rrow = a.part_rec + u0 * a.R + int64_t(rr) * S;
+            for (int s0 = j; s0 < S; s0 += 16 * RPF) {
+                float v[RPF];
 #pragma unroll
-        for (int k = 0; k < KPF; ++k) {
-            const int s = s0 + k * NGRP;
-            if (s < S) {
-                o[k] = *reinterpret_cast<const f32x4*>(a.part_o + ((u0 + s) * a.R + r) * D + 4 * d4);
-                ls[k] = lrow[s];
-            } else {
-                o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-                ls[k] = -INFINITY;
+                for (int q = 0; q < RPF; ++q) {
+                    const int s = s0 + 16 * q;
+                    v[q] = s < S ? rrow[s].x : -INFINITY;
+                }
+#pragma unroll
+                for (int q = 0; q < RPF; ++q) {
+                    if (v[q] == -INFINITY) continue;
+                    if (v[q] > m) {
+                        sm = sm * __builtin_amdgcn_exp2f(m - v[q]) + 1.f;
+                        m = v[q];
+                    } else {
+                        sm += __builtin_amdgcn_exp2f(v[q] - m);
+                    }
+                }
             }
         }
-        // row max and normaliser over all S splits: lane-strided loads, wave reductions
-        // (every wave computes the same values; no cross-wave synchronisation)
-        const float v0 = lane < S ? lrow[lane] : -INFINITY;
-        float mx = v0;
-        for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, lrow[s]);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        float sum = 0.f;
-        if (mx != -INFINITY) {
-            sum = v0 == -INFINITY ? 0.f : expf(v0 - mx);
-            for (int s = lane + 64; s < S; s += 64) sum += expf(lrow[s] - mx);
+        for (int off = 1; off < 16; off <<= 1) {
+            const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
+            const float mn = fmaxf(m, m2);
+            sm = (m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f(m - mn)) +
+                 (m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f(m2 - mn));
+            m = mn;
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-        lse = (mx == -INFINITY || !(sum > 0.f)) ? -INFINITY : mx + logf(sum);
-        if (lse != -INFINITY) {
-#pragma unroll
-            for (int k = 0; k < KPF; ++k) acc += expf(ls[k] - lse) * o[k];
-        }
+        if (j == 0) lse_row[tid >> 4] = (m == -INFINITY || !(sm > 0.f)) ? -INFINITY : m + __log2f(sm);
     }
-    part[tid] = acc;
     __syncthreads();
-    if (grp == 0) {
+
+    // ---- phase 2: lane l = 16g + ln of wave v: row 16t + ln, splits s = v (mod 4)
+    const int lane = tid & 63, v = tid >> 6;
+    const int ln = lane & 15, g = lane >> 4;
+    const int r = 16 * t + ln;
+    const bool valid = r < a.R;
+    const float lse = lse_row[ln];
+    const float2* rrow = a.part_rec + u0 * a.R + int64_t(valid ? r : 0) * S;
+    const uint16_t* pb = a.part_o + (int64_t(t) * KP + k) * 512 + lane * 8;
+    const int64_t ustride = int64_t(T) * KP * 512;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (valid && lse != -INFINITY) {
+        for (int s0 = v; s0 < S; s0 += 4 * KPF) {
+            u32x4 o[KPF];
+            float2 rc[KPF];
 #pragma unroll
-        for (int gg = 1; gg < NGRP; ++gg) acc += part[gg * NQ + d4];
-        const int i = r / a.G;
-        const int h = kvh * a.G + (r - i * a.G);
-        uint16_t* orow = a.out + ((int64_t(p) * a.W + i) * a.Hq + h) * D;
-        uint2 pkd;
-        pkd.x = uint32_t(f32_to_bf16_bits(acc[0])) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
-        pkd.y = uint32_t(f32_to_bf16_bits(acc[2])) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
-        *reinterpret_cast<uint2*>(orow + 4 * d4) = pkd;
-        if (tid == 0) a.lse[(int64_t(p) * a.W + i) * a.Hq + h] = lse;
+            for (int q = 0; q < KPF; ++q) {
+                const int s = s0 + 4 * q;
+                if (s < S) {
+                    o[q] = *reinterpret_cast<const u32x4*>(pb + (u0 + s) * ustride);
+                    rc[q] = rrow[s];
+                } else {
+                    o[q] = u32x4{0u, 0u, 0u, 0u};
+                    rc[q] = float2{-INFINITY, 0.f};
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < KPF; ++q) {
+                const float wgt = __builtin_amdgcn_exp2f(rc[q].x - lse) * rc[q].y;
+                f32x4 h0, h1;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    h0[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][i])));
+                    h0[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][i] >> 16)));
+                    h1[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][2 + i])));
+                    h1[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][2 + i] >> 16)));
+                }
+                acc0 += wgt * h0;
+                acc1 += wgt * h1;
+            }
+        }
     }
+
+    // ---- phase 3: waves 1..3 hand their sums to wave 0, which writes the row
+    if (v > 0) {
+        part[v - 1][0][lane] = acc0;
+        part[v - 1][1][lane] = acc1;
+    }
+    __syncthreads();
+    if (v > 0 || !valid) return;
+#pragma unroll
+    for (int vv = 0; vv < 3; ++vv) {
+        acc0 += part[vv][0][lane];
+        acc1 += part[vv][1][lane];
+    }
+    const int i = r / a.G;
+    const int h = kvh * a.G + (r - i * a.G);
+    uint16_t* orow = a.out + ((int64_t(p) * a.W + i) * a.Hq + h) * D + 32 * k + 4 * g;
+    uint2 pk;
+    pk.x = uint32_t(f32_to_bf16_bits(acc0[0])) | (uint32_t(f32_to_bf16_bits(acc0[1])) << 16);
+    pk.y = uint32_t(f32_to_bf16_bits(acc0[2])) | (uint32_t(f32_to_bf16_bits(acc0[3])) << 16);
+    *reinterpret_cast<uint2*>(orow) = pk;
+    pk.x = uint32_t(f32_to_bf16_bits(acc1[0])) | (uint32_t(f32_to_bf16_bits(acc1[1])) << 16);
+    pk.y = uint32_t(f32_to_bf16_bits(acc1[2])) | (uint32_t(f32_to_bf16_bits(acc1[3])) << 16);
+    *reinterpret_cast<uint2*>(orow + 16) = pk;
+    if (k == 0 && g == 0) a.lse[(int64_t(p) * a.W + i) * a.Hq + h] = lse * kLn2;
 }
 
 // Page-trace export: the pool pages each work unit streams, in order.
@@ -688,7 +780,8 @@ int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st) {
 
 template <int D>
 int launch_combine(const smallw_plan* pl, const Params& a, hipStream_t st) {
-    const int64_t blocks = int64_t(pl->prob.num_reqs) * pl->prob.num_kv_heads * pl->R;
+    const int64_t blocks =
+        int64_t(pl->prob.num_reqs) * pl->prob.num_kv_heads * ((pl->R + 15) / 16) * (D / 32);
     hipLaunchKernelGGL((combine_kernel<D>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, a);
     return check_launch("combine kernel launch");
 }
@@ -753,8 +846,8 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     if (pl->ws_bytes > 0) {
-        a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl->part_o_off);
-        a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl->part_lse_off);
+        a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + pl->part_o_off);
+        a.part_rec = reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) + pl->part_rec_off);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc = record(ev_start, st);

@@ -122,10 +122,11 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
                          force_splits=force)
         biggest = max(pe - pb for (_, _, _, pb, pe) in pl["units"])
         assert sw.small_w_attention_plan_max_unit_pages(plan) == biggest
-        # workspace: fp32 partial outputs and lse per unit and row, 256-byte aligned
+        # workspace: fp16 partial outputs in whole 16-row tiles and a {lse, scale}
+        # pair per unit and row, each region 256-byte aligned
         U, R = pl["U"], W * G
         a256 = lambda x: (x + 255) // 256 * 256
-        want = a256(U * R * D * 4) + a256(U * R * 4) if pl["any_split"] else 0
+        want = a256(U * (-(-R // 16) * 16) * D * 2) + a256(U * R * 8) if pl["any_split"] else 0
         assert sw.small_w_attention_workspace_bytes(plan) == want
 
 
