@@ -8,8 +8,10 @@ layer call (sweep kernel + log-sum-exp combine).  Each timed call starts from
 a cold cache: a 2 GiB buffer (8x the 256 MB Infinity Cache) is READ before it,
 outside the timed span (the pages' op bench measures cold).  The flush reads
 rather than writes so that it leaves no dirty lines whose write-back would be
-charged to the timed call.  Per-call times come from HIP events the
-library records on the stream it launches on.
+charged to the timed call.  Per-call times come from HIP events that the
+library sets from its own kernel dispatches (start of the sweep kernel, end of
+the sweep, end of the combine kernel), which is what a kernel profiler
+measures; the same calls between ordinary event markers are reported too.
 
 Prints one JSON line: microseconds per layer call at W=16 (value), the KV
 bandwidth (one sweep's K and V bytes / time, the pages' own definition) and
@@ -35,6 +37,8 @@ CTX = 65536
 WINDOWS = (1, 8, 12, 16)
 COUNTERS = os.path.join(ROOT, "profiles", "sweep_verify64k_w16_counters.json")
 SWEEP_SRC = os.path.join(ROOT, "speculative_decode_verify_sweep_amd", "csrc", "smallw.hip")
+SWEEP_KERNEL = "sweep_kernel<256, 4, false>"   # bf16 KV, head_dim 256, 4-chunk ring
+COMBINE_KERNEL = "combine_kernel<256>"
 
 
 def log(msg):
@@ -46,9 +50,17 @@ def kv_bytes(seq_lens, hkv, d, elt=2):
     return int(sum(int(x) for x in seq_lens)) * hkv * 2 * d * elt
 
 
+HOST_MARK = b"// ==== host side:"
+
+
 def source_hash():
+    """Hash of the kernel source (everything before the host-side section), so
+    that counters stay attached to the device code they were measured on."""
     with open(SWEEP_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        text = f.read()
+    cut = text.find(HOST_MARK)
+    assert cut > 0, "host-side marker missing from the kernel source"
+    return hashlib.sha256(text[:cut]).hexdigest()[:16]
 
 
 class Call:
@@ -151,42 +163,53 @@ def main():
         """Evict L2 and the Infinity Cache with a read-only pass over flush_buf."""
         flush_buf.amax()
 
-    def timed(fn_list, steps, warmup, sweep_pass=True):
+    def timed(fn_list, steps, warmup):
         """Cold-cache per-call timing: returns list of (total_ms, sweep_ms) per step.
 
-        The layer-call total is taken from events recorded before the first and
-        after the last kernel only (an event between the two kernels costs about
-        2 us itself); the sweep kernel's own time comes from a second pass of
-        the same cold calls with an event after the sweep instead."""
+        The library sets the events from the kernel dispatches themselves (start
+        of the sweep kernel, its end, end of the combine kernel), as a kernel
+        profiler does; no marker packet sits between the kernels."""
         for i in range(warmup):
             flush()
             for fn in fn_list:
                 fn()
         torch.cuda.synchronize()
+        evs = [[B.hip_event_create() for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            flush()
+            a, m, b = evs[i]
+            if len(fn_list) == 1:
+                fn_list[0](events=(a, m, b))
+            else:
+                fn_list[0](events=(a, None, None))
+                for fn in fn_list[1:-1]:
+                    fn()
+                fn_list[-1](events=(None, None, b))
+        torch.cuda.synchronize()
+        out = []
+        for a, m, b in evs:
+            tot = B.hip_event_elapsed_ms(a, b)
+            sw = B.hip_event_elapsed_ms(a, m) if len(fn_list) == 1 else float("nan")
+            out.append((tot, sw))
+            for x in (a, m, b):
+                B.hip_event_destroy(x)
+        return out
 
-        def one_pass(mid):
-            evs = [[B.hip_event_create() for _ in range(2)] for _ in range(steps)]
-            for i in range(steps):
-                flush()
-                a, b = evs[i]
-                if len(fn_list) == 1:
-                    fn_list[0](events=(a, b, None) if mid else (a, None, b))
-                else:
-                    fn_list[0](events=(a, None, None))
-                    for fn in fn_list[1:-1]:
-                        fn()
-                    fn_list[-1](events=(None, None, b))
-            torch.cuda.synchronize()
-            out = []
-            for a, b in evs:
-                out.append(B.hip_event_elapsed_ms(a, b))
-                B.hip_event_destroy(a)
-                B.hip_event_destroy(b)
-            return out
-
-        tot = one_pass(mid=False)
-        sw = one_pass(mid=True) if (sweep_pass and len(fn_list) == 1) else [float("nan")] * steps
-        return list(zip(tot, sw))
+    def timed_markers(fn, steps):
+        """The same cold calls bracketed by ordinary event markers (hipEventRecord
+        before and after): includes the markers' own cost of a few microseconds."""
+        evs = [[B.hip_event_create() for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            flush()
+            B.hip_event_record(evs[i][0], stream)
+            fn()
+            B.hip_event_record(evs[i][1], stream)
+        torch.cuda.synchronize()
+        out = [B.hip_event_elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            B.hip_event_destroy(a)
+            B.hip_event_destroy(b)
+        return out
 
     # --- the contract's timed region: K cold steps of the W=16 call, barrier + sync around
     torch.cuda.synchronize()
@@ -245,6 +268,10 @@ def main():
                              "units": int(sw_export_units(pl))}
             log(f"{label}: {t_us:.1f} us (sweep {s_us:.1f}), {others[label]['kv_GBps']} GB/s")
             del dd, wsb
+
+    # the same cold W=16 call between ordinary event markers (includes their cost)
+    marker_us = statistics.median(timed_markers(calls[16], args.steps)) * 1e3
+    log(f"W=16 cold between event markers: median {marker_us:.1f} us")
 
     # warm back-to-back rate of the W=16 call (no flush between calls)
     e0, e1 = B.hip_event_create(), B.hip_event_create()
@@ -309,8 +336,9 @@ def main():
         "ratio_W16_over_W1": round(us16 / per_w[1], 3) if 1 in per_w else None,
         "two_sweep_foil_us": round(foil_us, 2) if foil_us else None,
         "warm_back_to_back_us": round(warm_us, 2),
+        "us_per_layer_call_between_event_markers": round(marker_us, 2),
         "wall_s_timed_region_incl_flush": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "sweep_bf16<256,4>",
+        "roofline": {"bound": "hbm", "kernel": SWEEP_KERNEL,
                      "achieved": round(sweep_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(sweep_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "sweep_us_mean": round(sweep_us, 2),
@@ -367,19 +395,23 @@ def summarize_counters(fetch_csv, write_csv):
     copy_w, _ = pick(write, "MulFunctor")
     f_scale = COPY_BYTES / (copy_f * 1024.0)
     w_scale = COPY_BYTES / (copy_w * 1024.0)
-    sw_f, n_f = pick(fetch, "sweep_bf16")
-    sw_w, n_w = pick(write, "sweep_bf16")
+    sw_f, n_f = pick(fetch, SWEEP_KERNEL)
+    sw_w, n_w = pick(write, SWEEP_KERNEL)
+    cb_f, _ = pick(fetch, COMBINE_KERNEL)
+    cb_w, _ = pick(write, COMBINE_KERNEL)
     fetch_b = sw_f * 1024.0 * f_scale
     write_b = sw_w * 1024.0 * w_scale
     rec = {"source_sha256_16": source_hash(),
-           "kernel": "sweep_bf16 (64K, W=16)",
+           "kernel": SWEEP_KERNEL + " (64K, W=16)",
            "fetch_KiB_per_dispatch": sw_f, "write_KiB_per_dispatch": sw_w,
            "dispatches": [n_f, n_w],
            "copy_fetch_KiB": copy_f, "copy_write_KiB": copy_w,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
            "hbm_bytes_per_launch": fetch_b + write_b,
-           "algorithmic_kv_bytes": kv_bytes([CTX + 16], 4, 256)}
+           "algorithmic_kv_bytes": kv_bytes([CTX + 16], 4, 256),
+           "combine_hbm_fetch_bytes_per_launch": cb_f * 1024.0 * f_scale,
+           "combine_hbm_write_bytes_per_launch": cb_w * 1024.0 * w_scale}
     os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
     with open(COUNTERS, "w") as f:
         json.dump(rec, f, indent=1)

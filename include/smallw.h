@@ -136,10 +136,11 @@ int small_w_attention_run(const smallw_plan* plan, const void* q, const void* k_
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * As small_w_attention_run, and additionally records caller-created hipEvent_t
- * handles on `stream`: ev_start before the sweep kernel, ev_sweep_done after
- * it, ev_end after the combine (equal to ev_sweep_done's position when there
- * is no combine).  Any event may be NULL.  For timing the kernels in place.
+ * As small_w_attention_run, and additionally sets caller-created hipEvent_t
+ * handles (created with timing enabled) from the kernel dispatches themselves:
+ * ev_start takes the sweep kernel's start, ev_sweep_done its end, ev_end the
+ * combine kernel's end (the sweep's end when no request is split).  Any event
+ * may be NULL.  For timing the kernels in place, as a kernel profiler would.
  */
 int small_w_attention_run_events(const smallw_plan* plan, const void* q, const void* k_pool,
                                  const void* v_pool, const float* k_scale,

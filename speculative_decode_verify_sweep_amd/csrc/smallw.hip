@@ -19,6 +19,7 @@
 // row, so the online-softmax max/sum and the rescale factor are per-lane
 // scalars, and the S^T accumulator registers of two 16-token tiles are
 // exactly the B operand of the PV MFMA (no shuffle through LDS).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -732,7 +733,7 @@ __global__ void trace_kernel(Params a, int32_t* out, int64_t maxp) {
     for (; k < maxp; ++k) out[u * maxp + k] = -1;
 }
 
-// ----------------------------------------------------------------------------
+// ==== host side: launches, events, error text (device code ends above) ====
 thread_local char g_err[256] = "";
 
 }  // namespace
@@ -769,21 +770,38 @@ void fill_params(Params& a, const smallw_plan* pl) {
     for (int p = 0; p <= pr.num_reqs; ++p) a.unit_off[p] = pl->unit_off[p];
 }
 
-template <int D>
-int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st) {
-    if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        hipLaunchKernelGGL((sweep_kernel<D, 5, true>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((sweep_kernel<D, 4, false>), dim3(pl->U), dim3(kSweepThreads), 0, st, a);
-    return check_launch("sweep kernel launch");
+// Launch through hipExtLaunchKernel so optional events take the kernel's own
+// start and end timestamps (no marker packets between the kernels).
+template <typename K>
+int launch(K kernel, int64_t blocks, int threads, const Params& a, hipStream_t st, void* ev0,
+           void* ev1, const char* what) {
+    Params arg = a;
+    void* args[] = {&arg};
+    const hipError_t e =
+        hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(unsigned(blocks)),
+                           dim3(unsigned(threads)), args, 0, st, hipEvent_t(ev0), hipEvent_t(ev1), 0);
+    if (e != hipSuccess) {
+        smallw::set_device_error(what, int(e));
+        return SMALLW_EDEVICE;
+    }
+    return check_launch(what);
 }
 
 template <int D>
-int launch_combine(const smallw_plan* pl, const Params& a, hipStream_t st) {
+int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* ev0, void* ev1) {
+    if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
+        return launch(sweep_kernel<D, 5, true>, pl->U, kSweepThreads, a, st, ev0, ev1,
+                      "sweep kernel launch");
+    return launch(sweep_kernel<D, 4, false>, pl->U, kSweepThreads, a, st, ev0, ev1,
+                  "sweep kernel launch");
+}
+
+template <int D>
+int launch_combine(const smallw_plan* pl, const Params& a, hipStream_t st, void* ev1) {
     const int64_t blocks =
         int64_t(pl->prob.num_reqs) * pl->prob.num_kv_heads * ((pl->R + 15) / 16) * (D / 32);
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, a);
-    return check_launch("combine kernel launch");
+    return launch(combine_kernel<D>, blocks, kThreads, a, st, nullptr, ev1,
+                  "combine kernel launch");
 }
 
 int record(void* ev, hipStream_t st) {
@@ -850,25 +868,23 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
         a.part_rec = reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) + pl->part_rec_off);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int rc = record(ev_start, st);
-    if (rc) return rc;
+    // the sweep's end timestamp goes to ev_sweep_done, and to ev_end too when
+    // there is no combine (then a marker copies it if both were asked for)
+    void* sweep_stop = pl->any_split ? ev_sweep_done : (ev_sweep_done ? ev_sweep_done : ev_end);
+    int rc;
     switch (pl->prob.head_dim) {
-        case 64: rc = launch_sweep<64>(pl, a, st); break;
-        case 128: rc = launch_sweep<128>(pl, a, st); break;
-        case 256: rc = launch_sweep<256>(pl, a, st); break;
+        case 64: rc = launch_sweep<64>(pl, a, st, ev_start, sweep_stop); break;
+        case 128: rc = launch_sweep<128>(pl, a, st, ev_start, sweep_stop); break;
+        case 256: rc = launch_sweep<256>(pl, a, st, ev_start, sweep_stop); break;
         default: return SMALLW_EUNSUPPORTED;
     }
     if (rc) return rc;
-    if ((rc = record(ev_sweep_done, st))) return rc;
-    if (pl->any_split) {
-        switch (pl->prob.head_dim) {
-            case 64: rc = launch_combine<64>(pl, a, st); break;
-            case 128: rc = launch_combine<128>(pl, a, st); break;
-            default: rc = launch_combine<256>(pl, a, st); break;
-        }
-        if (rc) return rc;
+    if (!pl->any_split) return (ev_sweep_done && ev_end) ? record(ev_end, st) : SMALLW_OK;
+    switch (pl->prob.head_dim) {
+        case 64: return launch_combine<64>(pl, a, st, ev_end);
+        case 128: return launch_combine<128>(pl, a, st, ev_end);
+        default: return launch_combine<256>(pl, a, st, ev_end);
     }
-    return record(ev_end, st);
 }
 
 int small_w_attention_run(const smallw_plan* pl, const void* q, const void* k_pool,
