@@ -226,10 +226,14 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
     constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
     constexpr int CPR = D / 8;                     // 16-byte bf16 chunks per K token row
+    // chunks in flight ahead of the one being computed: fp8 frees a ring slot
+    // when its chunk is decoded, one iteration before the chunk is computed
+    constexpr int AHEAD = FP8 ? NS : NS - 1;
+    constexpr int NSS = FP8 ? NS + 1 : 1;          // fp8 scale slots: chunks c .. c+NS live
     static_assert(REG_INST >= 1 && NS >= (FP8 ? 3 : 2), "config");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) float scl[FP8 ? NS : 1][64];
+    __shared__ __attribute__((aligned(16))) float scl[FP8 ? NSS : 1][64];
     __shared__ int32_t ptab[kPtab];
 
     const int tid = threadIdx.x;
@@ -294,6 +298,12 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
     const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
     const uint8_t* const pool = region_v ? a.v : a.k;
+    // The scale DMA picks k_scale or v_scale per lane.  Kept opaque in SGPRs so
+    // the compiler cannot turn that select into a per-lane load of the pointer
+    // from the kernel arguments, whose vmcnt(0) wait would drain the ring.
+    const float* kscale = a.k_scale;
+    const float* vscale = a.v_scale;
+    asm volatile("" : "+s"(kscale), "+s"(vscale));
 
     auto issue_chunk = [&](int c) {
         if (issues_kv) {
@@ -313,9 +323,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             int n = 2 * c + (arr & 1);
             if (n >= npages) n = 2 * c;
             const int phys = ptab[n - tbase];
-            const float* src = (arr < 2 ? a.k_scale : a.v_scale) +
+            const float* src = (arr < 2 ? kscale : vscale) +
                                (int64_t(phys) * a.Hkv + kvh) * kPage + (l & 15);
-            dma4(src, __builtin_amdgcn_readfirstlane(scl_base + uint32_t((c % NS) * 256)));
+            dma4(src, __builtin_amdgcn_readfirstlane(scl_base + uint32_t((c % NSS) * 256)));
         }
     };
 
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- prologue: start the ring, then load Q while the first chunks are in
     // flight (one memory round trip for both), and wait for all of it here so
     // that no compiler-visible vector load is pending inside the loop
-    const int pro = min(NS - 1, nchunks);
+    const int pro = min(AHEAD, nchunks);
     for (int c = 0; c < pro; ++c) issue_chunk(c);
     {
         const bool valid = has_tile && r < a.R;
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         float ksc[8], vsc[8];
         if constexpr (FP8) {
             // scales of chunk tokens 8g..8g+7: k at [8g], v at [32 + 8g]
-            const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[c % NS][0]);
+            const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[c % NSS][0]);
             const f32x4 k0 = sp[2 * g], k1 = sp[2 * g + 1], v0 = sp[8 + 2 * g], v1 = sp[9 + 2 * g];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -486,14 +496,17 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     };
 
     // ---- ring step for iteration c.
-    // bf16: wait for chunk c, then refill the slot freed by chunk c-1.
-    // fp8:  chunk c was decoded during iteration c-1; wait for chunk c+1 (to
-    //       decode it now), then refill the ring slot of chunk c-1.
+    // bf16: wait for chunk c, then refill the slot freed by chunk c-1 with
+    //       chunk c+NS-1.
+    // fp8:  chunk c was decoded (out of its ring slot) during iteration c-1;
+    //       wait for chunk c+1 (to decode it now), then refill chunk c's slot
+    //       with chunk c+NS.  Either way NS-2 chunks stay in flight past the
+    //       one waited for.
     auto ring_step = [&](int c) {
         const int need = FP8 ? c + 1 : c;
-        if (need < nchunks) wait_vmcnt_dyn(min(NS - 2 - (FP8 ? 1 : 0), nchunks - 1 - need) * nload);
+        if (need < nchunks) wait_vmcnt_dyn(min(NS - 2, nchunks - 1 - need) * nload);
         __syncthreads();
-        const int cn = c + NS - 1;
+        const int cn = c + AHEAD;
         if (cn < nchunks) {
             if (2 * cn - tbase >= kPtab) {  // slide the page-table window (long units only)
                 tbase = 2 * cn;
@@ -506,7 +519,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         if (FP8 && c + 1 < nchunks) decode_chunk(c + 1);
     };
     if (FP8 && nchunks > 0) {  // decode chunk 0 ahead of the loop
-        wait_vmcnt_dyn(min(NS - 2, nchunks - 1) * nload);
+        wait_vmcnt_dyn(min(AHEAD - 1, nchunks - 1) * nload);
         __syncthreads();
         decode_chunk(0);
     }
