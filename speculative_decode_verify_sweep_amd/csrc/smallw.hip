@@ -605,17 +605,32 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 // the stored partial o_s = 2^e_s * h_s:
 //   M = max_s lse_s;  lse = M + log2 sum_s 2^(lse_s - M);
 //   o = sum_s 2^(lse_s - lse) * 2^e_s * h_s
-// Phase 1: the 16 rows' lse, 16 threads per row (online max/sum, shuffles).
-// Phase 2: wave v accumulates the splits s = v (mod 4), all of a lane's loads
-// in flight together.  Phase 3: the four waves' sums meet in LDS.  Fixed
-// reduction order, so repeated calls are bitwise identical.
+// Row phase: 16 threads per row load that row's records (contiguous), fold
+// them into a running (max, sum), merge by shuffles and leave the weights
+// 2^(lse_s - lse) * 2^e_s in LDS.  Column phase: lane l = 16g + ln of wave v
+// owns row 16t + ln, its 8 columns of block k and the splits s = v (mod 4).
+// Every lane issues its partial-block loads right after the record loads, so
+// both are in flight together (one memory round trip when S <= 64).  The
+// waves' sums meet in LDS in a fixed order: repeated calls are bitwise equal.
 // ----------------------------------------------------------------------------
+__device__ __forceinline__ void lse_fold(float& m, float& sm, float v) {
+    if (v == -INFINITY) return;
+    if (v > m) {
+        sm = sm * __builtin_amdgcn_exp2f(m - v) + 1.f;
+        m = v;
+    } else {
+        sm += __builtin_amdgcn_exp2f(v - m);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
-    constexpr int KP = D / 32;   // d blocks of two 16-wide tiles
-    constexpr int KPF = 16;      // partial loads in flight per lane
-    constexpr int RPF = 4;       // record loads in flight per phase-1 thread
+    constexpr int KP = D / 32;    // d blocks of two 16-wide tiles
+    constexpr int KPF = 16;       // partial blocks per lane per batch
+    constexpr int BATCH = 4 * KPF;  // splits per batch
+    constexpr int RPT = BATCH / 16;  // records per row-phase thread per batch
     static_assert(kThreads == 256, "four waves");
+    __shared__ float wts[16][BATCH + 1];
     __shared__ float lse_row[16];
     __shared__ f32x4 part[3][2][64];
 
@@ -632,86 +647,89 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
     const int64_t u0 = a.unit_off[p] + int64_t(kvh) * S;
     const int tid = threadIdx.x;
 
-    // ---- phase 1: thread (row tid/16, part j) folds records s = j (mod 16)
-    {
-        const int rr = 16 * t + (tid >> 4), j = tid & 15;
-        float m = -INFINITY, sm = 0.f;
-        if (rr < a.R) {
-            const float2* rrow = a.part_rec + u0 * a.R + int64_t(rr) * S;
-            for (int s0 = j; s0 < S; s0 += 16 * RPF) {
-                float v[RPF];
-#pragma unroll
-                for (int q = 0; q < RPF; ++q) {
-                    const int s = s0 + 16 * q;
-                    v[q] = s < S ? rrow[s].x : -INFINITY;
-                }
-#pragma unroll
-                for (int q = 0; q < RPF; ++q) {
-                    if (v[q] == -INFINITY) continue;
-                    if (v[q] > m) {
-                        sm = sm * __builtin_amdgcn_exp2f(m - v[q]) + 1.f;
-                        m = v[q];
-                    } else {
-                        sm += __builtin_amdgcn_exp2f(v[q] - m);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
-            const float mn = fmaxf(m, m2);
-            sm = (m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f(m - mn)) +
-                 (m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f(m2 - mn));
-            m = mn;
-        }
-        if (j == 0) lse_row[tid >> 4] = (m == -INFINITY || !(sm > 0.f)) ? -INFINITY : m + __log2f(sm);
-    }
-    __syncthreads();
-
-    // ---- phase 2: lane l = 16g + ln of wave v: row 16t + ln, splits s = v (mod 4)
+    // row phase mapping: row pr of the tile, records s = pj (mod 16)
+    const int pr = tid >> 4, pj = tid & 15;
+    const bool pvalid = 16 * t + pr < a.R;
+    const float2* prow = a.part_rec + u0 * a.R + int64_t(pvalid ? 16 * t + pr : 0) * S;
+    // column phase mapping
     const int lane = tid & 63, v = tid >> 6;
     const int ln = lane & 15, g = lane >> 4;
     const int r = 16 * t + ln;
     const bool valid = r < a.R;
-    const float lse = lse_row[ln];
-    const float2* rrow = a.part_rec + u0 * a.R + int64_t(valid ? r : 0) * S;
     const uint16_t* pb = a.part_o + (int64_t(t) * KP + k) * 512 + lane * 8;
     const int64_t ustride = int64_t(T) * KP * 512;
+
+    // records of the first batch, then partial blocks: all in flight together
+    // (indices clamped to a written split; weights past S are zero)
+    float2 rv[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) rv[q] = prow[min(pj + 16 * q, S - 1)];
+    u32x4 o[KPF];
+#pragma unroll
+    for (int q = 0; q < KPF; ++q)
+        o[q] = *reinterpret_cast<const u32x4*>(pb + (u0 + min(v + 4 * q, S - 1)) * ustride);
+
+    // the row's lse over all S records
+    float m = -INFINITY, sm = 0.f;
+    if (pvalid) {
+#pragma unroll
+        for (int q = 0; q < RPT; ++q)
+            if (pj + 16 * q < S) lse_fold(m, sm, rv[q].x);
+        for (int s = pj + BATCH; s < S; s += 16) lse_fold(m, sm, prow[s].x);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
+        const float mn = fmaxf(m, m2);
+        if (mn != -INFINITY) {
+            sm = (m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f(m - mn)) +
+                 (m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f(m2 - mn));
+            m = mn;
+        }
+    }
+    const float lse_p = (m == -INFINITY || !(sm > 0.f)) ? -INFINITY : m + __log2f(sm);
+    if (pj == 0) lse_row[pr] = lse_p;
+    auto weight = [&](float2 rec, int s) {
+        return (pvalid && s < S && lse_p != -INFINITY)
+                   ? __builtin_amdgcn_exp2f(rec.x - lse_p) * rec.y : 0.f;
+    };
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) wts[pr][pj + 16 * q] = weight(rv[q], pj + 16 * q);
+    __syncthreads();
+    const float lse = lse_row[ln];
+
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (valid && lse != -INFINITY) {
-        for (int s0 = v; s0 < S; s0 += 4 * KPF) {
-            u32x4 o[KPF];
-            float2 rc[KPF];
+    for (int s0 = 0; s0 < S; s0 += BATCH) {
+        if (s0 > 0) {  // more than one batch of splits: refill weights and blocks
+            __syncthreads();
 #pragma unroll
-            for (int q = 0; q < KPF; ++q) {
-                const int s = s0 + 4 * q;
-                if (s < S) {
-                    o[q] = *reinterpret_cast<const u32x4*>(pb + (u0 + s) * ustride);
-                    rc[q] = rrow[s];
-                } else {
-                    o[q] = u32x4{0u, 0u, 0u, 0u};
-                    rc[q] = float2{-INFINITY, 0.f};
-                }
+            for (int q = 0; q < RPT; ++q) {
+                const int s = s0 + pj + 16 * q;
+                wts[pr][pj + 16 * q] = weight(prow[min(s, S - 1)], s);
             }
 #pragma unroll
-            for (int q = 0; q < KPF; ++q) {
-                const float wgt = __builtin_amdgcn_exp2f(rc[q].x - lse) * rc[q].y;
-                f32x4 h0, h1;
+            for (int q = 0; q < KPF; ++q)
+                o[q] = *reinterpret_cast<const u32x4*>(pb + (u0 + min(s0 + v + 4 * q, S - 1)) *
+                                                                ustride);
+            __syncthreads();
+        }
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    h0[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][i])));
-                    h0[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][i] >> 16)));
-                    h1[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][2 + i])));
-                    h1[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][2 + i] >> 16)));
-                }
-                acc0 += wgt * h0;
-                acc1 += wgt * h1;
+        for (int q = 0; q < KPF; ++q) {
+            const float wgt = wts[ln][v + 4 * q];
+            f32x4 h0, h1;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                h0[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][i])));
+                h0[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][i] >> 16)));
+                h1[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][2 + i])));
+                h1[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(o[q][2 + i] >> 16)));
             }
+            acc0 += wgt * h0;
+            acc1 += wgt * h1;
         }
     }
 
-    // ---- phase 3: waves 1..3 hand their sums to wave 0, which writes the row
+    // ---- waves 1..3 hand their sums to wave 0, which writes the row
     if (v > 0) {
         part[v - 1][0][lane] = acc0;
         part[v - 1][1][lane] = acc1;
