@@ -54,13 +54,19 @@ HOST_MARK = b"// ==== host side:"
 
 
 def source_hash():
-    """Hash of the kernel source (everything before the host-side section), so
-    that counters stay attached to the device code they were measured on."""
+    """Hash of the kernel source (everything before the host-side section, with
+    comments and blank space removed), so that counters stay attached to the
+    device code they were measured on and comment edits do not detach them."""
+    import re
     with open(SWEEP_SRC, "rb") as f:
         text = f.read()
     cut = text.find(HOST_MARK)
     assert cut > 0, "host-side marker missing from the kernel source"
-    return hashlib.sha256(text[:cut]).hexdigest()[:16]
+    code = text[:cut].decode()
+    code = re.sub(r"/\*.*?\*/", "", code, flags=re.S)
+    code = re.sub(r"//[^\n]*", "", code)
+    code = re.sub(r"\s+", " ", code).strip()
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 class Call:

@@ -8,11 +8,11 @@
 // unit holds ALL W*G query rows of its KV head, so every K/V byte of the
 // visible context is streamed from HBM exactly once per call.
 //
-// Work unit u = (request p, KV head kvh, key split s), one 256-thread
-// workgroup (4 wave64s).  The unit walks its pages two at a time ("chunks" of
-// 32 tokens) through an NSTAGE-deep ring of LDS buffers that the four waves
-// fill with 16-byte global->LDS DMA loads, each load instruction moving 1 KiB
-// of one page-head.  Rows are the N side of the MFMAs:
+// Work unit u = (request p, KV head kvh, key split s), one 512-thread
+// workgroup (8 wave64s).  The unit walks its pages two at a time ("chunks" of
+// 32 tokens) through an NS-deep ring of LDS buffers that the eight waves fill
+// with 16-byte global->LDS DMA loads, each load instruction moving 1 KiB of
+// one page-head.  Rows are the N side of the MFMAs:
 //   S^T[token][row]  = K[token][:] . Q[row][:]       (v_mfma_f32_16x16x32_bf16)
 //   O^T[d][row]     += V^T[d][token] . P^T[token][row]
 // In this orientation a lane's accumulator registers all belong to one query
@@ -136,14 +136,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Wait until at most k*LPW of this wave's DMA loads are still in flight.
-template <int LPW>
-__device__ __forceinline__ void wait_stages(int k) {
-    if (k <= 0) wait_vmcnt<0>();
-    else if (k == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<2 * LPW>();
-}
-
 __device__ __forceinline__ float wave_max_groups(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));
     x = fmaxf(x, __shfl_xor(x, 32));
@@ -167,7 +159,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 //   D    head dim (64/128/256)
 //   NS   LDS ring depth in chunks (2 pages each)
 //   FP8  K/V stored as OCP e4m3fn codes with per-(token, KV-head) fp32 scales,
-//        dequantised to bf16 in registers (the MFMAs stay bf16)
+//        decoded to bf16 once per chunk into an LDS staging tile (the MFMAs
+//        stay bf16); the scales multiply S and P
 // LDS chunk layout (bytes): [K page0 | K page1 | V^T page0 | V^T page1], each a
 // page-head of 16*D*elt bytes; fp8 chunks add 256 bytes of scales (k page0,
 // k page1, v page0, v page1; 16 floats each) in a separate small array.
