@@ -253,11 +253,13 @@ def main():
         specs = [("verify16k W=16", dict(name="verify16k", W=16)),
                  ("verify16k W=1", dict(name="verify16k", W=1)),
                  ("draft P=8 W=9 non-causal", dict(name="draft")),
-                 ("fp8 P=4 8K..64K W=16", dict(name="fp8"))]
+                 ("fp8 P=4 8K..64K W=16", dict(name="fp8")),
+                 ("verify64k W=16 row-exact, 65-page splits",
+                  dict(name="verify64k", W=16, split_pages=65))]
         for label, spec in specs:
             wl = make_workload(spec["name"], W=spec.get("W"))
             dd = dv.upload(wl)
-            pl = dv.plan_for(wl)
+            pl = dv.plan_for(wl, split_pages=spec.get("split_pages", 0))
             wsb = dv.workspace_for(pl)
 
             def fn(events=None, pl=pl, dd=dd, wsb=wsb):

@@ -93,6 +93,13 @@ typedef struct smallw_problem {
     int32_t num_cus;           /* compute units to plan for; 0 = ask current device  */
     int32_t force_splits;      /* 0 = automatic; > 0 = this many key splits per
                                   request (capped at its page count)                 */
+    int32_t split_pages;       /* 0 = automatic; > 0 = row-exact mode: every request
+                                  is split at multiples of this many pages, counted
+                                  from its first page, and every row is finished by
+                                  the combine kernel, so a row's result depends only
+                                  on its own query, keys and values: it is bitwise
+                                  the same whatever W, the other rows and the other
+                                  requests are (exclusive with force_splits)         */
 } smallw_problem;
 
 typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
@@ -108,6 +115,9 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  * (Hkv * sum_q n_q)), floor(n_p / 8))) (or min(force_splits, n_p)), S_p = 1 for
  * an empty request.  Work unit
  * u = unit_off[p] + kvh*S_p + s covers pages [floor(s n/S), floor((s+1) n/S)).
+ * Row-exact mode (split_pages = B > 0): S_p = max(1, ceil(n_p / B)) and split
+ * s covers pages [s*B, min((s+1)*B, n_p)) (the last split takes every page up
+ * to the device length).
  * Returns SMALLW_EINVAL / SMALLW_EUNSUPPORTED on bad input (nothing allocated),
  * SMALLW_EDEVICE if num_cus == 0 and the device query fails, SMALLW_ENOMEM.
  */
@@ -115,7 +125,8 @@ int small_w_attention_plan(const smallw_problem* problem, const int32_t* seq_len
                            smallw_plan** out);
 
 /* Device workspace bytes small_w_attention_run needs (0 when no request is
- * split).  Holds per-split partial outputs and log-sum-exps. */
+ * split and the plan is not row-exact).  Holds per-split partial outputs and
+ * log-sum-exps. */
 size_t small_w_attention_workspace_bytes(const smallw_plan* plan);
 
 /*

@@ -13,8 +13,8 @@ HIP library and never imports it.
 """
 from ._lib import attention, decode_bf16, decode_e4m3, build_oracle, oracle_threads
 from .ref import (PLAN_MIN_PAGES, attention_pairs, gather_unit_pages, kv_bytes, lse_combine,
-                  plan, plan_export, split_pages)
+                  plan, plan_export, split_range)
 
 __all__ = ["attention", "decode_bf16", "decode_e4m3", "build_oracle", "oracle_threads",
            "PLAN_MIN_PAGES", "attention_pairs", "gather_unit_pages", "kv_bytes", "lse_combine",
-           "plan", "plan_export", "split_pages"]
+           "plan", "plan_export", "split_range"]

@@ -27,19 +27,22 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None):
+def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0, W=None,
+         G=None):
     """Split plan for one call.
 
     n_pg(p)     = ceil(L_p / 16)
     slots       = num_cus * (1 if D == 256 else 2)          units resident per CU
     total       = Hkv * sum_p n_pg(p)
     S_p         = 1                         if n_pg(p) == 0
+                = ceil(n_pg / split_pages)  if split_pages > 0   (row-exact mode)
                 = min(force_splits, n_pg)   if force_splits > 0
                 = max(1, min(floor(n_pg(p) * slots / total), floor(n_pg(p) / 8)))
                   otherwise (a request's share of the slots, at least 8 pages a split;
                   the floors keep sum_p Hkv*S_p <= slots whenever P*Hkv <= slots)
     unit_off[p] = Hkv * sum_{q<p} S_q;  unit u = unit_off[p] + kvh*S_p + s
-    split s covers logical pages [floor(s*n/S), floor((s+1)*n/S))
+    split s covers logical pages [floor(s*n/S), floor((s+1)*n/S)), or in row-exact
+    mode [s*B, (s+1)*B) with the last split ending at n (B = split_pages)
     """
     seq = [int(x) for x in seq_lens]
     assert len(seq) == P
@@ -51,6 +54,8 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
     for n in n_pg:
         if n == 0:
             splits.append(1)
+        elif split_pages > 0:
+            splits.append(_ceil_div(n, split_pages))
         elif force_splits > 0:
             splits.append(min(force_splits, n))
         else:
@@ -63,13 +68,19 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, W=None, G=None
         S, n = splits[p], n_pg[p]
         for kvh in range(Hkv):
             for s in range(S):
-                pb, pe = split_pages(n, S, s)
+                if split_pages > 0:
+                    pb, pe = s * split_pages, (n if s + 1 == S else (s + 1) * split_pages)
+                else:
+                    pb, pe = split_range(n, S, s)
                 units.append((p, kvh, s, pb, pe))
+    any_split = any(s > 1 for s in splits)
     return {"P": P, "Hkv": Hkv, "n_pg": n_pg, "splits": splits, "unit_off": unit_off,
-            "units": units, "U": unit_off[-1], "any_split": any(s > 1 for s in splits)}
+            "units": units, "U": unit_off[-1], "any_split": any_split,
+            "combine": any_split or split_pages > 0}
 
 
-def split_pages(n: int, S: int, s: int):
+def split_range(n: int, S: int, s: int):
+    """Balanced split s of n pages into S (the automatic and forced modes)."""
     return (s * n) // S, ((s + 1) * n) // S
 
 

@@ -13,6 +13,9 @@
 //   S_p   = 1 (empty request) | min(force_splits, n_p) |
 //           max(1, min(floor(n_p * slots / (Hkv * sum_q n_q)), floor(n_p / 8)))
 //   unit  u = unit_off[p] + kvh*S_p + s,  pages [floor(s n/S), floor((s+1) n/S))
+// Row-exact mode (split_pages = B > 0): S_p = max(1, ceil(n_p / B)), split s covers [s B, min((s+1) B, n_p)),
+// and every row goes through the combine, so split boundaries sit at fixed
+// page indices whatever W, P or the other lengths are.
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -30,8 +33,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int validate(const smallw_problem& pr, const int32_t* seq) {
     if (pr.num_reqs < 1 || pr.window < 1 || pr.num_q_heads < 1 || pr.num_kv_heads < 1 ||
         pr.head_dim < 1 || pr.page_size < 1 || pr.num_pages < 1 || pr.max_pages_per_req < 1 ||
-        pr.num_cus < 0 || pr.force_splits < 0)
+        pr.num_cus < 0 || pr.force_splits < 0 || pr.split_pages < 0)
         return SMALLW_EINVAL;
+    if (pr.force_splits > 0 && pr.split_pages > 0) return SMALLW_EINVAL;
     if (pr.causal != 0 && pr.causal != 1) return SMALLW_EINVAL;
     if (pr.kv_dtype != SMALLW_KV_BF16 && pr.kv_dtype != SMALLW_KV_FP8_E4M3) return SMALLW_EINVAL;
     if (std::isnan(pr.scale) || std::isinf(pr.scale)) return SMALLW_EINVAL;
@@ -81,6 +85,7 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             const int64_t n = pl->npg[p];
             int64_t S;
             if (n == 0) S = 1;
+            else if (in.split_pages > 0) S = ceil_div(n, in.split_pages);
             else if (in.force_splits > 0) S = in.force_splits < n ? in.force_splits : n;
             else {
                 S = n * slots / total;                       // share of the slots (floor)
@@ -92,11 +97,15 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             const int64_t next = int64_t(pl->unit_off[p]) + Hkv * S;
             if (next > INT32_MAX / 2) { delete pl; return SMALLW_EUNSUPPORTED; }
             pl->unit_off[p + 1] = int32_t(next);
-            const int64_t biggest = ceil_div(n, S);
-            if (size_t(biggest) > pl->max_unit_pages) pl->max_unit_pages = size_t(biggest);
+            for (int64_t s = 0; s < S; ++s) {
+                int64_t pb, pe;
+                smallw::split_range(n, S, s, in.split_pages, &pb, &pe);
+                if (size_t(pe - pb) > pl->max_unit_pages) pl->max_unit_pages = size_t(pe - pb);
+            }
         }
         pl->U = pl->unit_off[P];
-        if (pl->any_split) {
+        pl->combine = pl->any_split || in.split_pages > 0;
+        if (pl->combine) {
             // fp16 partials (16-row tiles, the last one padded), then one
             // {lse, scale} float pair per (unit, row)
             const size_t po = size_t(pl->U) * ((pl->R + 15) / 16 * 16) * D * 2;
@@ -143,11 +152,13 @@ int small_w_attention_plan_export(const smallw_plan* plan, int32_t* buf, size_t 
         const int64_t npg = plan->npg[p], S = plan->splits[p];
         for (int kvh = 0; kvh < Hkv; ++kvh)
             for (int64_t s = 0; s < S; ++s) {
+                int64_t pb, pe;
+                smallw::split_range(npg, S, s, plan->prob.split_pages, &pb, &pe);
                 buf[k++] = p;
                 buf[k++] = kvh;
                 buf[k++] = int32_t(s);
-                buf[k++] = int32_t(s * npg / S);
-                buf[k++] = int32_t((s + 1) * npg / S);
+                buf[k++] = int32_t(pb);
+                buf[k++] = int32_t(pe);
             }
     }
     return SMALLW_OK;

@@ -64,6 +64,8 @@ struct Params {
     uint16_t* part_o;  // split partials: fp16, lane-native blocks, rows scaled by 2^-e
     float2* part_rec;  // per (unit, row): {base-2 lse, 2^e}, [unit group][row][split]
     int32_t P, W, Hq, Hkv, G, R, bt_stride, num_pages, causal;
+    int32_t split_pages;  // > 0: row-exact splits at multiples of this many pages
+    int32_t combine;      // 1: every row goes through partials and the combine
     float scale_log2;  // softmax scale * log2(e): scores are kept in base 2
     int32_t unit_off[SMALLW_MAX_REQS + 1];
 };
@@ -93,8 +95,13 @@ __device__ __forceinline__ Unit decode_unit(const Params& a, int u) {
     L = L < 0 ? 0 : (L > cap ? cap : L);
     r.L = L;
     const int64_t n = (L + kPage - 1) / kPage;
-    r.pb = int((int64_t(r.s) * n) / r.S);
-    r.pe = int((int64_t(r.s + 1) * n) / r.S);
+    if (a.split_pages > 0) {  // row-exact: fixed boundaries, the last split runs to n
+        r.pb = int(min(int64_t(r.s) * a.split_pages, n));
+        r.pe = r.s + 1 == r.S ? int(n) : int(min(int64_t(r.s + 1) * a.split_pages, n));
+    } else {
+        r.pb = int((int64_t(r.s) * n) / r.S);
+        r.pe = int((int64_t(r.s + 1) * n) / r.S);
+    }
     return r;
 }
 
@@ -545,7 +552,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     mabs = wave_max_groups(mabs) * inv;
     if (r >= a.R) return;
     const int h = kvh * a.G + (r - qi * a.G);
-    if (un.S == 1) {
+    if (un.S == 1 && !a.combine) {
         uint16_t* orow = a.out + ((int64_t(p) * a.W + qi) * a.Hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
     const int kvh = b % a.Hkv;
     const int p = b / a.Hkv;
     const int S = (a.unit_off[p + 1] - a.unit_off[p]) / a.Hkv;
-    if (S <= 1) return;
+    if (S <= 1 && !a.combine) return;
     const int64_t u0 = a.unit_off[p] + int64_t(kvh) * S;
     const int tid = threadIdx.x;
 
@@ -791,6 +798,8 @@ void fill_params(Params& a, const smallw_plan* pl) {
     a.num_pages = pr.num_pages;
     a.causal = pr.causal;
     a.scale_log2 = pr.scale * kLog2e;
+    a.split_pages = pr.split_pages;
+    a.combine = pl->combine ? 1 : 0;
     for (int p = 0; p <= pr.num_reqs; ++p) a.unit_off[p] = pl->unit_off[p];
 }
 
@@ -894,7 +903,7 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
     hipStream_t st = static_cast<hipStream_t>(stream);
     // the sweep's end timestamp goes to ev_sweep_done, and to ev_end too when
     // there is no combine (then a marker copies it if both were asked for)
-    void* sweep_stop = pl->any_split ? ev_sweep_done : (ev_sweep_done ? ev_sweep_done : ev_end);
+    void* sweep_stop = pl->combine ? ev_sweep_done : (ev_sweep_done ? ev_sweep_done : ev_end);
     int rc;
     switch (pl->prob.head_dim) {
         case 64: rc = launch_sweep<64>(pl, a, st, ev_start, sweep_stop); break;
@@ -903,7 +912,7 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
         default: return SMALLW_EUNSUPPORTED;
     }
     if (rc) return rc;
-    if (!pl->any_split) return (ev_sweep_done && ev_end) ? record(ev_end, st) : SMALLW_OK;
+    if (!pl->combine) return (ev_sweep_done && ev_end) ? record(ev_end, st) : SMALLW_OK;
     switch (pl->prob.head_dim) {
         case 64: return launch_combine<64>(pl, a, st, ev_end);
         case 128: return launch_combine<128>(pl, a, st, ev_end);

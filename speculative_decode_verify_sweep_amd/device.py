@@ -38,12 +38,13 @@ def upload(w, device: str = "cuda:0") -> dict:
     return d
 
 
-def plan_for(w, *, num_cus: int = 0, force_splits: int = 0) -> B.Plan:
+def plan_for(w, *, num_cus: int = 0, force_splits: int = 0, split_pages: int = 0) -> B.Plan:
     pr = B.make_problem(num_reqs=w.P, window=w.W, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
                         head_dim=w.D, num_pages=w.num_pages,
                         max_pages_per_req=w.block_table.shape[1], causal=w.causal,
                         kv_dtype=B.SMALLW_KV_FP8_E4M3 if w.kv == "fp8" else B.SMALLW_KV_BF16,
-                        scale=w.scale, num_cus=num_cus, force_splits=force_splits)
+                        scale=w.scale, num_cus=num_cus, force_splits=force_splits,
+                        split_pages=split_pages)
     return B.small_w_attention_plan(pr, w.seq_lens)
 
 

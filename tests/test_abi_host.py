@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
 def base_problem(**kw):
     d = dict(num_reqs=1, window=4, num_q_heads=4, num_kv_heads=1, head_dim=64, num_pages=32,
              max_pages_per_req=32, causal=1, kv_dtype=0, scale=0.0, num_cus=256,
-             force_splits=0)
+             force_splits=0, split_pages=0)
     d.update(kw)
     return B.make_problem(**d)
 
@@ -62,6 +62,7 @@ def base_problem(**kw):
     ("scale", float("nan"), B.SMALLW_EINVAL),
     ("num_cus", -1, B.SMALLW_EINVAL),
     ("force_splits", -2, B.SMALLW_EINVAL),
+    ("split_pages", -1, B.SMALLW_EINVAL),
 ])
 def test_plan_rejects_bad_problems(field, value, code):
     kw = {field: value}
@@ -71,6 +72,12 @@ def test_plan_rejects_bad_problems(field, value, code):
     with pytest.raises(B.SmallwError) as e:
         sw.small_w_attention_plan(pr, [260])
     assert e.value.code == code
+
+
+def test_plan_rejects_forced_and_row_exact_splits_together():
+    with pytest.raises(B.SmallwError) as e:
+        sw.small_w_attention_plan(base_problem(force_splits=2, split_pages=4), [260])
+    assert e.value.code == B.SMALLW_EINVAL
 
 
 def test_plan_rejects_bad_lengths_and_too_many_rows():
@@ -103,6 +110,7 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         fp8 = int(rng.integers(0, 2))
         causal = int(rng.integers(0, 2))
         force = int(rng.choice([0, 0, 0, 1, 2, 5, 64]))
+        spg = int(rng.choice([0, 0, 0, 1, 7, 64])) if force == 0 else 0
         cus = int(rng.choice([1, 8, 80, 256, 304]))
         hi = int(rng.choice([40, 3000, 70000]))
         seq = rng.integers(W if causal else 0, hi, size=P).astype(np.int32)
@@ -111,22 +119,19 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         maxp = int(-(-int(seq.max()) // 16)) + int(rng.integers(0, 3)) or 1
         pr = B.make_problem(num_reqs=P, window=W, num_q_heads=Hkv * G, num_kv_heads=Hkv,
                             head_dim=D, num_pages=100000, max_pages_per_req=maxp, causal=causal,
-                            kv_dtype=fp8, num_cus=cus, force_splits=force)
+                            kv_dtype=fp8, num_cus=cus, force_splits=force, split_pages=spg)
         plan = sw.small_w_attention_plan(pr, seq)
         mine = sw.small_w_attention_plan_export(plan)
-        ref = oracle.plan_export(
-            oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=bool(fp8), seq_lens=seq, num_cus=cus,
-                        force_splits=force), R=W * G)
-        np.testing.assert_array_equal(mine, ref)
         pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=bool(fp8), seq_lens=seq, num_cus=cus,
-                         force_splits=force)
+                         force_splits=force, split_pages=spg)
+        np.testing.assert_array_equal(mine, oracle.plan_export(pl, R=W * G))
         biggest = max(pe - pb for (_, _, _, pb, pe) in pl["units"])
         assert sw.small_w_attention_plan_max_unit_pages(plan) == biggest
         # workspace: fp16 partial outputs in whole 16-row tiles and a {lse, scale}
         # pair per unit and row, each region 256-byte aligned
         U, R = pl["U"], W * G
         a256 = lambda x: (x + 255) // 256 * 256
-        want = a256(U * (-(-R // 16) * 16) * D * 2) + a256(U * R * 8) if pl["any_split"] else 0
+        want = a256(U * (-(-R // 16) * 16) * D * 2) + a256(U * R * 8) if pl["combine"] else 0
         assert sw.small_w_attention_workspace_bytes(plan) == want
 
 

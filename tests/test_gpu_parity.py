@@ -25,8 +25,8 @@ def announce(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def gpu_run(w, force_splits=0, num_cus=0, repeats=1):
-    plan = dv.plan_for(w, force_splits=force_splits, num_cus=num_cus)
+def gpu_run(w, force_splits=0, num_cus=0, repeats=1, split_pages=0):
+    plan = dv.plan_for(w, force_splits=force_splits, num_cus=num_cus, split_pages=split_pages)
     d = dv.upload(w)
     ws = dv.workspace_for(plan)
     outs = []
@@ -317,3 +317,44 @@ def test_long_unit_slides_the_page_table_window(kv):
     rows = sampled_rows(w, [0, 11, 23])
     ro, rl = oracle.attention(w, rows=np.array(rows))
     check(w, o, l, ro, rl, rows=rows)
+
+
+# ------------------------------------------------------------------ row-exact mode
+@pytest.mark.parametrize("name,B", [("tiny", 5), ("tiny", 64), ("verify16k", 16), ("draft", 9)])
+def test_row_exact_mode_matches_oracle(name, B):
+    w = make_workload(name)
+    announce(f"row-exact {name} split_pages={B}")
+    o, l = gpu_run(w, split_pages=B)
+    check(w, o, l, *oracle.attention(w))
+
+
+@pytest.mark.parametrize("kv,B", [("bf16", 8), ("bf16", 100), ("fp8", 8)])
+def test_row_exact_rows_do_not_depend_on_the_window(kv, B):
+    """In row-exact mode, row i of a W-row causal call is bitwise the 1-row call
+    at length L - W + i + 1 with the same query, pool and block table."""
+    w = make_workload(None, P=2, Hq=24, Hkv=4, D=256, ctx=(1500, 333), W=16, causal=True,
+                      kv=kv, placement="permuted", pool_pages=140, seed=61, poison=False)
+    announce(f"row-exact window independence {kv} B={B}")
+    o, l = gpu_run(w, split_pages=B)
+    for i in (0, 5, 15):
+        w1 = dataclasses.replace(w, W=1, q=np.ascontiguousarray(w.q[:, i:i + 1]),
+                                 seq_lens=(w.seq_lens - w.W + i + 1).astype(np.int32))
+        o1, l1 = gpu_run(w1, split_pages=B)
+        np.testing.assert_array_equal(o[:, i], o1[:, 0])
+        np.testing.assert_array_equal(l[:, i], l1[:, 0])
+    check(w, o, l, *oracle.attention(w))
+
+
+def test_row_exact_requests_do_not_depend_on_the_batch():
+    w = make_workload("draft")
+    announce("row-exact batch independence (draft)")
+    o, l = gpu_run(w, split_pages=9)
+    for p in (0, 3, 7):
+        n = -(-int(w.seq_lens[p]) // 16)
+        w1 = dataclasses.replace(w, P=1, q=np.ascontiguousarray(w.q[p:p + 1]),
+                                 block_table=np.ascontiguousarray(w.block_table[p:p + 1]),
+                                 seq_lens=w.seq_lens[p:p + 1].copy())
+        o1, l1 = gpu_run(w1, split_pages=9)
+        np.testing.assert_array_equal(o[p], o1[0])
+        np.testing.assert_array_equal(l[p], l1[0])
+        assert n > 9  # the request really is split

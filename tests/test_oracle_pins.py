@@ -288,7 +288,7 @@ def test_split_partials_combine_to_the_full_result(force):
     S = pl["splits"][0]
     parts_o, parts_l = [], []
     for s in range(S):
-        pb, pe = oracle.split_pages(n, S, s)
+        pb, pe = oracle.split_range(n, S, s)
         po, plse = oracle.attention(w, key_lo=pb * 16, key_hi=pe * 16)
         parts_o.append(po)
         parts_l.append(plse)
@@ -408,3 +408,44 @@ def test_plan_at_the_long_context_shapes():
     # tiny: 17 pages, one head, 512 slots (D=64) -> the 8-page floor: floor(17/8) = 2
     pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256)
     assert pl["splits"] == [2] and [u[3:] for u in pl["units"]] == [(0, 8), (8, 17)]
+
+
+def test_row_exact_plan_splits_at_fixed_page_multiples():
+    # tiny, B = 8: 17 pages -> ceil(17/8) = 3 splits [0,8) [8,16) [16,17)
+    pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256, split_pages=8)
+    assert pl["splits"] == [3] and [u[3:] for u in pl["units"]] == [(0, 8), (8, 16), (16, 17)]
+    assert pl["combine"] and pl["any_split"]
+    # one split only: still finished by the combine (row-exactness across W)
+    pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256,
+                     split_pages=64)
+    assert pl["splits"] == [1] and pl["combine"] and not pl["any_split"]
+    # 64K, B = 65: 4097 pages -> 64 splits of 65 pages except the last (2 pages)
+    pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[65552], num_cus=256,
+                     split_pages=65)
+    assert pl["splits"] == [64] and pl["U"] == 256
+    assert pl["units"][62][3:] == (4030, 4095) and pl["units"][63][3:] == (4095, 4097)
+    # boundaries do not move with the length or with other requests
+    a = oracle.plan(P=2, Hkv=2, D=128, kv_fp8=False, seq_lens=[1000, 37], num_cus=8,
+                    split_pages=10)
+    b = oracle.plan(P=1, Hkv=2, D=128, kv_fp8=False, seq_lens=[990], num_cus=256,
+                    split_pages=10)
+    ua = [u[3:] for u in a["units"] if u[0] == 0 and u[1] == 0]
+    ub = [u[3:] for u in b["units"] if u[1] == 0]
+    assert ua[:-1] == ub[:-1] and ua[-1] == (60, 63) and ub[-1] == (60, 62)
+
+
+def test_row_exact_split_partials_combine_to_the_full_result():
+    w = tiny(P=1, Hq=4, Hkv=2, D=16, ctx=(200,), W=6, causal=True, seed=18)
+    pl = oracle.plan(P=1, Hkv=w.Hkv, D=w.D, kv_fp8=False, seq_lens=w.seq_lens, num_cus=1,
+                     split_pages=4)
+    o, l = oracle.attention(w)
+    parts_o, parts_l = [], []
+    for (_, kvh, _, pb, pe) in pl["units"]:
+        if kvh == 0:
+            po, plse = oracle.attention(w, key_lo=pb * 16, key_hi=pe * 16)
+            parts_o.append(po)
+            parts_l.append(plse)
+    assert len(parts_o) == 4                  # 13 pages -> [0,4) [4,8) [8,12) [12,13)
+    co, cl = oracle.lse_combine(np.stack(parts_o), np.stack(parts_l))
+    np.testing.assert_allclose(co, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(cl, l, rtol=1e-13, atol=1e-12)
