@@ -186,6 +186,28 @@ int small_w_attention_trace_pages(const smallw_plan* plan, const int32_t* block_
 /* Largest page count of any work unit of the plan (host lengths). */
 size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan);
 
+/*
+ * Paged KV append (the step right before a verify call): on `stream`, write the
+ * W window tokens' K and V rows into their pool slots, using the plan's shapes.
+ * "perf(dflash): widen the verify window past the compact graph's four-row
+ * limit", section What changed: the window rows are written into the paged
+ * cache, and slots past a request's length are overwritten later, never read.
+ *   k_new, v_new  device bf16 [P][W][Hkv][D]: token i of request p sits at
+ *                 position pos = L_p - W + i (requests with L_p < W - i skip it)
+ *   k_pool, v_pool, k_scale, v_scale, block_table, seq_lens: as for
+ *                 small_w_attention_run (scales required for an e4m3 pool)
+ * The K row goes to slot pos % 16 of page block_table[p][pos / 16], the V row
+ * to the same slot of the transposed value page.  bf16 pools get the bits as
+ * given.  e4m3 pools get, per (token, KV head) row, scale = amax|x| / 448 (1.0
+ * for an all-zero row) and codes = round-to-nearest-even of x / scale on the
+ * OCP e4m3fn grid, computed in fp32 with IEEE division.  Rows of different
+ * tokens must map to different slots.  Returns SMALLW_EINVAL (null pointer or
+ * plan), SMALLW_EDEVICE (launch failure).
+ */
+int small_w_kv_append(const smallw_plan* plan, const void* k_new, const void* v_new,
+                      void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                      const int32_t* block_table, const int32_t* seq_lens, void* stream);
+
 /* Release a plan (NULL is allowed). */
 void small_w_attention_plan_destroy(smallw_plan* plan);
 

@@ -68,6 +68,7 @@ def lib():
         L.small_w_attention_plan_export.argtypes = [vp, i32p, sz, ctypes.POINTER(sz)]
         L.small_w_attention_plan_export.restype = ctypes.c_int
         L.small_w_attention_trace_pages.argtypes = [vp, vp, vp, vp, sz, vp]
+        L.small_w_kv_append.argtypes = [vp] * 10
         L.small_w_attention_trace_pages.restype = ctypes.c_int
         L.small_w_attention_plan_destroy.argtypes = [vp]
         L.small_w_attention_plan_destroy.restype = None
@@ -171,6 +172,18 @@ def small_w_attention_trace_pages(plan: Plan, block_table, seq_lens, pages_out,
                                              _ptr(pages_out), maxp, _stream(stream))
     if rc != SMALLW_OK:
         raise SmallwError(rc, "small_w_attention_trace_pages")
+
+
+def small_w_kv_append(plan: Plan, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                      block_table, seq_lens, stream=None) -> None:
+    """Write the plan's W window tokens (bf16 [P][W][Hkv][D] device tensors) into
+    their pool slots, quantising to e4m3 with per-(token, KV-head) scales for an
+    fp8 pool.  Tensors are device tensors in the documented layouts."""
+    rc = lib().small_w_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                 _ptr(seq_lens), _stream(stream))
+    if rc != SMALLW_OK:
+        raise SmallwError(rc, "small_w_kv_append")
 
 
 def small_w_attention_strerror(code: int) -> str:

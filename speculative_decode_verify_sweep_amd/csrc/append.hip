@@ -1,0 +1,158 @@
+// Paged KV append: write the W window tokens' K and V into their pool slots,
+// the step right before a verify call reads them.
+//
+// "perf(dflash): widen the verify window past the compact graph's four-row
+// limit", section What changed: the window's K/V rows are written into the
+// paged cache (stale slots past a request's length are later overwritten and
+// never read); "DFlash2 leaves the paged graph fast path ...", section Scope:
+// one shared pool addressed by a batched block table and per-request lengths.
+// Token i of request p sits at position L_p - W + i; its K row goes to slot
+// pos % 16 of pool page block_table[p][pos / 16] and its V row to the same
+// slot of the transposed (d-major) value page.  For e4m3 pools each (token,
+// KV head) row gets scale = amax|x| / 448 (1 when the row is all zero) and
+// codes = round-to-nearest-even of x / scale on the OCP e4m3fn grid, all in
+// fp32 (IEEE division), so the codes are exactly reproducible.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "plan_internal.h"
+
+namespace {
+
+struct AppendParams {
+    const uint16_t* k_new;  // bf16 [P][W][Hkv][D]
+    const uint16_t* v_new;
+    uint8_t* k_pool;
+    uint8_t* v_pool;
+    float* k_scale;
+    float* v_scale;
+    const int32_t* bt;
+    const int32_t* seq;
+    int32_t P, W, Hkv, bt_stride, num_pages;
+};
+
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, uint32_t(b) << 16);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// One wave per (p, i, kvh); lane l owns elements [E*l, E*l + E) of the row.
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
+    constexpr int E = D / 64;
+    const int b = blockIdx.x;
+    const int kvh = b % a.Hkv;
+    const int i = (b / a.Hkv) % a.W;
+    const int p = b / (a.Hkv * a.W);
+    int L = a.seq[p];
+    const int cap = a.bt_stride * SMALLW_PAGE_SIZE;
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int pos = L - a.W + i;
+    if (pos < 0) return;  // the request is shorter than the window: no slot
+    int page = a.bt[int64_t(p) * a.bt_stride + (pos >> 4)];
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    const int slot = pos & 15;
+    const int l = threadIdx.x;
+    const int64_t row = ((int64_t(p) * a.W + i) * a.Hkv + kvh) * D + E * l;
+    const int64_t ph = int64_t(page) * a.Hkv + kvh;  // page-head index
+    float kx[E], vx[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kx[e] = bf16_to_f32(a.k_new[row + e]);
+        vx[e] = bf16_to_f32(a.v_new[row + e]);
+    }
+    if constexpr (!FP8) {
+        uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pool) + (ph * 16 + slot) * D + E * l;
+        uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool) + ph * D * 16 + slot;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            kp[e] = a.k_new[row + e];
+            vp[int64_t(E * l + e) * 16] = a.v_new[row + e];
+        }
+    } else {
+        float km = 0.f, vm = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            km = fmaxf(km, fabsf(kx[e]));
+            vm = fmaxf(vm, fabsf(vx[e]));
+        }
+        km = wave_max(km);
+        vm = wave_max(vm);
+        const float ks = km > 0.f ? km / kE4m3Max : 1.f;
+        const float vs = vm > 0.f ? vm / kE4m3Max : 1.f;
+        uint8_t* kp = a.k_pool + (ph * 16 + slot) * D + E * l;
+        uint8_t* vp = a.v_pool + ph * D * 16 + slot;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float kq = fminf(fmaxf(kx[e] / ks, -kE4m3Max), kE4m3Max);
+            const float vq = fminf(fmaxf(vx[e] / vs, -kE4m3Max), kE4m3Max);
+            // v_cvt_pk_fp8_f32: round to nearest even onto the OCP e4m3fn grid
+            const uint32_t kc = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(kq, kq, 0, false));
+            const uint32_t vc = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(vq, vq, 0, false));
+            kp[e] = uint8_t(kc & 0xFF);
+            vp[int64_t(E * l + e) * 16] = uint8_t(vc & 0xFF);
+        }
+        if (l == 0) {
+            a.k_scale[ph * 16 + slot] = ks;
+            a.v_scale[ph * 16 + slot] = vs;
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_append(const smallw_plan* pl, const AppendParams& a, hipStream_t st) {
+    const unsigned blocks = unsigned(int64_t(a.P) * a.W * a.Hkv);
+    if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
+        hipLaunchKernelGGL((append_kernel<D, true>), dim3(blocks), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((append_kernel<D, false>), dim3(blocks), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int small_w_kv_append(const smallw_plan* pl, const void* k_new, const void* v_new,
+                                 void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 void* stream) {
+    if (!pl || !k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens)
+        return SMALLW_EINVAL;
+    const bool fp8 = pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3;
+    if (fp8 && (!k_scale || !v_scale)) return SMALLW_EINVAL;
+    AppendParams a;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.k_pool = static_cast<uint8_t*>(k_pool);
+    a.v_pool = static_cast<uint8_t*>(v_pool);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.bt = block_table;
+    a.seq = seq_lens;
+    a.P = pl->prob.num_reqs;
+    a.W = pl->prob.window;
+    a.Hkv = pl->prob.num_kv_heads;
+    a.bt_stride = pl->prob.max_pages_per_req;
+    a.num_pages = pl->prob.num_pages;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (pl->prob.head_dim) {
+        case 64: e = launch_append<64>(pl, a, st); break;
+        case 128: e = launch_append<128>(pl, a, st); break;
+        case 256: e = launch_append<256>(pl, a, st); break;
+        default: return SMALLW_EUNSUPPORTED;
+    }
+    if (e != hipSuccess) {
+        smallw::set_device_error("append kernel launch", int(e));
+        return SMALLW_EDEVICE;
+    }
+    return SMALLW_OK;
+}

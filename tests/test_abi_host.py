@@ -26,12 +26,13 @@ HEADER = os.path.join(ROOT, "include", "smallw.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(small_w_attention_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(small_w_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert "small_w_attention_plan" in names and "small_w_attention_run" in names
+    assert "small_w_kv_append" in names
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -157,6 +158,20 @@ def test_run_rejects_null_pointers_and_bad_workspace_before_any_launch():
     misaligned[10] = fake + 16
     assert lib.small_w_attention_run(*misaligned) == B.SMALLW_EWORKSPACE
     assert lib.small_w_attention_run(None, *args[1:]) == B.SMALLW_EINVAL
+
+
+def test_kv_append_rejects_null_pointers_before_any_launch():
+    lib = B.lib()
+    plan = sw.small_w_attention_plan(base_problem(), [260])
+    fake = 1 << 40  # never dereferenced
+    args = [plan.handle, fake, fake, fake, fake, None, None, fake, fake, None]
+    for k in (1, 2, 3, 4, 7, 8):
+        bad = list(args)
+        bad[k] = None
+        assert lib.small_w_kv_append(*bad) == B.SMALLW_EINVAL
+    assert lib.small_w_kv_append(None, *args[1:]) == B.SMALLW_EINVAL
+    fp8 = sw.small_w_attention_plan(base_problem(kv_dtype=1), [260])
+    assert lib.small_w_kv_append(fp8.handle, *args[1:]) == B.SMALLW_EINVAL   # scales missing
 
 
 def test_fp8_run_requires_scales():

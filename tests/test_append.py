@@ -1,0 +1,208 @@
+"""Paged KV append: the oracle's e4m3 encoder and append pinned on the CPU,
+then the HIP kernel (through the C ABI) against the oracle, bit for bit.
+
+The e4m3 encoder is pinned against torch's own float8_e4m3fn cast (a library
+routine with the same round-to-nearest-even definition), against every finite
+code's exact value, and against the midpoints between codes (ties to even).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_workload
+from workloads.synth import quantize_e4m3, to_bf16_bits
+
+
+# ---------------------------------------------------------------- CPU: oracle pins
+def test_e4m3_encoder_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = oracle.decode_e4m3(codes).astype(np.float32)
+    vals[codes == 0x80] = -0.0
+    np.testing.assert_array_equal(oracle.e4m3_encode(vals), codes)
+
+
+def test_e4m3_encoder_sends_midpoints_to_the_even_code():
+    pos = np.array([c for c in range(0x7F)], dtype=np.uint8)
+    v = oracle.decode_e4m3(pos)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (v[:-1] + v[1:]) / 2)   # exact in fp32
+    got = oracle.e4m3_encode(mids)
+    want = np.where(pos[:-1] % 2 == 0, pos[:-1], pos[1:])
+    np.testing.assert_array_equal(got, want)
+    # a hair above / below a midpoint goes to the nearer code
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    np.testing.assert_array_equal(oracle.e4m3_encode(up), pos[1:])
+    np.testing.assert_array_equal(oracle.e4m3_encode(dn), pos[:-1])
+
+
+def test_e4m3_encoder_agrees_with_torch_cast():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 60000), rng.normal(0, 1, 60000),
+                        rng.normal(0, 2 ** -8, 60000)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(x), want)
+
+
+def test_oracle_append_bf16_writes_exactly_the_window_slots():
+    w = make_workload(None, P=2, Hq=8, Hkv=2, D=64, ctx=(40, 5), W=4, causal=True, kv="bf16",
+                      placement="permuted", pool_pages=12, seed=71, poison=False)
+    rng = np.random.default_rng(3)
+    kn = to_bf16_bits(rng.normal(size=(2, 4, 2, 64)).astype(np.float32))
+    vn = to_bf16_bits(rng.normal(size=(2, 4, 2, 64)).astype(np.float32))
+    kp, vp, _, _ = oracle.kv_append(P=2, W=4, Hkv=2, D=64, kv_fp8=False, k_new_bits=kn,
+                                    v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                    k_scale=None, v_scale=None, block_table=w.block_table,
+                                    seq_lens=w.seq_lens, num_pages=w.num_pages)
+    touched = np.zeros(kp.shape[:3], bool)
+    for p in range(2):
+        for i in range(4):
+            pos = int(w.seq_lens[p]) - 4 + i
+            pg, sl = int(w.block_table[p, pos // 16]), pos % 16
+            np.testing.assert_array_equal(kp[pg, :, sl, :], kn[p, i])
+            np.testing.assert_array_equal(vp[pg, :, :, sl], vn[p, i])
+            touched[pg, :, sl] = True
+    np.testing.assert_array_equal(kp[~touched], w.k_pool[~touched])
+    np.testing.assert_array_equal(vp.transpose(0, 1, 3, 2)[~touched],
+                                  w.v_pool.transpose(0, 1, 3, 2)[~touched])
+
+
+def test_oracle_fp8_row_quantizer_matches_the_input_generator():
+    rng = np.random.default_rng(4)
+    x = rng.normal(0, 3, size=(64, 256)).astype(np.float32)
+    x = (to_bf16_bits(x).astype(np.uint32) << 16).view(np.float32)   # bf16-exact rows
+    x[5] = 0.0                                                         # all-zero row
+    codes, scales = quantize_e4m3(x)
+    for r in range(64):
+        c, s = oracle.e4m3_row_quantize(x[r])
+        np.testing.assert_array_equal(c, codes[r])
+        assert np.float32(s) == scales[r]
+    assert scales[5] == 1.0
+
+
+# ---------------------------------------------------------------- GPU: kernel parity
+def host_bits(t):
+    """Device pool tensor -> host array of its raw bits (uint16 bf16 or uint8 codes)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint8)
+
+
+def _append_case(kv, D=128, W=16, ctx=(700, 45, 0), seed=72, Hq=8):
+    w = make_workload(None, P=len(ctx), Hq=Hq, Hkv=4, D=D, ctx=ctx, W=W, causal=True, kv=kv,
+                      placement="permuted", pool_pages=sum(-(-(c + W) // 16) for c in ctx) + 6,
+                      seed=seed, seq_lens=tuple(c + W if c > 0 else 0 for c in ctx))
+    rng = np.random.default_rng(seed)
+    shape = (w.P, W, w.Hkv, D)
+    kn = to_bf16_bits(rng.normal(0, 1, size=shape).astype(np.float32))   # same draw as the
+    vn = to_bf16_bits(rng.normal(0, 1, size=shape).astype(np.float32))   # workloads' K and V
+    kn[0, 3, 1] = 0                              # an all-zero row: scale 1
+    return w, kn, vn
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_append_kernel_matches_oracle_bitwise(kv, D):
+    from speculative_decode_verify_sweep_amd import device as dv
+    import speculative_decode_verify_sweep_amd as sw
+    w, kn, vn = _append_case(kv, D=D)
+    print(f"[case] append {kv} D={D}", flush=True)
+    d = dv.upload(w)
+    plan = dv.plan_for(w)
+    kt = torch.from_numpy(kn.view(np.int16)).cuda()
+    vt = torch.from_numpy(vn.view(np.int16)).cuda()
+    sw.small_w_kv_append(plan, kt, vt, d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
+                         d["block_table"], d["seq_lens"])
+    torch.cuda.synchronize()
+    fp8 = kv == "fp8"
+    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=D, kv_fp8=fp8, k_new_bits=kn,
+                                      v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                      k_scale=w.k_scale if fp8 else None,
+                                      v_scale=w.v_scale if fp8 else None,
+                                      block_table=w.block_table, seq_lens=w.seq_lens,
+                                      num_pages=w.num_pages)
+    np.testing.assert_array_equal(host_bits(d["k_pool"]), kp)
+    np.testing.assert_array_equal(host_bits(d["v_pool"]), vp)
+    if fp8:
+        np.testing.assert_array_equal(d["k_scale"].cpu().numpy(), ks)
+        np.testing.assert_array_equal(d["v_scale"].cpu().numpy(), vs)
+
+
+@pytest.mark.gpu
+def test_append_kernel_rounds_every_tie_to_even():
+    """Rows holding 448 have scale exactly 1, so the codes are the e4m3 rounding
+    of the bf16 inputs themselves: every code value, every midpoint and their
+    bf16 neighbours go through the kernel's conversion."""
+    from speculative_decode_verify_sweep_amd import device as dv
+    import speculative_decode_verify_sweep_amd as sw
+    pos = np.arange(0x7F, dtype=np.uint8)
+    v = oracle.decode_e4m3(pos)
+    mids = (v[:-1] + v[1:]) / 2
+    cand = np.concatenate([v, mids, -v, -mids]).astype(np.float32)
+    bits = to_bf16_bits(cand)
+    near = np.concatenate([bits, bits + 1, bits - 1]).astype(np.uint16)
+    vals = (near.astype(np.uint32) << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
+    D, W = 256, 16
+    per_row = D - 1
+    rows = -(-vals.size // per_row)
+    assert rows <= W * 4
+    data = np.zeros((rows * per_row,), np.float32)
+    data[:vals.size] = vals
+    data = data.reshape(rows, per_row)
+    data = np.concatenate([np.full((rows, 1), 448, np.float32), data], axis=1)   # amax = 448
+    full = np.zeros((1, W, 4, D), np.float32)
+    full.reshape(W * 4, D)[:rows] = data
+    full.reshape(W * 4, D)[rows:, 0] = 448
+    w = make_workload(None, P=1, Hq=4, Hkv=4, D=D, ctx=(48,), W=W, causal=True, kv="fp8",
+                      placement="in_order", pool_pages=5, seed=73)
+    kn = to_bf16_bits(full)
+    d = dv.upload(w)
+    plan = dv.plan_for(w)
+    kt = torch.from_numpy(kn.view(np.int16)).cuda()
+    print("[case] append e4m3 ties", flush=True)
+    sw.small_w_kv_append(plan, kt, kt, d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
+                         d["block_table"], d["seq_lens"])
+    torch.cuda.synchronize()
+    assert int(w.block_table[0, 3]) == 3 and np.all(d["k_scale"].cpu().numpy()[3] == 1.0)
+    kp, _, _, _ = oracle.kv_append(P=1, W=W, Hkv=4, D=D, kv_fp8=True, k_new_bits=kn,
+                                   v_new_bits=kn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                   k_scale=w.k_scale, v_scale=w.v_scale,
+                                   block_table=w.block_table, seq_lens=w.seq_lens,
+                                   num_pages=w.num_pages)
+    np.testing.assert_array_equal(host_bits(d["k_pool"]), kp)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_then_verify_matches_oracle(kv):
+    """The step pair a verify does: append the window's K/V, then attend."""
+    from speculative_decode_verify_sweep_amd import device as dv
+    import speculative_decode_verify_sweep_amd as sw
+    from test_gpu_parity import check
+    w, kn, vn = _append_case(kv, D=256, W=16, ctx=(3000, 200, 0), seed=74, Hq=24)
+    fp8 = kv == "fp8"
+    d = dv.upload(w)
+    plan = dv.plan_for(w)
+    ws = dv.workspace_for(plan)
+    print(f"[case] append + verify {kv}", flush=True)
+    sw.small_w_kv_append(plan, torch.from_numpy(kn.view(np.int16)).cuda(),
+                         torch.from_numpy(vn.view(np.int16)).cuda(), d["k_pool"], d["v_pool"],
+                         d["k_scale"], d["v_scale"], d["block_table"], d["seq_lens"])
+    dv.run(plan, d, ws)
+    torch.cuda.synchronize()
+    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=w.D, kv_fp8=fp8, k_new_bits=kn,
+                                      v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                      k_scale=w.k_scale if fp8 else None,
+                                      v_scale=w.v_scale if fp8 else None,
+                                      block_table=w.block_table, seq_lens=w.seq_lens,
+                                      num_pages=w.num_pages)
+    w2 = dataclasses.replace(w, k_pool=kp, v_pool=vp, k_scale=ks if fp8 else w.k_scale,
+                             v_scale=vs if fp8 else w.v_scale)
+    o = d["out"].float().cpu().numpy().astype(np.float64)
+    l = d["lse"].cpu().numpy().astype(np.float64)
+    check(w2, o, l, *oracle.attention(w2))
