@@ -255,9 +255,12 @@ def main():
                  ("draft P=8 W=9 non-causal", dict(name="draft")),
                  ("fp8 P=4 8K..64K W=16", dict(name="fp8")),
                  ("verify64k W=16 row-exact, 65-page splits",
-                  dict(name="verify64k", W=16, split_pages=65))]
+                  dict(name="verify64k", W=16, split_pages=65)),
+                 ("verify64k W=16 sliding window 4096",
+                  dict(name="verify64k", W=16, window_left=4096))]
         for label, spec in specs:
-            wl = make_workload(spec["name"], W=spec.get("W"))
+            wl = make_workload(spec["name"], W=spec.get("W"),
+                               window_left=spec.get("window_left", 0))
             dd = dv.upload(wl)
             pl = dv.plan_for(wl, split_pages=spec.get("split_pages", 0))
             wsb = dv.workspace_for(pl)
@@ -268,7 +271,9 @@ def main():
             r = timed([fn], args.steps, args.warmup)
             t_us = statistics.median([x[0] for x in r]) * 1e3
             s_us = statistics.median([x[1] for x in r]) * 1e3
-            b = kv_bytes(wl.seq_lens, wl.Hkv, wl.D, elt=1 if wl.kv == "fp8" else 2)
+            seen = [int(L) - max(0, int(L) - wl.W - wl.window_left + 1) if wl.window_left
+                    else int(L) for L in wl.seq_lens]      # keys some row can see
+            b = kv_bytes(seen, wl.Hkv, wl.D, elt=1 if wl.kv == "fp8" else 2)
             if wl.kv == "fp8":
                 b += int(sum(int(x) for x in wl.seq_lens)) * wl.Hkv * 8   # k and v scales
             others[label] = {"us_per_call": round(t_us, 2), "sweep_us": round(s_us, 2),

@@ -29,6 +29,9 @@
  *                 j <= L - W + i              (causal == 1, verify window:
  *                                              L counts the window's own rows,
  *                                              row i sits at position L-W+i)
+ *                 and j >= h - N + 1 with window_left = N > 0, h the row's
+ *                 last visible key ("DFlash2 leaves the paged graph fast path
+ *                 ...", section Scope, names a sliding window as its own case)
  *   s_j = scale * <q, k_j>;  out = softmax(s) . V;  lse = ln sum_j exp(s_j)
  *   A row with no visible key (only when L == 0) gets out = 0, lse = -inf.
  *
@@ -100,6 +103,10 @@ typedef struct smallw_problem {
                                   on its own query, keys and values: it is bitwise
                                   the same whatever W, the other rows and the other
                                   requests are (exclusive with force_splits)         */
+    int32_t window_left;       /* 0 = none; N > 0 = sliding window: a row whose last
+                                  visible key is at position h sees only the keys
+                                  h-N+1 .. h (pages before the lowest row's window
+                                  are not read at all)                               */
 } smallw_problem;
 
 typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
@@ -118,6 +125,11 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  * Row-exact mode (split_pages = B > 0): S_p = max(1, ceil(n_p / B)) and split
  * s covers pages [s*B, min((s+1)*B, n_p)) (the last split takes every page up
  * to the device length).
+ * Sliding window (window_left = N > 0): pages before n_lo = floor(max(0, h0 -
+ * N + 1) / 16), h0 = L - W (causal) or L - 1, are skipped: the formulas above
+ * apply to the n_p - n_lo pages from n_lo on (row-exact pieces stay on the
+ * absolute grid of multiples of B; the first one starts at n_lo moved down to
+ * an even offset from its grid point, so two-page chunks line up in every call).
  * Returns SMALLW_EINVAL / SMALLW_EUNSUPPORTED on bad input (nothing allocated),
  * SMALLW_EDEVICE if num_cus == 0 and the device query fails, SMALLW_ENOMEM.
  */

@@ -32,7 +32,7 @@ def _load():
         P = ctypes.c_void_p
         i = ctypes.c_int
         lib.oracle_attention.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.c_double, P, P, P, P,
-                                         P, P, P, P, i, i, i, P, P]
+                                         P, P, P, P, i, i, i, i, P, P]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_decode_bf16.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_decode_e4m3.argtypes = [P, P, ctypes.c_int64]
@@ -72,7 +72,8 @@ def attention(w, rows=None, key_lo: int = 0, key_hi: int = 2**31 - 1):
                       w.v_scale if fp8 else None, w.block_table, w.seq_lens)]
     rc = lib.oracle_attention(w.P, w.W, w.Hq, w.Hkv, w.D, w.num_pages, w.block_table.shape[1],
                               int(w.causal), int(fp8), float(w.scale), *[_ptr(a) for a in arrs],
-                              _ptr(rows_arr), n, int(key_lo), int(key_hi), _ptr(out), _ptr(lse))
+                              _ptr(rows_arr), n, int(key_lo), int(key_hi),
+                              int(getattr(w, "window_left", 0)), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle rejected the input (code {rc})")
     return out, lse

@@ -18,6 +18,9 @@
  *    never looked at); section Exactness: rows are independent.
  *  - causal verify alignment: window row i sits at absolute position
  *    L - W + i and sees keys at positions <= L - W + i (bottom-right mask).
+ *  - "DFlash2 leaves the paged graph fast path ...", section Scope, lists a
+ *    sliding window that a path did not apply: with window_left = N > 0 a row
+ *    whose last visible key is at position h sees only keys h - N + 1 .. h.
  *
  * Steps, in order: gather the request's visible pages into contiguous K and V
  * (decoded exactly to fp64), then for each row the textbook softmax attention
@@ -145,7 +148,8 @@ static void attend_row(const oracle_in *in, const double *qrow, const double *K,
  *   rows == NULL: every (p, i, h); out is [P][W][Hq][D], lse is [P][W][Hq].
  *   rows != NULL: n_rows triples (p, i, h); out is [n_rows][D], lse [n_rows].
  * Keys are further restricted to absolute positions [key_lo, key_hi) (pass
- * 0 and INT32_MAX for plain attention) so a test can form split partials.
+ * 0 and INT32_MAX for plain attention) so a test can form split partials, and
+ * to the row's last window_left keys when window_left > 0.
  * Returns 0, or -1 on an argument the library would also reject.
  */
 int oracle_attention(int P, int W, int Hq, int Hkv, int D, int num_pages, int bt_stride,
@@ -153,7 +157,7 @@ int oracle_attention(int P, int W, int Hq, int Hkv, int D, int num_pages, int bt
                      const void *k_pool, const void *v_pool, const float *k_scale,
                      const float *v_scale, const int32_t *block_table,
                      const int32_t *seq_lens, const int32_t *rows, int n_rows,
-                     int key_lo, int key_hi, double *out, double *lse)
+                     int key_lo, int key_hi, int window_left, double *out, double *lse)
 {
     if (P < 1 || W < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || bt_stride < 1)
         return -1;
@@ -213,6 +217,8 @@ int oracle_attention(int P, int W, int Hq, int Hkv, int D, int num_pages, int bt
                         n_vis = 0;
                     int lo = key_lo > 0 ? key_lo : 0;
                     int hi = key_hi < n_vis ? key_hi : n_vis;
+                    if (window_left > 0 && n_vis - window_left > lo)
+                        lo = n_vis - window_left;    /* sliding window */
                     const uint16_t *qsrc = q + (((int64_t)rp * W + ri) * Hq + rh) * D;
                     for (int d = 0; d < D; ++d)
                         qrow[d] = oracle_bf16_to_double(qsrc[d]);

@@ -27,51 +27,68 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0, W=None,
-         G=None):
+def first_page(L: int, W: int, causal: bool, window_left: int) -> int:
+    """First page any row of the request needs: with a sliding window of N keys,
+    row 0 (the lowest) sees keys from (L - W if causal else L - 1) - N + 1 on."""
+    if window_left <= 0 or L <= 0:
+        return 0
+    hi0 = (L - W) if causal else (L - 1)
+    return max(0, hi0 - window_left + 1) // PAGE
+
+
+def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0, W=1,
+         causal=True, window_left=0):
     """Split plan for one call.
 
-    n_pg(p)     = ceil(L_p / 16)
+    n_pg(p)     = ceil(L_p / 16);  n_lo(p) = first page any row needs (0 without a
+                  sliding window);  n_eff(p) = n_pg - n_lo  pages streamed
     slots       = num_cus * (1 if D == 256 else 2)          units resident per CU
-    total       = Hkv * sum_p n_pg(p)
-    S_p         = 1                         if n_pg(p) == 0
-                = ceil(n_pg / split_pages)  if split_pages > 0   (row-exact mode)
-                = min(force_splits, n_pg)   if force_splits > 0
-                = max(1, min(floor(n_pg(p) * slots / total), floor(n_pg(p) / 8)))
+    total       = Hkv * sum_p n_eff(p)
+    S_p         = 1                          if n_pg(p) == 0
+                = ceil(n_pg/B) - floor(n_lo/B) if split_pages = B > 0 (row-exact mode)
+                = min(force_splits, n_eff)   if force_splits > 0
+                = max(1, min(floor(n_eff * slots / total), floor(n_eff / 8)))
                   otherwise (a request's share of the slots, at least 8 pages a split;
                   the floors keep sum_p Hkv*S_p <= slots whenever P*Hkv <= slots)
     unit_off[p] = Hkv * sum_{q<p} S_q;  unit u = unit_off[p] + kvh*S_p + s
-    split s covers logical pages [floor(s*n/S), floor((s+1)*n/S)), or in row-exact
-    mode [s*B, (s+1)*B) with the last split ending at n (B = split_pages)
+    split s covers pages n_lo + [floor(s*n_eff/S), floor((s+1)*n_eff/S)), or in
+    row-exact mode the s-th piece of the absolute grid [k*B, (k+1)*B), the last
+    split ending at n_pg and the first starting at n_lo moved down to an even
+    offset from its k*B (the piece's two-page chunks then line up in every call)
     """
     seq = [int(x) for x in seq_lens]
     assert len(seq) == P
-    elt = 1 if kv_fp8 else 2
     n_pg = [_ceil_div(L, PAGE) for L in seq]
+    n_lo = [first_page(L, W, causal, window_left) for L in seq]
+    n_eff = [n - lo for n, lo in zip(n_pg, n_lo)]
     slots = num_cus * (1 if D == 256 else 2)
-    total = Hkv * sum(n_pg)
+    total = Hkv * sum(n_eff)
     splits = []
-    for n in n_pg:
+    for n, lo, ne in zip(n_pg, n_lo, n_eff):
         if n == 0:
             splits.append(1)
         elif split_pages > 0:
-            splits.append(_ceil_div(n, split_pages))
+            splits.append(_ceil_div(n, split_pages) - lo // split_pages)
         elif force_splits > 0:
-            splits.append(min(force_splits, n))
+            splits.append(min(force_splits, ne))
         else:
-            splits.append(max(1, min((n * slots) // total, n // PLAN_MIN_PAGES)))
+            splits.append(max(1, min((ne * slots) // total, ne // PLAN_MIN_PAGES)))
     unit_off = [0]
     for s in splits:
         unit_off.append(unit_off[-1] + Hkv * s)
     units = []
     for p in range(P):
-        S, n = splits[p], n_pg[p]
+        S, n, lo, ne = splits[p], n_pg[p], n_lo[p], n_eff[p]
         for kvh in range(Hkv):
             for s in range(S):
                 if split_pages > 0:
-                    pb, pe = s * split_pages, (n if s + 1 == S else (s + 1) * split_pages)
+                    k = lo // split_pages + s
+                    b0 = k * split_pages
+                    pb = (b0 + ((lo - b0) // 2) * 2) if s == 0 else b0
+                    pe = n if s + 1 == S else (k + 1) * split_pages
                 else:
-                    pb, pe = split_range(n, S, s)
+                    pb, pe = split_range(ne, S, s)
+                    pb, pe = pb + lo, pe + lo
                 units.append((p, kvh, s, pb, pe))
     any_split = any(s > 1 for s in splits)
     return {"P": P, "Hkv": Hkv, "n_pg": n_pg, "splits": splits, "unit_off": unit_off,

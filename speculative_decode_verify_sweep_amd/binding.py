@@ -38,7 +38,8 @@ class smallw_problem(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("num_cus", ctypes.c_int32),
                 ("force_splits", ctypes.c_int32),
-                ("split_pages", ctypes.c_int32)]
+                ("split_pages", ctypes.c_int32),
+                ("window_left", ctypes.c_int32)]
 
 
 _lib = None
@@ -93,10 +94,10 @@ class Plan:
 
 def make_problem(*, num_reqs, window, num_q_heads, num_kv_heads, head_dim, num_pages,
                  max_pages_per_req, causal, kv_dtype=SMALLW_KV_BF16, scale=0.0, num_cus=0,
-                 force_splits=0, split_pages=0, page_size=16) -> smallw_problem:
+                 force_splits=0, split_pages=0, window_left=0, page_size=16) -> smallw_problem:
     return smallw_problem(num_reqs, window, num_q_heads, num_kv_heads, head_dim, page_size,
                           num_pages, max_pages_per_req, int(causal), int(kv_dtype),
-                          float(scale), num_cus, force_splits, split_pages)
+                          float(scale), num_cus, force_splits, split_pages, window_left)
 
 
 def small_w_attention_plan(problem: smallw_problem, seq_lens_host) -> Plan:

@@ -33,7 +33,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int validate(const smallw_problem& pr, const int32_t* seq) {
     if (pr.num_reqs < 1 || pr.window < 1 || pr.num_q_heads < 1 || pr.num_kv_heads < 1 ||
         pr.head_dim < 1 || pr.page_size < 1 || pr.num_pages < 1 || pr.max_pages_per_req < 1 ||
-        pr.num_cus < 0 || pr.force_splits < 0 || pr.split_pages < 0)
+        pr.num_cus < 0 || pr.force_splits < 0 || pr.split_pages < 0 || pr.window_left < 0)
         return SMALLW_EINVAL;
     if (pr.force_splits > 0 && pr.split_pages > 0) return SMALLW_EINVAL;
     if (pr.causal != 0 && pr.causal != 1) return SMALLW_EINVAL;
@@ -72,24 +72,26 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
         pl->R = in.window * pl->G;
         pl->seq.assign(seq, seq + P);
         pl->npg.resize(P);
+        pl->nlo.resize(P);
         int64_t total = 0;
         for (int p = 0; p < P; ++p) {
             pl->npg[p] = int32_t(ceil_div(seq[p], SMALLW_PAGE_SIZE));
-            total += pl->npg[p];
+            pl->nlo[p] = int32_t(smallw::first_page(seq[p], in.window, in.causal, in.window_left));
+            total += pl->npg[p] - pl->nlo[p];
         }
         total *= Hkv;
         const int64_t slots = int64_t(in.num_cus) * (D == 256 ? 1 : 2);
         pl->splits.resize(P);
         pl->unit_off.assign(P + 1, 0);
         for (int p = 0; p < P; ++p) {
-            const int64_t n = pl->npg[p];
+            const int64_t n = pl->npg[p], lo = pl->nlo[p], ne = n - lo;
             int64_t S;
             if (n == 0) S = 1;
-            else if (in.split_pages > 0) S = ceil_div(n, in.split_pages);
-            else if (in.force_splits > 0) S = in.force_splits < n ? in.force_splits : n;
+            else if (in.split_pages > 0) S = ceil_div(n, in.split_pages) - lo / in.split_pages;
+            else if (in.force_splits > 0) S = in.force_splits < ne ? in.force_splits : ne;
             else {
-                S = n * slots / total;                       // share of the slots (floor)
-                if (S > n / kMinPagesPerSplit) S = n / kMinPagesPerSplit;
+                S = ne * slots / total;                      // share of the slots (floor)
+                if (S > ne / kMinPagesPerSplit) S = ne / kMinPagesPerSplit;
                 if (S < 1) S = 1;
             }
             pl->splits[p] = int32_t(S);
@@ -99,7 +101,7 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             pl->unit_off[p + 1] = int32_t(next);
             for (int64_t s = 0; s < S; ++s) {
                 int64_t pb, pe;
-                smallw::split_range(n, S, s, in.split_pages, &pb, &pe);
+                smallw::split_range(lo, n, S, s, in.split_pages, &pb, &pe);
                 if (size_t(pe - pb) > pl->max_unit_pages) pl->max_unit_pages = size_t(pe - pb);
             }
         }
@@ -149,11 +151,11 @@ int small_w_attention_plan_export(const smallw_plan* plan, int32_t* buf, size_t 
     for (int p = 0; p < P; ++p) buf[k++] = plan->splits[p];
     for (int p = 0; p <= P; ++p) buf[k++] = plan->unit_off[p];
     for (int p = 0; p < P; ++p) {
-        const int64_t npg = plan->npg[p], S = plan->splits[p];
+        const int64_t npg = plan->npg[p], lo = plan->nlo[p], S = plan->splits[p];
         for (int kvh = 0; kvh < Hkv; ++kvh)
             for (int64_t s = 0; s < S; ++s) {
                 int64_t pb, pe;
-                smallw::split_range(npg, S, s, plan->prob.split_pages, &pb, &pe);
+                smallw::split_range(lo, npg, S, s, plan->prob.split_pages, &pb, &pe);
                 buf[k++] = p;
                 buf[k++] = kvh;
                 buf[k++] = int32_t(s);

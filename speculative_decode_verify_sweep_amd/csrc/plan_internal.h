@@ -15,6 +15,7 @@ struct smallw_plan {
     bool combine = false;         // partials + combine kernel: any_split or row-exact
     std::vector<int32_t> seq;     // host lengths the plan was built from
     std::vector<int32_t> npg;     // pages per request
+    std::vector<int32_t> nlo;     // first page streamed (sliding window), else 0
     std::vector<int32_t> splits;  // S_p
     std::vector<int32_t> unit_off;// P + 1 prefix offsets of work units
     size_t part_o_off = 0, part_rec_off = 0, ws_bytes = 0;
@@ -22,16 +23,30 @@ struct smallw_plan {
 };
 
 namespace smallw {
-// Page range [*pb, *pe) of split s of a request with n pages and S splits:
-// balanced (split_pages == 0) or at multiples of split_pages.
-inline void split_range(int64_t n, int64_t S, int64_t s, int32_t split_pages, int64_t* pb,
-                        int64_t* pe) {
+// First page any row of a request needs (0 without a sliding window): row 0
+// has the lowest last key h0 = L - W (causal) or L - 1, and sees keys from
+// h0 - window_left + 1 on.
+inline int64_t first_page(int64_t L, int32_t W, int32_t causal, int32_t window_left) {
+    if (window_left <= 0 || L <= 0) return 0;
+    const int64_t lo = (causal ? L - W : L - 1) - window_left + 1;
+    return lo > 0 ? lo / SMALLW_PAGE_SIZE : 0;
+}
+
+// Page range [*pb, *pe) of split s of a request whose pages [n_lo, n) are
+// streamed in S splits: balanced (split_pages == 0) or on the absolute grid of
+// multiples of split_pages, the last piece ending at n and the first starting
+// at n_lo moved down to the piece's own page-pair grid (so that every call
+// groups the pages of a piece into the same two-page chunks).
+inline void split_range(int64_t n_lo, int64_t n, int64_t S, int64_t s, int32_t split_pages,
+                        int64_t* pb, int64_t* pe) {
     if (split_pages > 0) {
-        *pb = s * split_pages;
-        *pe = (s + 1 == S) ? n : (s + 1) * split_pages;
+        const int64_t k = n_lo / split_pages + s;
+        *pb = s == 0 ? k * split_pages + ((n_lo - k * split_pages) & ~int64_t(1))
+                     : k * split_pages;
+        *pe = (s + 1 == S) ? n : (k + 1) * split_pages;
     } else {
-        *pb = s * n / S;
-        *pe = (s + 1) * n / S;
+        *pb = n_lo + s * (n - n_lo) / S;
+        *pe = n_lo + (s + 1) * (n - n_lo) / S;
     }
 }
 // Planner core shared by small_w_attention_plan; num_cus must be resolved (> 0).

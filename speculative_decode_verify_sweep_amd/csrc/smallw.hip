@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -66,6 +67,7 @@ struct Params {
     int32_t P, W, Hq, Hkv, G, R, bt_stride, num_pages, causal;
     int32_t split_pages;  // > 0: row-exact splits at multiples of this many pages
     int32_t combine;      // 1: every row goes through partials and the combine
+    int32_t window_left;  // > 0: sliding window of this many keys per row
     float scale_log2;  // softmax scale * log2(e): scores are kept in base 2
     int32_t unit_off[SMALLW_MAX_REQS + 1];
 };
@@ -95,12 +97,21 @@ __device__ __forceinline__ Unit decode_unit(const Params& a, int u) {
     L = L < 0 ? 0 : (L > cap ? cap : L);
     r.L = L;
     const int64_t n = (L + kPage - 1) / kPage;
-    if (a.split_pages > 0) {  // row-exact: fixed boundaries, the last split runs to n
-        r.pb = int(min(int64_t(r.s) * a.split_pages, n));
-        r.pe = r.s + 1 == r.S ? int(n) : int(min(int64_t(r.s + 1) * a.split_pages, n));
+    // first page any row needs: row 0's window start (0 without a window)
+    int64_t n_lo = 0;
+    if (a.window_left > 0 && L > 0) {
+        const int64_t k0 = (a.causal ? L - a.W : L - 1) - a.window_left + 1;
+        n_lo = k0 > 0 ? k0 / kPage : 0;
+    }
+    if (a.split_pages > 0) {  // row-exact: absolute grid of pieces; the first one
+        // starts at n_lo moved down to its page-pair grid, the last ends at n
+        const int64_t k = n_lo / a.split_pages + r.s;
+        const int64_t b0 = k * a.split_pages;
+        r.pb = int(min(r.s == 0 ? b0 + ((n_lo - b0) & ~int64_t(1)) : b0, n));
+        r.pe = r.s + 1 == r.S ? int(n) : int(min((k + 1) * a.split_pages, n));
     } else {
-        r.pb = int((int64_t(r.s) * n) / r.S);
-        r.pe = int((int64_t(r.s + 1) * n) / r.S);
+        r.pb = int(n_lo + (int64_t(r.s) * (n - n_lo)) / r.S);
+        r.pe = int(n_lo + (int64_t(r.s + 1) * (n - n_lo)) / r.S);
     }
     return r;
 }
@@ -250,13 +261,17 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const int jend = min(L, un.pe * kPage);            // keys past this: not in the unit
     const int lim_lo = a.causal ? (L - a.W + 1) : L;  // first key some row may not see
     const int first_masked = min(jend, lim_lo);
+    // sliding window: keys below L - window_left are outside some row's window
+    const int win_hi = a.window_left > 0 ? L - a.window_left : INT_MIN;
 
     // ---- this wave's query rows (tile w)
     const int T = (a.R + 15) >> 4;
     const bool has_tile = w < T;
     const int r = 16 * w + ln;
     const int qi = r / a.G;
-    const int hi_tok = min(jend - 1, a.causal ? (L - a.W + qi) : (L - 1));
+    const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);  // this row's last key
+    const int hi_tok = min(jend - 1, hi_row);
+    const int lo_tok = a.window_left > 0 ? hi_row - a.window_left + 1 : INT_MIN;
     bf16x8_t qf[KS];
 
     // ---- pool page ids of this unit, staged in LDS (window of kPtab pages)
@@ -451,7 +466,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         for (int e = 0; e < 8; ++e) {
             const int t = e >> 2, j = e & 3;
             x[e] = (s4[t][0][j] + s4[t][1][j]) * (FP8 ? ksc[e] : a.scale_log2);
-            if (TAIL) x[e] = (j0 + 8 * g + e <= hi_tok) ? x[e] : -INFINITY;
+            if (TAIL) {
+                const int j = j0 + 8 * g + e;
+                x[e] = (j <= hi_tok && j >= lo_tok) ? x[e] : -INFINITY;
+            }
         }
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -527,8 +545,16 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // unit's end, or past some row's causal limit) are always a suffix.
     int c_tail = nchunks;
     while (c_tail > 0 && (un.pb + 2 * (c_tail - 1)) * kPage + 32 > first_masked) --c_tail;
+    // with a sliding window the chunks holding keys below some row's window
+    // start are a prefix, also run masked
+    int c_head = 0;
+    while (c_head < c_tail && (un.pb + 2 * c_head) * kPage < win_hi) ++c_head;
 
     int c = 0;
+    for (; c < c_head; ++c) {
+        ring_step(c);
+        if (has_tile) process(c, std::true_type{});
+    }
     for (; c < c_tail; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::false_type{});
@@ -800,6 +826,7 @@ void fill_params(Params& a, const smallw_plan* pl) {
     a.scale_log2 = pr.scale * kLog2e;
     a.split_pages = pr.split_pages;
     a.combine = pl->combine ? 1 : 0;
+    a.window_left = pr.window_left;
     for (int p = 0; p <= pr.num_reqs; ++p) a.unit_off[p] = pl->unit_off[p];
 }
 

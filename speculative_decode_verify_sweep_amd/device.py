@@ -44,7 +44,7 @@ def plan_for(w, *, num_cus: int = 0, force_splits: int = 0, split_pages: int = 0
                         max_pages_per_req=w.block_table.shape[1], causal=w.causal,
                         kv_dtype=B.SMALLW_KV_FP8_E4M3 if w.kv == "fp8" else B.SMALLW_KV_BF16,
                         scale=w.scale, num_cus=num_cus, force_splits=force_splits,
-                        split_pages=split_pages)
+                        split_pages=split_pages, window_left=getattr(w, "window_left", 0))
     return B.small_w_attention_plan(pr, w.seq_lens)
 
 

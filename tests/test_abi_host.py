@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function():
 def base_problem(**kw):
     d = dict(num_reqs=1, window=4, num_q_heads=4, num_kv_heads=1, head_dim=64, num_pages=32,
              max_pages_per_req=32, causal=1, kv_dtype=0, scale=0.0, num_cus=256,
-             force_splits=0, split_pages=0)
+             force_splits=0, split_pages=0, window_left=0)
     d.update(kw)
     return B.make_problem(**d)
 
@@ -64,6 +64,7 @@ def base_problem(**kw):
     ("num_cus", -1, B.SMALLW_EINVAL),
     ("force_splits", -2, B.SMALLW_EINVAL),
     ("split_pages", -1, B.SMALLW_EINVAL),
+    ("window_left", -5, B.SMALLW_EINVAL),
 ])
 def test_plan_rejects_bad_problems(field, value, code):
     kw = {field: value}
@@ -112,6 +113,7 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         causal = int(rng.integers(0, 2))
         force = int(rng.choice([0, 0, 0, 1, 2, 5, 64]))
         spg = int(rng.choice([0, 0, 0, 1, 7, 64])) if force == 0 else 0
+        win = int(rng.choice([0, 0, 0, 1, 37, 1000]))
         cus = int(rng.choice([1, 8, 80, 256, 304]))
         hi = int(rng.choice([40, 3000, 70000]))
         seq = rng.integers(W if causal else 0, hi, size=P).astype(np.int32)
@@ -120,11 +122,13 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         maxp = int(-(-int(seq.max()) // 16)) + int(rng.integers(0, 3)) or 1
         pr = B.make_problem(num_reqs=P, window=W, num_q_heads=Hkv * G, num_kv_heads=Hkv,
                             head_dim=D, num_pages=100000, max_pages_per_req=maxp, causal=causal,
-                            kv_dtype=fp8, num_cus=cus, force_splits=force, split_pages=spg)
+                            kv_dtype=fp8, num_cus=cus, force_splits=force, split_pages=spg,
+                            window_left=win)
         plan = sw.small_w_attention_plan(pr, seq)
         mine = sw.small_w_attention_plan_export(plan)
         pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=bool(fp8), seq_lens=seq, num_cus=cus,
-                         force_splits=force, split_pages=spg)
+                         force_splits=force, split_pages=spg, W=W, causal=bool(causal),
+                         window_left=win)
         np.testing.assert_array_equal(mine, oracle.plan_export(pl, R=W * G))
         biggest = max(pe - pb for (_, _, _, pb, pe) in pl["units"])
         assert sw.small_w_attention_plan_max_unit_pages(plan) == biggest

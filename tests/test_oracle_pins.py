@@ -63,12 +63,15 @@ def q_f64(w):
     return torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).double().numpy()
 
 
-def mask_matrix(L, W, causal, Lmax):
+def mask_matrix(L, W, causal, Lmax, window_left=0):
     i = np.arange(W)[:, None]
     j = np.arange(Lmax)[None, :]
     vis = np.broadcast_to(j < L, (W, Lmax))
+    hi = (L - W + i) if causal else np.full((W, 1), L - 1)
     if causal:
-        vis = vis & (j <= (L - W + i))
+        vis = vis & (j <= hi)
+    if window_left > 0:
+        vis = vis & (j >= hi - window_left + 1)
     return vis
 
 
@@ -80,7 +83,7 @@ def brute(w):
     out = np.zeros((w.P, w.W, w.Hq, w.D))
     lse = np.full((w.P, w.W, w.Hq), -np.inf)
     for p in range(w.P):
-        M = mask_matrix(int(w.seq_lens[p]), w.W, w.causal, Lmax)
+        M = mask_matrix(int(w.seq_lens[p]), w.W, w.causal, Lmax, w.window_left)
         for h in range(w.Hq):
             S = (Q[p, :, h, :] @ K[p, h // G].T) * w.scale      # [W][Lmax]
             S = np.where(M, S, -np.inf)
@@ -101,6 +104,10 @@ CASES = [
     dict(P=1, Hq=12, Hkv=2, D=64, ctx=(300,), W=16, causal=True),
     dict(P=2, Hq=4, Hkv=1, D=8, ctx=(17, 31), W=3, causal=True, kv="fp8"),
     dict(P=2, Hq=8, Hkv=2, D=16, ctx=(50, 9), W=4, causal=False, kv="fp8"),
+    dict(P=2, Hq=4, Hkv=2, D=8, ctx=(40, 70), W=5, causal=True, window_left=20),
+    dict(P=1, Hq=4, Hkv=1, D=16, ctx=(50,), W=6, causal=True, window_left=3),   # window < W
+    dict(P=2, Hq=4, Hkv=2, D=8, ctx=(33, 10), W=3, causal=False, window_left=17),
+    dict(P=2, Hq=4, Hkv=1, D=8, ctx=(90, 4), W=4, causal=True, kv="fp8", window_left=33),
 ]
 
 
@@ -122,7 +129,7 @@ def test_oracle_matches_torch_sdpa_fp64(case):
     Q = q_f64(w)
     for p in range(w.P):
         L = int(w.seq_lens[p])
-        M = torch.from_numpy(mask_matrix(L, w.W, w.causal, K.shape[2]))
+        M = torch.from_numpy(mask_matrix(L, w.W, w.causal, K.shape[2], w.window_left))
         kk = torch.from_numpy(K[p]).repeat_interleave(w.G, dim=0)[None]     # [1][Hq][L][D]
         vv = torch.from_numpy(V[p]).repeat_interleave(w.G, dim=0)[None]
         qq = torch.from_numpy(Q[p]).permute(1, 0, 2)[None]                   # [1][Hq][W][D]
@@ -449,3 +456,43 @@ def test_row_exact_split_partials_combine_to_the_full_result():
     co, cl = oracle.lse_combine(np.stack(parts_o), np.stack(parts_l))
     np.testing.assert_allclose(co, o, rtol=0, atol=1e-12)
     np.testing.assert_allclose(cl, l, rtol=1e-13, atol=1e-12)
+
+
+# ---------------------------------------------------------------- sliding window
+def test_window_of_one_key_returns_the_rows_own_value_and_score():
+    w = tiny(P=2, Hq=4, Hkv=2, D=16, ctx=(45, 20), W=5, causal=True, seed=81, window_left=1)
+    o, l = oracle.attention(w)
+    K, V = dense_kv(w)
+    Q = q_f64(w)
+    for p in range(w.P):
+        L = int(w.seq_lens[p])
+        for i in range(w.W):
+            j = L - w.W + i
+            for h in range(w.Hq):
+                np.testing.assert_array_equal(o[p, i, h], V[p, h // w.G, j])
+                assert l[p, i, h] == pytest.approx(w.scale * Q[p, i, h] @ K[p, h // w.G, j],
+                                                   abs=1e-12)
+
+
+def test_window_covering_every_key_changes_nothing():
+    w = tiny(P=2, Hq=4, Hkv=2, D=16, ctx=(45, 20), W=5, causal=True, seed=82)
+    o, l = oracle.attention(w)
+    o2, l2 = oracle.attention(dataclasses.replace(w, window_left=int(w.seq_lens.max())))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+
+
+def test_plan_skips_the_pages_before_the_window():
+    # 64K verify, window 4096: row 0's window starts at 65536 - 4096 + 1 = 61441
+    # -> page 3840; 4097 - 3840 = 257 pages streamed per head; 4*257 = 1028
+    # page-heads on 256 slots -> S = min(floor(257*256/1028), floor(257/8)) = 32
+    pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[65552], num_cus=256, W=16,
+                     causal=True, window_left=4096)
+    assert pl["splits"] == [32] and pl["U"] == 128
+    # split 31: 3840 + floor(31*257/32) = 3840 + 248
+    assert pl["units"][0][3:] == (3840, 3848) and pl["units"][31][3:] == (4088, 4097)
+    # row-exact pieces stay on the absolute grid: B = 100 -> pieces from 3800
+    pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[65552], num_cus=256, W=16,
+                     causal=True, window_left=4096, split_pages=100)
+    assert pl["splits"] == [41 - 38]
+    assert [u[3:] for u in pl["units"][:3]] == [(3840, 3900), (3900, 4000), (4000, 4097)]

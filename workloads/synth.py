@@ -87,6 +87,7 @@ class Workload:
     block_table: np.ndarray      # int32 [P][max_pages]
     seq_lens: np.ndarray         # int32 [P]
     seed: int
+    window_left: int = 0         # sliding window (keys per row); 0 = none
 
     @property
     def G(self) -> int:
@@ -186,4 +187,5 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
                     causal=bool(spec["causal"]), kv=spec["kv"], scale=1.0 / math.sqrt(D),
                     num_pages=pool_pages, max_pages=max_pages, q=q, k_pool=k_pool,
                     v_pool=v_pool, k_scale=k_scale, v_scale=v_scale, block_table=bt,
-                    seq_lens=np.asarray(seq, dtype=np.int32), seed=seed)
+                    seq_lens=np.asarray(seq, dtype=np.int32), seed=seed,
+                    window_left=int(spec.get("window_left", 0)))
