@@ -184,9 +184,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // k page1, v page0, v page1; 16 floats each) in a separate small array.
 // K rows are 16-byte-chunk swizzled: token row tau stores global chunk c at
 // slot c ^ h(tau), h(tau) = ((tau>>1)&12)|(tau&3) (masked to the row), so the
-// 16 lanes of one MFMA operand read hit distinct banks.  bf16 V^T rows (32
-// bytes) swap their halves when bit 2 xor bit 3 of d is set, for the same
-// reason; fp8 V^T rows are a single 16-byte chunk.
+// 16 lanes of one MFMA operand read hit distinct banks.  A bf16 V^T page
+// (rows d of 16 tokens, 32 bytes) is stored in 512-byte groups of 16 rows:
+// tokens 0..7 of rows 16k..16k+15 at 512k + 16*(d&15), tokens 8..15 256 bytes
+// later.  The two halves of a row then share a bank slot, so a lane's bank
+// depends only on its row, as in a linear read, and each 1 KiB DMA instruction
+// still reads 1 KiB of contiguous HBM.  fp8 V^T rows are a single 16-byte chunk.
 // ----------------------------------------------------------------------------
 constexpr int kSweepWaves = 8;
 constexpr int kSweepThreads = 64 * kSweepWaves;
@@ -305,9 +308,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
             goff[i] = uint32_t(tr * (2 * D) + (slot ^ hsw) * 16);
         } else {
-            const int d = qc >> 1, slot = qc & 1;
-            const int sv = ((d >> 2) ^ (d >> 3)) & 1;
-            goff[i] = uint32_t(d * 32 + (slot ^ sv) * 16);
+            // LDS slot qc = 32*a + 16*h + r of its 1 KiB block holds half h of
+            // row 16*(2*block + a) + r
+            const int d = (qc & ~31) / 2 + (qc & 15), h = (qc >> 4) & 1;
+            goff[i] = uint32_t(d * 32 + h * 16);
         }
     }
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
@@ -362,10 +366,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
                 *reinterpret_cast<bf16x8_t*>(row + ((2 * cp) ^ h) * 16) = lo;
                 *reinterpret_cast<bf16x8_t*>(row + ((2 * cp + 1) ^ h) * 16) = hi;
             } else {        // V^T: 16 codes = tokens 0..15 of d-row `within`
-                const int sv = ((within >> 2) ^ (within >> 3)) & 1;
-                uint8_t* row = dst + 2 * BF_PAGE + pg * BF_PAGE + within * 32;
-                *reinterpret_cast<bf16x8_t*>(row + sv * 16) = lo;
-                *reinterpret_cast<bf16x8_t*>(row + (sv ^ 1) * 16) = hi;
+                uint8_t* row = dst + 2 * BF_PAGE + pg * BF_PAGE + 512 * (within >> 4) +
+                               16 * (within & 15);
+                *reinterpret_cast<bf16x8_t*>(row) = lo;
+                *reinterpret_cast<bf16x8_t*>(row + 256) = hi;
             }
         }
     };
@@ -406,8 +410,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
                 kaddr[t][b] = uint32_t(row_base + 64 * ((b ^ mh) & (KS - 1)) + 16 * (g ^ ml));
         }
     }
-    const uint32_t vaddr = uint32_t(2 * BF_PAGE + (g >> 1) * BF_PAGE +
-                                    (2 * ln + ((g & 1) ^ (((ln >> 2) ^ (ln >> 3)) & 1))) * 16);
+    const uint32_t vaddr = uint32_t(2 * BF_PAGE + (g >> 1) * BF_PAGE + (g & 1) * 256 + ln * 16);
 
     f32x4 acc[DT];
 #pragma unroll
