@@ -12,6 +12,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
+# storage format codes the C oracle takes
+KV_FORMATS = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 
 
 def build_oracle(force: bool = False) -> str:
@@ -36,6 +38,8 @@ def _load():
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_decode_bf16.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_decode_e4m3.argtypes = [P, P, ctypes.c_int64]
+        lib.oracle_decode_e2m1.argtypes = [P, P, ctypes.c_int64]
+        lib.oracle_decode_e8m0.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -66,12 +70,13 @@ def attention(w, rows=None, key_lo: int = 0, key_hi: int = 2**31 - 1):
         n = rows_arr.shape[0]
         out = np.zeros((n, w.D), dtype=np.float64)
         lse = np.zeros((n,), dtype=np.float64)
-    fp8 = w.kv == "fp8"
+    fmt = KV_FORMATS[w.kv]
+    scaled = fmt != 0
     arrs = [np.ascontiguousarray(a) if a is not None else None
-            for a in (w.q, w.k_pool, w.v_pool, w.k_scale if fp8 else None,
-                      w.v_scale if fp8 else None, w.block_table, w.seq_lens)]
+            for a in (w.q, w.k_pool, w.v_pool, w.k_scale if scaled else None,
+                      w.v_scale if scaled else None, w.block_table, w.seq_lens)]
     rc = lib.oracle_attention(w.P, w.W, w.Hq, w.Hkv, w.D, w.num_pages, w.block_table.shape[1],
-                              int(w.causal), int(fp8), float(w.scale), *[_ptr(a) for a in arrs],
+                              int(w.causal), fmt, float(w.scale), *[_ptr(a) for a in arrs],
                               _ptr(rows_arr), n, int(key_lo), int(key_hi),
                               int(getattr(w, "window_left", 0)), _ptr(out), _ptr(lse))
     if rc != 0:
@@ -90,6 +95,21 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     src = np.ascontiguousarray(codes, dtype=np.uint8)
     dst = np.empty(src.shape, dtype=np.float64)
     _load().oracle_decode_e4m3(_ptr(src), _ptr(dst), src.size)
+    return dst
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """One E2M1 code per element (its low nibble) -> float64."""
+    src = np.ascontiguousarray(codes, dtype=np.uint8)
+    dst = np.empty(src.shape, dtype=np.float64)
+    _load().oracle_decode_e2m1(_ptr(src), _ptr(dst), src.size)
+    return dst
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    src = np.ascontiguousarray(codes, dtype=np.uint8)
+    dst = np.empty(src.shape, dtype=np.float64)
+    _load().oracle_decode_e8m0(_ptr(src), _ptr(dst), src.size)
     return dst
 
 

@@ -21,6 +21,10 @@
  *  - "DFlash2 leaves the paged graph fast path ...", section Scope, lists a
  *    sliding window that a path did not apply: with window_left = N > 0 a row
  *    whose last visible key is at position h sees only keys h - N + 1 .. h.
+ *  - "ChunkedSmallT re-streams full KV per query chunk", section Measurement,
+ *    times a 4-bit KV cache ("nvfp4") without defining it.  The 4-bit format
+ *    read here is OCP MXFP4: E2M1 elements in blocks of 32 consecutive head-dim
+ *    elements of one token, each block with one E8M0 power-of-two scale.
  *
  * Steps, in order: gather the request's visible pages into contiguous K and V
  * (decoded exactly to fp64), then for each row the textbook softmax attention
@@ -33,6 +37,11 @@
  *   k_pool   [num_pages][Hkv][16][D]   bf16 bits or e4m3fn bytes
  *   v_pool   [num_pages][Hkv][D][16]   (each page-head stored transposed)
  *   k_scale, v_scale  fp32 [num_pages][Hkv][16]  (fp8 only)
+ *   MXFP4 (two E2M1 codes per byte, the even element in the low nibble):
+ *   k_pool   [num_pages][Hkv][16][D/2]  byte (t, i): elements 2i, 2i+1 of token t
+ *   v_pool   [num_pages][Hkv][D][8]     byte (d, i): element d of tokens 2i, 2i+1
+ *   k_scale, v_scale  E8M0 bytes [num_pages][Hkv][16][D/32]: block b of token t
+ *            covers elements 32b .. 32b+31
  *   block_table int32 [P][bt_stride], seq_lens int32 [P]
  */
 #include <math.h>
@@ -69,20 +78,60 @@ double oracle_e4m3_to_double(uint8_t code)
     return s ? -mag : mag;
 }
 
+/* OCP MX E2M1 (4-bit: sign, 2 exponent bits with bias 1, 1 mantissa bit):
+ *   normal    (-1)^s * 2^(e-1) * (1 + m/2),  e in 1..3
+ *   subnormal (-1)^s * (m/2),                e == 0
+ * No infinities or NaN. */
+double oracle_e2m1_to_double(uint8_t nibble)
+{
+    int s = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 3;
+    int m = nibble & 1;
+    double mag = e == 0 ? m / 2.0 : ldexp(1.0 + m / 2.0, e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP MX E8M0 scale: 2^(e-127); 0xFF is NaN. */
+double oracle_e8m0_to_double(uint8_t e)
+{
+    return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127);
+}
+
+enum { ORACLE_KV_BF16 = 0, ORACLE_KV_E4M3 = 1, ORACLE_KV_MXFP4 = 2 };
+
 typedef struct {
-    int P, W, Hq, Hkv, D, num_pages, bt_stride, causal, kv_fp8;
+    int P, W, Hq, Hkv, D, num_pages, bt_stride, causal, kv_fmt;
     double scale;
     const uint16_t *q;
     const void *k_pool, *v_pool;
-    const float *k_scale, *v_scale;
+    const void *k_scale, *v_scale;
     const int32_t *block_table, *seq_lens;
 } oracle_in;
 
+/* nibble k (0 = low) of byte b */
+static uint8_t nibble(uint8_t b, int k)
+{
+    return k ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+}
+
+/* MX block scale of element d of token slot in a page-head */
+static double mx_scale(const void *scales, const oracle_in *in, int64_t page, int kvh, int slot,
+                       int d)
+{
+    int64_t idx = ((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * (in->D / 32) + d / 32;
+    return oracle_e8m0_to_double(((const uint8_t *)scales)[idx]);
+}
+
 static double k_elem(const oracle_in *in, int64_t page, int kvh, int slot, int d)
 {
+    if (in->kv_fmt == ORACLE_KV_MXFP4) {
+        int64_t byte = ((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * (in->D / 2) + d / 2;
+        uint8_t code = nibble(((const uint8_t *)in->k_pool)[byte], d & 1);
+        return oracle_e2m1_to_double(code) * mx_scale(in->k_scale, in, page, kvh, slot, d);
+    }
     int64_t idx = ((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * in->D + d;
-    if (in->kv_fp8) {
-        double sc = (double)in->k_scale[(page * in->Hkv + kvh) * ORACLE_PAGE + slot];
+    if (in->kv_fmt == ORACLE_KV_E4M3) {
+        double sc = (double)((const float *)in->k_scale)[(page * in->Hkv + kvh) * ORACLE_PAGE + slot];
         return oracle_e4m3_to_double(((const uint8_t *)in->k_pool)[idx]) * sc;
     }
     return oracle_bf16_to_double(((const uint16_t *)in->k_pool)[idx]);
@@ -90,9 +139,14 @@ static double k_elem(const oracle_in *in, int64_t page, int kvh, int slot, int d
 
 static double v_elem(const oracle_in *in, int64_t page, int kvh, int slot, int d)
 {
+    if (in->kv_fmt == ORACLE_KV_MXFP4) {
+        int64_t byte = ((page * in->Hkv + kvh) * in->D + d) * (ORACLE_PAGE / 2) + slot / 2;
+        uint8_t code = nibble(((const uint8_t *)in->v_pool)[byte], slot & 1);
+        return oracle_e2m1_to_double(code) * mx_scale(in->v_scale, in, page, kvh, slot, d);
+    }
     int64_t idx = ((page * in->Hkv + kvh) * in->D + d) * ORACLE_PAGE + slot;
-    if (in->kv_fp8) {
-        double sc = (double)in->v_scale[(page * in->Hkv + kvh) * ORACLE_PAGE + slot];
+    if (in->kv_fmt == ORACLE_KV_E4M3) {
+        double sc = (double)((const float *)in->v_scale)[(page * in->Hkv + kvh) * ORACLE_PAGE + slot];
         return oracle_e4m3_to_double(((const uint8_t *)in->v_pool)[idx]) * sc;
     }
     return oracle_bf16_to_double(((const uint16_t *)in->v_pool)[idx]);
@@ -153,15 +207,19 @@ static void attend_row(const oracle_in *in, const double *qrow, const double *K,
  * Returns 0, or -1 on an argument the library would also reject.
  */
 int oracle_attention(int P, int W, int Hq, int Hkv, int D, int num_pages, int bt_stride,
-                     int causal, int kv_fp8, double scale, const uint16_t *q,
-                     const void *k_pool, const void *v_pool, const float *k_scale,
-                     const float *v_scale, const int32_t *block_table,
+                     int causal, int kv_fmt, double scale, const uint16_t *q,
+                     const void *k_pool, const void *v_pool, const void *k_scale,
+                     const void *v_scale, const int32_t *block_table,
                      const int32_t *seq_lens, const int32_t *rows, int n_rows,
                      int key_lo, int key_hi, int window_left, double *out, double *lse)
 {
     if (P < 1 || W < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || bt_stride < 1)
         return -1;
-    if (kv_fp8 && (!k_scale || !v_scale))
+    if (kv_fmt < ORACLE_KV_BF16 || kv_fmt > ORACLE_KV_MXFP4)
+        return -1;
+    if (kv_fmt != ORACLE_KV_BF16 && (!k_scale || !v_scale))
+        return -1;
+    if (kv_fmt == ORACLE_KV_MXFP4 && D % 32)
         return -1;
     for (int p = 0; p < P; ++p) {
         int L = seq_lens[p];
@@ -175,7 +233,7 @@ int oracle_attention(int P, int W, int Hq, int Hkv, int D, int num_pages, int bt
                 return -1;
         }
     }
-    oracle_in in = {P, W, Hq, Hkv, D, num_pages, bt_stride, causal, kv_fp8, scale,
+    oracle_in in = {P, W, Hq, Hkv, D, num_pages, bt_stride, causal, kv_fmt, scale,
                     q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens};
     int G = Hq / Hkv;
     int total = rows ? n_rows : P * W * Hq;
@@ -246,6 +304,19 @@ void oracle_decode_e4m3(const uint8_t *src, double *dst, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
         dst[i] = oracle_e4m3_to_double(src[i]);
+}
+
+/* src holds one E2M1 code per byte (low nibble) */
+void oracle_decode_e2m1(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_e2m1_to_double(src[i] & 15);
+}
+
+void oracle_decode_e8m0(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_e8m0_to_double(src[i]);
 }
 
 #ifdef _OPENMP

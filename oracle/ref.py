@@ -138,11 +138,14 @@ def lse_combine(o_parts: np.ndarray, lse_parts: np.ndarray):
     return o, lse
 
 
-def kv_bytes(seq_lens, Hkv: int, D: int, kv_fp8: bool = False) -> int:
-    """Bytes of one sweep over every visible K and V element (plus fp8 scales)."""
+def kv_bytes(seq_lens, Hkv: int, D: int, kv_fp8: bool = False, kv: str | None = None) -> int:
+    """Bytes of one sweep over every visible K and V element plus their scales
+    (fp8: one fp32 per token and head; MXFP4: half a byte per element and one
+    byte per 32 elements)."""
     tokens = int(sum(int(L) for L in seq_lens))
-    elt = 1 if kv_fp8 else 2
-    per_token_head = 2 * D * elt + (2 * 4 if kv_fp8 else 0)
+    kv = kv or ("fp8" if kv_fp8 else "bf16")
+    per_token_head = {"bf16": 2 * D * 2, "fp8": 2 * D + 2 * 4,
+                      "mxfp4": 2 * (D // 2) + 2 * (D // 32)}[kv]
     return tokens * Hkv * per_token_head
 
 

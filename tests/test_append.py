@@ -4,6 +4,10 @@ then the HIP kernel (through the C ABI) against the oracle, bit for bit.
 The e4m3 encoder is pinned against torch's own float8_e4m3fn cast (a library
 routine with the same round-to-nearest-even definition), against every finite
 code's exact value, and against the midpoints between codes (ties to even).
+The MXFP4 quantizer (OCP Microscaling Formats v1.0: E2M1 elements, one E8M0
+scale per 32 elements) is pinned by the E2M1 value table, midpoints and
+saturation, worked blocks derived by hand from the format's rules, and the
+error bound and block-maximum range that those rules imply.
 """
 import dataclasses
 
@@ -53,7 +57,7 @@ def test_oracle_append_bf16_writes_exactly_the_window_slots():
     rng = np.random.default_rng(3)
     kn = to_bf16_bits(rng.normal(size=(2, 4, 2, 64)).astype(np.float32))
     vn = to_bf16_bits(rng.normal(size=(2, 4, 2, 64)).astype(np.float32))
-    kp, vp, _, _ = oracle.kv_append(P=2, W=4, Hkv=2, D=64, kv_fp8=False, k_new_bits=kn,
+    kp, vp, _, _ = oracle.kv_append(P=2, W=4, Hkv=2, D=64, kv="bf16", k_new_bits=kn,
                                     v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
                                     k_scale=None, v_scale=None, block_table=w.block_table,
                                     seq_lens=w.seq_lens, num_pages=w.num_pages)
@@ -81,6 +85,125 @@ def test_oracle_fp8_row_quantizer_matches_the_input_generator():
         np.testing.assert_array_equal(c, codes[r])
         assert np.float32(s) == scales[r]
     assert scales[5] == 1.0
+
+
+# MXFP4 (OCP Microscaling Formats v1.0): E2M1 magnitudes of codes 0..7
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_encoder_round_trips_every_code():
+    vals = np.array(E2M1 + [-x for x in E2M1])
+    vals[8] = -0.0
+    np.testing.assert_array_equal(oracle.e2m1_encode(vals), np.arange(16, dtype=np.uint8))
+
+
+def test_e2m1_encoder_sends_midpoints_to_the_even_code_and_saturates():
+    # midpoints of neighbouring values and the code that holds them
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0, 2, 2, 4, 4, 6, 6]
+    np.testing.assert_array_equal(oracle.e2m1_encode(mids), want)
+    np.testing.assert_array_equal(oracle.e2m1_encode([-x for x in mids]),
+                                  [8 | c for c in want])
+    eps = 1e-9
+    np.testing.assert_array_equal(oracle.e2m1_encode([m + eps for m in mids]), [1, 2, 3, 4, 5, 6, 7])
+    np.testing.assert_array_equal(oracle.e2m1_encode([m - eps for m in mids]), [0, 1, 2, 3, 4, 5, 6])
+    # past the largest value (6) everything below 8 saturates to it
+    np.testing.assert_array_equal(oracle.e2m1_encode([6.5, 7.0, 7.99, -7.5]), [7, 7, 7, 15])
+
+
+def _blk(vals):
+    x = np.zeros(32)
+    x[:len(vals)] = vals
+    return x
+
+
+def test_mxfp4_block_quantizer_worked_examples():
+    # amax 5 -> floor(log2 5) = 2 -> X = 0, scale byte 127; 5 ties to 4 (even)
+    c, s = oracle.mxfp4_row_quantize(_blk([5.0, 1.0, 0.3, -2.5, -0.0]))
+    assert list(s) == [127]
+    assert list(c[:6]) == [6, 2, 1, 8 | 4, 8, 0]
+    # amax 0.75 -> floor(log2 0.75) = -1 -> X = -3 (byte 124), 0.75 * 8 = 6
+    c, s = oracle.mxfp4_row_quantize(_blk([0.75, -0.1, 0.0625]))
+    assert list(s) == [124]
+    assert list(c[:3]) == [7, 8 | 2, 1]     # -0.8 is nearer -1.0 than -0.5; 0.5 exact
+    # amax exactly 4 -> X = 0; amax just under 8 saturates to 6
+    c, s = oracle.mxfp4_row_quantize(_blk([4.0, 7.96875]))
+    assert list(s) == [127] and list(c[:2]) == [6, 7]
+    # all-zero block -> scale byte 0, codes 0 (negative zero keeps its sign)
+    c, s = oracle.mxfp4_row_quantize(_blk([0.0, -0.0]))
+    assert list(s) == [0] and list(c[:3]) == [0, 8, 0]
+    # tiny block: X = floor(log2 2^-130) - 2 = -132 clamps to -127
+    c, s = oracle.mxfp4_row_quantize(_blk([2.0 ** -130, 2.0 ** -126]))
+    assert list(s) == [0] and list(c[:2]) == [0, 4]   # y = 2^-3 -> 0 and y = 2 -> 2.0
+    # two blocks of one row get their own scales
+    c, s = oracle.mxfp4_row_quantize(np.concatenate([_blk([1.0]), _blk([96.0])]))
+    assert list(s) == [127 - 2, 127 + 4] and c[0] == 6 and c[32] == 7   # y = 4 and y = 6
+
+
+def test_mxfp4_block_quantizer_error_bound_and_block_maximum():
+    rng = np.random.default_rng(9)
+    x = rng.normal(0, 1, size=(500, 256)) * rng.choice([1e-3, 1.0, 40.0], size=(500, 1))
+    x = (to_bf16_bits(x.astype(np.float32)).astype(np.uint32) << 16).view(np.float32)
+    table = np.array(E2M1 + [-v for v in E2M1])
+    for row in x.astype(np.float64):
+        c, s = oracle.mxfp4_row_quantize(row)
+        scale = np.repeat(2.0 ** (s.astype(np.int64) - 127), 32)
+        y = row / scale
+        deq = table[c]
+        # the largest |y| of each block is in [4, 8)
+        amax = np.abs(y).reshape(-1, 32).max(axis=1)
+        assert ((amax >= 4) & (amax < 8)).all()
+        # error: at most half the spacing of the grid around |y| (0.5 below 2,
+        # 1 up to 4, 2 up to 6), or the distance to 6 when saturated
+        a = np.abs(y)
+        half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+        err = np.abs(deq - y)
+        assert (err <= np.where(a > 6, a - 6, half)).all()
+        assert (np.sign(deq) * np.sign(y) >= 0).all()
+
+
+def test_oracle_append_mxfp4_writes_only_the_window_nibbles():
+    w = make_workload(None, P=2, Hq=8, Hkv=2, D=64, ctx=(41, 6), W=5, causal=True, kv="mxfp4",
+                      placement="permuted", pool_pages=12, seed=75, poison=True)
+    rng = np.random.default_rng(5)
+    kn = to_bf16_bits(rng.normal(size=(2, 5, 2, 64)).astype(np.float32))
+    vn = to_bf16_bits(rng.normal(size=(2, 5, 2, 64)).astype(np.float32))
+    kp, vp, ks, vs = oracle.kv_append(P=2, W=5, Hkv=2, D=64, kv="mxfp4", k_new_bits=kn,
+                                      v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                      k_scale=w.k_scale, v_scale=w.v_scale,
+                                      block_table=w.block_table, seq_lens=w.seq_lens,
+                                      num_pages=w.num_pages)
+    table = np.array(E2M1 + [-v for v in E2M1])
+    touched = np.zeros((w.num_pages, 2, 16), bool)
+    for p in range(2):
+        for i in range(5):
+            pos = int(w.seq_lens[p]) - 5 + i
+            pg, sl = int(w.block_table[p, pos // 16]), pos % 16
+            touched[pg, :, sl] = True
+            for h in range(2):
+                kx = (kn[p, i, h].astype(np.uint32) << 16).view(np.float32)
+                vx = (vn[p, i, h].astype(np.uint32) << 16).view(np.float32)
+                kc, ksc = oracle.mxfp4_row_quantize(kx)
+                vc, vsc = oracle.mxfp4_row_quantize(vx)
+                kcodes = np.stack([kp[pg, h, sl] & 15, kp[pg, h, sl] >> 4], -1).reshape(-1)
+                vcodes = (vp[pg, h, :, sl // 2] >> (4 * (sl % 2))) & 15
+                np.testing.assert_array_equal(kcodes, kc)
+                np.testing.assert_array_equal(vcodes, vc)
+                np.testing.assert_array_equal(ks[pg, h, sl], ksc)
+                np.testing.assert_array_equal(vs[pg, h, sl], vsc)
+                # the stored values are the quantised row
+                deq = table[kcodes] * np.repeat(2.0 ** (ksc.astype(int) - 127), 32)
+                assert np.abs(deq - kx).max() <= np.abs(kx).max() / 4 + 1e-30
+    # everything else is untouched: K rows and scales of other slots, and the
+    # other token's nibble of every value byte
+    np.testing.assert_array_equal(kp[~touched], w.k_pool[~touched])
+    np.testing.assert_array_equal(ks[~touched], w.k_scale[~touched])
+    np.testing.assert_array_equal(vs[~touched], w.v_scale[~touched])
+    for sl in range(16):
+        keep = ~touched[:, :, sl]                                       # [pages][Hkv]
+        old = (w.v_pool[:, :, :, sl // 2] >> (4 * (sl % 2))) & 15
+        new = (vp[:, :, :, sl // 2] >> (4 * (sl % 2))) & 15
+        np.testing.assert_array_equal(new[keep], old[keep])
 
 
 # ---------------------------------------------------------------- GPU: kernel parity
@@ -119,7 +242,7 @@ def test_append_kernel_matches_oracle_bitwise(kv, D):
                          d["block_table"], d["seq_lens"])
     torch.cuda.synchronize()
     fp8 = kv == "fp8"
-    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=D, kv_fp8=fp8, k_new_bits=kn,
+    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=D, kv=kv, k_new_bits=kn,
                                       v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
                                       k_scale=w.k_scale if fp8 else None,
                                       v_scale=w.v_scale if fp8 else None,
@@ -169,7 +292,7 @@ def test_append_kernel_rounds_every_tie_to_even():
                          d["block_table"], d["seq_lens"])
     torch.cuda.synchronize()
     assert int(w.block_table[0, 3]) == 3 and np.all(d["k_scale"].cpu().numpy()[3] == 1.0)
-    kp, _, _, _ = oracle.kv_append(P=1, W=W, Hkv=4, D=D, kv_fp8=True, k_new_bits=kn,
+    kp, _, _, _ = oracle.kv_append(P=1, W=W, Hkv=4, D=D, kv="fp8", k_new_bits=kn,
                                    v_new_bits=kn, k_pool=w.k_pool, v_pool=w.v_pool,
                                    k_scale=w.k_scale, v_scale=w.v_scale,
                                    block_table=w.block_table, seq_lens=w.seq_lens,
@@ -195,7 +318,7 @@ def test_append_then_verify_matches_oracle(kv):
                          d["k_scale"], d["v_scale"], d["block_table"], d["seq_lens"])
     dv.run(plan, d, ws)
     torch.cuda.synchronize()
-    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=w.D, kv_fp8=fp8, k_new_bits=kn,
+    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=w.D, kv=kv, k_new_bits=kn,
                                       v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
                                       k_scale=w.k_scale if fp8 else None,
                                       v_scale=w.v_scale if fp8 else None,

@@ -6,7 +6,8 @@
 * closed forms (Q = 0, equal keys, constant V, one key, W = 1);
 * invariants (window split, page relabelling, GQA = replicated MHA, batch =
   singles, NaN poison, split partials + log-sum-exp combine);
-* format tables (all bf16 and e4m3fn codes against torch);
+* format tables (all bf16, e4m3fn and E8M0 codes against torch; the sixteen
+  E2M1 codes against the value table of the OCP MX format);
 * numbers the pages print (tests/golden/).
 """
 import dataclasses
@@ -44,6 +45,11 @@ def dense_kv(w):
         t = np.arange(L)
         phys = w.block_table[p, t // 16]
         slot = t % 16
+        if w.kv == "mxfp4":
+            kd, vd = dense_mxfp4(w, phys, slot)
+            K[p, :, :L] = kd.transpose(1, 0, 2)
+            V[p, :, :L] = vd.transpose(1, 0, 2)
+            continue
         kc = w.k_pool[phys, :, slot, :]                  # [L][Hkv][D]
         vc = w.v_pool[phys, :, :, slot]                  # [L][Hkv][D]
         if w.kv == "fp8":
@@ -57,6 +63,27 @@ def dense_kv(w):
         K[p, :, :L] = kd.numpy().transpose(1, 0, 2)
         V[p, :, :L] = vd.numpy().transpose(1, 0, 2)
     return K, V
+
+
+# E2M1 magnitudes of codes 0..7 as the OCP MX format tabulates them
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def dense_mxfp4(w, phys, slot):
+    """K, V [L][Hkv][D] of the tokens at (phys[t], slot[t]): nibbles unpacked
+    with numpy, E2M1 by the table above, E8M0 by torch's float8_e8m0fnu."""
+    table = np.array(E2M1_TABLE + [-x for x in E2M1_TABLE])
+    kb = w.k_pool[phys, :, slot, :]                          # [L][Hkv][D/2]
+    kn = np.stack([kb & 15, kb >> 4], axis=-1).reshape(kb.shape[0], w.Hkv, w.D)
+    vb = w.v_pool[phys, :, :, slot // 2]                     # [L][Hkv][D]
+    vn = np.where((slot % 2 == 1)[:, None, None], vb >> 4, vb & 15)
+
+    def e8m0(b):
+        return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e8m0fnu).double().numpy()
+
+    ks = np.repeat(e8m0(w.k_scale[phys, :, slot, :]), 32, axis=-1)   # [L][Hkv][D]
+    vs = np.repeat(e8m0(w.v_scale[phys, :, slot, :]), 32, axis=-1)
+    return table[kn] * ks, table[vn] * vs
 
 
 def q_f64(w):
@@ -108,6 +135,9 @@ CASES = [
     dict(P=1, Hq=4, Hkv=1, D=16, ctx=(50,), W=6, causal=True, window_left=3),   # window < W
     dict(P=2, Hq=4, Hkv=2, D=8, ctx=(33, 10), W=3, causal=False, window_left=17),
     dict(P=2, Hq=4, Hkv=1, D=8, ctx=(90, 4), W=4, causal=True, kv="fp8", window_left=33),
+    dict(P=2, Hq=4, Hkv=2, D=32, ctx=(17, 45), W=3, causal=True, kv="mxfp4"),
+    dict(P=2, Hq=6, Hkv=1, D=64, ctx=(60, 3), W=5, causal=False, kv="mxfp4"),
+    dict(P=1, Hq=4, Hkv=2, D=96, ctx=(70,), W=4, causal=True, kv="mxfp4", window_left=21),
 ]
 
 
@@ -234,9 +264,9 @@ def test_sixteen_rows_equal_two_eight_row_calls():
     np.testing.assert_array_equal(o[:, 8:], oracle.attention(hi)[0])
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_page_relabelling_is_bitwise_invariant(kv):
-    w = tiny(P=2, Hq=4, Hkv=2, D=16, ctx=(50, 77), W=5, causal=True, kv=kv, seed=13, pool=20)
+    w = tiny(P=2, Hq=4, Hkv=2, D=32, ctx=(50, 77), W=5, causal=True, kv=kv, seed=13, pool=20)
     perm = np.random.default_rng(0).permutation(w.num_pages)
     inv = np.empty_like(perm)
     inv[perm] = np.arange(w.num_pages)
@@ -273,10 +303,11 @@ def test_batch_equals_single_requests():
         np.testing.assert_array_equal(l[p], l1[0])
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_nan_in_stale_slots_and_free_pages_is_never_read(kv):
-    a = tiny(P=2, Hq=4, Hkv=2, D=8, ctx=(19, 42), W=3, kv=kv, seed=16, poison=True, pool=12)
-    b = tiny(P=2, Hq=4, Hkv=2, D=8, ctx=(19, 42), W=3, kv=kv, seed=16, poison=False, pool=12)
+    D = 32 if kv == "mxfp4" else 8
+    a = tiny(P=2, Hq=4, Hkv=2, D=D, ctx=(19, 42), W=3, kv=kv, seed=16, poison=True, pool=12)
+    b = tiny(P=2, Hq=4, Hkv=2, D=D, ctx=(19, 42), W=3, kv=kv, seed=16, poison=False, pool=12)
     assert np.isnan(oracle.decode_bf16(a.k_pool)).any() if kv == "bf16" else True
     oa, la = oracle.attention(a)
     ob, lb = oracle.attention(b)
@@ -332,6 +363,52 @@ def test_e4m3_decode_matches_torch_for_every_code():
     assert nan.sum() == 2 and np.array_equal(np.isnan(mine), nan)
     np.testing.assert_array_equal(mine[~nan], ref[~nan])
     assert np.nanmax(mine) == 448.0 and mine[1] == 2.0 ** -9
+
+
+def test_e2m1_decode_matches_the_format_table():
+    codes = np.arange(16, dtype=np.uint8)
+    mine = oracle.decode_e2m1(codes)
+    np.testing.assert_array_equal(mine[:8], E2M1_TABLE)
+    np.testing.assert_array_equal(mine[8:], [-x for x in E2M1_TABLE])
+    assert np.signbit(mine[8]) and not np.signbit(mine[0])
+    # only the low nibble of each byte is a code
+    np.testing.assert_array_equal(oracle.decode_e2m1(codes | 0xF0), mine)
+
+
+def test_e8m0_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    mine = oracle.decode_e8m0(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.isnan(mine[255]) and np.isnan(ref[255]) and not np.isnan(mine[:255]).any()
+    np.testing.assert_array_equal(mine[:255], ref[:255])
+    assert mine[127] == 1.0 and mine[0] == 2.0 ** -127
+
+
+def test_mxfp4_pools_decode_like_the_same_values_stored_as_bf16():
+    """Every E2M1 value times a power of two in bf16 range is a bf16 value, so
+    an MXFP4 workload re-stored as bf16 (decoded here with the test's own table)
+    must give bitwise the oracle's MXFP4 result."""
+    w = tiny(P=2, Hq=6, Hkv=2, D=64, ctx=(40, 21), W=4, causal=True, kv="mxfp4", seed=31,
+             poison=False)
+    npg, Hkv, D = w.num_pages, w.Hkv, w.D
+    pages = np.repeat(np.arange(npg), 16)
+    slots = np.tile(np.arange(16), npg)
+    kd, vd = dense_mxfp4(w, pages, slots)                        # [npg*16][Hkv][D]
+    kbits = to_bf16_bits(kd.astype(np.float32)).reshape(npg, 16, Hkv, D).transpose(0, 2, 1, 3)
+    vbits = to_bf16_bits(vd.astype(np.float32)).reshape(npg, 16, Hkv, D).transpose(0, 2, 3, 1)
+    np.testing.assert_array_equal(oracle.decode_bf16(kbits).transpose(0, 2, 1, 3).reshape(-1, Hkv, D), kd)
+    w2 = dataclasses.replace(w, kv="bf16", k_pool=np.ascontiguousarray(kbits),
+                             v_pool=np.ascontiguousarray(vbits), k_scale=None, v_scale=None)
+    a, b = oracle.attention(w), oracle.attention(w2)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_mxfp4_kv_byte_count():
+    # per token and KV head: K and V at half a byte per element, one scale byte
+    # per 32 elements each
+    assert oracle.kv_bytes([16384 + 16], 4, 256, kv="mxfp4") == (16384 + 16) * 4 * (256 + 16)
+    assert oracle.kv_bytes([10], 1, 64, kv="mxfp4") == 10 * (64 + 4)
 
 
 # ---------------------------------------------------------------- counts and the pages' numbers

@@ -6,12 +6,18 @@ Storage layout (the library's documented layout):
   v_pool    [num_pages][Hkv][D][16]     each page-head stored transposed
   k_scale   fp32 [num_pages][Hkv][16]   fp8 only (dequantised value = code * scale)
   v_scale   fp32 [num_pages][Hkv][16]
+  MXFP4 (kv = "mxfp4"): uint8, two E2M1 codes per byte, the even element in the
+  low nibble; k_pool [num_pages][Hkv][16][D/2] (byte i of token t: elements 2i,
+  2i+1), v_pool [num_pages][Hkv][D][8] (byte i of row d: tokens 2i, 2i+1),
+  k_scale / v_scale E8M0 bytes [num_pages][Hkv][16][D/32], one per 32-element
+  block of a token's row
   block_table int32 [P][max_pages_per_req]   (-1 past a request's last page)
   seq_lens    int32 [P]   (context + window: the window's own K/V rows are
               already in the pool, so a verify row i sits at position L - W + i)
 
 Pool pages that no block table references, and the slots of a request's last
-page past its length, hold NaN so a read of them would show in the output.
+page past its length, hold NaN so a read of them would show in the output (for
+MXFP4, whose codes have no NaN, the NaN scale byte 0xFF).
 """
 from __future__ import annotations
 
@@ -45,6 +51,10 @@ CONFIGS = {
     # pages randomly placed in a 10000-page pool
     "fp8": dict(P=4, Hq=24, Hkv=4, D=256, ctx=(8192, 16384, 32768, 65536), W=16, causal=True,
                 kv="fp8", placement="permuted", pool_pages=10000),
+    # batch 1, 24 q / 4 KV heads, D 256, 16K context, W=16 causal, 4-bit (MXFP4)
+    # KV, pages in order
+    "fp4_16k": dict(P=1, Hq=24, Hkv=4, D=256, ctx=(16384,), W=16, causal=True, kv="mxfp4",
+                    placement="in_order", pool_pages=None),
 }
 
 CONFIG_SEED_BASE = 20261202
@@ -75,7 +85,7 @@ class Workload:
     Hkv: int
     D: int
     causal: bool
-    kv: str                      # "bf16" | "fp8"
+    kv: str                      # "bf16" | "fp8" | "mxfp4"
     scale: float
     num_pages: int
     max_pages: int
@@ -109,7 +119,9 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
     """Build a seeded workload.  Any recipe field may be overridden by keyword,
     e.g. make_workload("tiny", W=2, Hq=2, Hkv=1, D=8, ctx=(5,)) for tiny cases.
 
-    Value draws: Q, K, V ~ N(0, 1) in fp32, rounded to the storage format.
+    Value draws: Q, K, V ~ N(0, 1) in fp32, rounded to the storage format
+    (bf16, or e4m3 with a per-row scale).  MXFP4 K and V are drawn as codes:
+    every E2M1 code equally likely, E8M0 block scales uniform over 2^-3 .. 2^0.
     """
     spec = dict(CONFIGS[name]) if name else {}
     spec.update(over)
@@ -129,6 +141,7 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
     pool_pages = spec.get("pool_pages") or max(need, 1)
     pool_pages = max(pool_pages, need)
     fp8 = spec["kv"] == "fp8"
+    fp4 = spec["kv"] == "mxfp4"
 
     q = to_bf16_bits(rng.standard_normal((P, Wn, Hq, D), dtype=np.float32))
 
@@ -143,7 +156,12 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
         bt[p, :npg[p]] = order[pos:pos + npg[p]]
         pos += npg[p]
 
-    if fp8:
+    if fp4:
+        k_pool = np.full((pool_pages, Hkv, PAGE, D // 2), 0x77, dtype=np.uint8)
+        v_pool = np.full((pool_pages, Hkv, D, PAGE // 2), 0x77, dtype=np.uint8)
+        k_scale = np.full((pool_pages, Hkv, PAGE, D // 32), 0xFF, dtype=np.uint8)
+        v_scale = np.full((pool_pages, Hkv, PAGE, D // 32), 0xFF, dtype=np.uint8)
+    elif fp8:
         k_pool = np.full((pool_pages, Hkv, PAGE, D), 0x7F, dtype=np.uint8)
         v_pool = np.full((pool_pages, Hkv, D, PAGE), 0x7F, dtype=np.uint8)
         k_scale = np.full((pool_pages, Hkv, PAGE), np.nan, dtype=np.float32)
@@ -158,10 +176,31 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
         if fp8:
             k_scale[...] = 1.0
             v_scale[...] = 1.0
+        if fp4:
+            k_scale[...] = 127
+            v_scale[...] = 127
 
     for p in range(P):
         L = seq[p]
         if L == 0:
+            continue
+        if fp4:
+            # codes [Hkv][L][D], scales [Hkv][L][D/32]
+            kc = rng.integers(0, 16, size=(Hkv, L, D), dtype=np.uint8)
+            vc = rng.integers(0, 16, size=(Hkv, L, D), dtype=np.uint8)
+            ksc = rng.integers(124, 128, size=(Hkv, L, D // 32), dtype=np.uint8)
+            vsc = rng.integers(124, 128, size=(Hkv, L, D // 32), dtype=np.uint8)
+            for n in range(npg[p]):
+                t0, t1 = n * PAGE, min(L, (n + 1) * PAGE)
+                phys = bt[p, n]
+                k_pool[phys, :, :t1 - t0, :] = kc[:, t0:t1, 0::2] | (kc[:, t0:t1, 1::2] << 4)
+                k_scale[phys, :, :t1 - t0, :] = ksc[:, t0:t1]
+                v_scale[phys, :, :t1 - t0, :] = vsc[:, t0:t1]
+                for t in range(t0, t1):
+                    slot = t - t0
+                    sh = 4 * (slot & 1)
+                    cur = v_pool[phys, :, :, slot // 2] & np.uint8(0xF0 >> sh)
+                    v_pool[phys, :, :, slot // 2] = cur | (vc[:, t, :] << sh)
             continue
         kl = rng.standard_normal((Hkv, L, D), dtype=np.float32)
         vl = rng.standard_normal((Hkv, L, D), dtype=np.float32)
