@@ -37,7 +37,7 @@ CTX = 65536
 WINDOWS = (1, 8, 12, 16)
 COUNTERS = os.path.join(ROOT, "profiles", "sweep_verify64k_w16_counters.json")
 SWEEP_SRC = os.path.join(ROOT, "speculative_decode_verify_sweep_amd", "csrc", "smallw.hip")
-SWEEP_KERNEL = "sweep_kernel<256, 4, false>"   # bf16 KV, head_dim 256, 4-chunk ring
+SWEEP_KERNEL = "sweep_kernel<256, 4, 0>"   # bf16 KV (format code 0), head_dim 256, 4-chunk ring
 COMBINE_KERNEL = "combine_kernel<256>"
 
 
@@ -45,9 +45,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kv_bytes(seq_lens, hkv, d, elt=2):
-    """K and V bytes of one sweep over every visible token (the pages' GB/s numerator)."""
-    return int(sum(int(x) for x in seq_lens)) * hkv * 2 * d * elt
+def kv_bytes(seq_lens, hkv, d, kv="bf16"):
+    """K and V bytes of one sweep over every visible token (the pages' GB/s
+    numerator), with the scales of the 8-bit (one fp32 per token and head for
+    K and V) and 4-bit (one byte per 32 elements) formats."""
+    per = {"bf16": 4 * d, "fp8": 2 * d + 8, "mxfp4": d + 2 * (d // 32)}[kv]
+    return int(sum(int(x) for x in seq_lens)) * hkv * per
 
 
 HOST_MARK = b"// ==== host side:"
@@ -254,6 +257,10 @@ def main():
                  ("verify16k W=1", dict(name="verify16k", W=1)),
                  ("draft P=8 W=9 non-causal", dict(name="draft")),
                  ("fp8 P=4 8K..64K W=16", dict(name="fp8")),
+                 ("MXFP4 16K W=16", dict(name="fp4_16k", W=16)),
+                 ("MXFP4 16K W=8", dict(name="fp4_16k", W=8)),
+                 ("MXFP4 16K W=1", dict(name="fp4_16k", W=1)),
+                 ("verify16k W=8", dict(name="verify16k", W=8)),
                  ("verify64k W=16 row-exact, 65-page splits",
                   dict(name="verify64k", W=16, split_pages=65)),
                  ("verify64k W=16 sliding window 4096",
@@ -273,9 +280,7 @@ def main():
             s_us = statistics.median([x[1] for x in r]) * 1e3
             seen = [int(L) - max(0, int(L) - wl.W - wl.window_left + 1) if wl.window_left
                     else int(L) for L in wl.seq_lens]      # keys some row can see
-            b = kv_bytes(seen, wl.Hkv, wl.D, elt=1 if wl.kv == "fp8" else 2)
-            if wl.kv == "fp8":
-                b += int(sum(int(x) for x in wl.seq_lens)) * wl.Hkv * 8   # k and v scales
+            b = kv_bytes(seen, wl.Hkv, wl.D, wl.kv)
             others[label] = {"us_per_call": round(t_us, 2), "sweep_us": round(s_us, 2),
                              "kv_bytes": b, "kv_GBps": round(b / (t_us * 1e-6) / 1e9, 1),
                              "units": int(sw_export_units(pl))}

@@ -43,6 +43,18 @@
  *                                            transposed (d-major)
  *   k_scale      fp32 [num_pages][Hkv][16]   fp8 only: value = code * scale
  *   v_scale      fp32 [num_pages][Hkv][16]   fp8 only
+ * MXFP4 pools (kv_dtype SMALLW_KV_MXFP4, head_dim 128 or 256) hold two E2M1
+ * codes per byte, the even element in the low nibble:
+ *   k_pool       uint8 [num_pages][Hkv][16][D/2]   byte i of token t: elements
+ *                                                  2i, 2i+1 of its row
+ *   v_pool       uint8 [num_pages][Hkv][D][8]      byte i of row d: element d
+ *                                                  of tokens 2i, 2i+1
+ *   k_scale      uint8 E8M0 [num_pages][Hkv][16][D/32]: block b of token t
+ *   v_scale      uint8 E8M0 [num_pages][Hkv][16][D/32]  scales elements
+ *                32b .. 32b+31 of that token's row by 2^(e-127)
+ * ("ChunkedSmallT re-streams full KV per query chunk", section Measurement,
+ * times a 4-bit KV cache; the format here is OCP MXFP4: E2M1 values
+ * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, 32-element blocks, E8M0 scales.)
  *   block_table  int32 [P][max_pages_per_req]; entry n of row p is the pool
  *                page holding tokens [16n, 16n+16) of request p
  *   seq_lens     int32 [P]; must equal the host lengths given to the plan
@@ -79,14 +91,14 @@ extern "C" {
 #define SMALLW_MAX_REQS      256
 #define SMALLW_MAX_ROWS      128  /* W * (Hq / Hkv) */
 
-typedef enum { SMALLW_KV_BF16 = 0, SMALLW_KV_FP8_E4M3 = 1 } smallw_kv_dtype;
+typedef enum { SMALLW_KV_BF16 = 0, SMALLW_KV_FP8_E4M3 = 1, SMALLW_KV_MXFP4 = 2 } smallw_kv_dtype;
 
 typedef struct smallw_problem {
     int32_t num_reqs;          /* P, 1..SMALLW_MAX_REQS                              */
     int32_t window;            /* W, 1..SMALLW_MAX_WINDOW                            */
     int32_t num_q_heads;       /* Hq >= 1                                            */
     int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0, W*Hq/Hkv <= 128           */
-    int32_t head_dim;          /* D: 64, 128 or 256                                  */
+    int32_t head_dim;          /* D: 64, 128 or 256 (MXFP4: 128 or 256)              */
     int32_t page_size;         /* must be 16                                         */
     int32_t num_pages;         /* pool capacity in pages, >= 1                       */
     int32_t max_pages_per_req; /* block_table row stride, >= 1                       */
@@ -146,15 +158,15 @@ size_t small_w_attention_workspace_bytes(const smallw_plan* plan);
  * default stream).  Launches the split-K sweep kernel and, when any request
  * is split, the log-sum-exp combine kernel.  No host synchronisation and no
  * allocation, so the call can be captured in a HIP graph.  All pointers are
- * device pointers in the layouts above; k_scale / v_scale are required for
- * fp8 KV and ignored otherwise.  workspace must be 256-byte aligned and hold
+ * device pointers in the layouts above; k_scale / v_scale (fp32 for fp8,
+ * E8M0 bytes for MXFP4) are required for those formats and ignored for bf16.  workspace must be 256-byte aligned and hold
  * small_w_attention_workspace_bytes(plan) bytes (may be NULL when that is 0);
  * it is scratch owned by the caller and may be reused between calls on the
  * same stream.  Returns SMALLW_EINVAL (null pointer / plan), SMALLW_EWORKSPACE,
  * or SMALLW_EDEVICE (launch failure).
  */
 int small_w_attention_run(const smallw_plan* plan, const void* q, const void* k_pool,
-                          const void* v_pool, const float* k_scale, const float* v_scale,
+                          const void* v_pool, const void* k_scale, const void* v_scale,
                           const int32_t* block_table, const int32_t* seq_lens, void* out,
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -166,8 +178,8 @@ int small_w_attention_run(const smallw_plan* plan, const void* q, const void* k_
  * may be NULL.  For timing the kernels in place, as a kernel profiler would.
  */
 int small_w_attention_run_events(const smallw_plan* plan, const void* q, const void* k_pool,
-                                 const void* v_pool, const float* k_scale,
-                                 const float* v_scale, const int32_t* block_table,
+                                 const void* v_pool, const void* k_scale,
+                                 const void* v_scale, const int32_t* block_table,
                                  const int32_t* seq_lens, void* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* ev_start, void* ev_sweep_done, void* ev_end);
@@ -207,17 +219,22 @@ size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan);
  *   k_new, v_new  device bf16 [P][W][Hkv][D]: token i of request p sits at
  *                 position pos = L_p - W + i (requests with L_p < W - i skip it)
  *   k_pool, v_pool, k_scale, v_scale, block_table, seq_lens: as for
- *                 small_w_attention_run (scales required for an e4m3 pool)
+ *                 small_w_attention_run (scales required for e4m3 and MXFP4)
  * The K row goes to slot pos % 16 of page block_table[p][pos / 16], the V row
  * to the same slot of the transposed value page.  bf16 pools get the bits as
  * given.  e4m3 pools get, per (token, KV head) row, scale = amax|x| / 448 (1.0
  * for an all-zero row) and codes = round-to-nearest-even of x / scale on the
- * OCP e4m3fn grid, computed in fp32 with IEEE division.  Rows of different
- * tokens must map to different slots.  Returns SMALLW_EINVAL (null pointer or
+ * OCP e4m3fn grid, computed in fp32 with IEEE division.  MXFP4 pools get, per
+ * 32-element block of a row, the E8M0 byte X + 127 with X = floor(log2 amax)
+ * - 2 clamped to [-127, 127] (0 for an all-zero block) and codes = the E2M1
+ * value nearest x / 2^X, ties to the even code, saturating at 6, with the sign
+ * of x (OCP Microscaling Formats v1.0 conversion); only the window tokens'
+ * nibbles of the shared value bytes change.  Rows of different tokens must map
+ * to different slots.  Returns SMALLW_EINVAL (null pointer or
  * plan), SMALLW_EDEVICE (launch failure).
  */
 int small_w_kv_append(const smallw_plan* plan, const void* k_new, const void* v_new,
-                      void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                      void* k_pool, void* v_pool, void* k_scale, void* v_scale,
                       const int32_t* block_table, const int32_t* seq_lens, void* stream);
 
 /* Release a plan (NULL is allowed). */

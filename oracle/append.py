@@ -114,7 +114,8 @@ def kv_append(*, P, W, Hkv, D, k_new_bits, v_new_bits, k_pool, v_pool, k_scale,
     k_new_bits / v_new_bits: uint16 bf16 bits [P][W][Hkv][D].  Pools and scales
     in the library's layouts for kv = "bf16" | "fp8" | "mxfp4" (uint8 bytes
     for the last two; the MXFP4 value pool packs tokens 2i, 2i+1 of a row d
-    into byte i, the even token in the low nibble)."""
+    into byte i, the even token in the low nibble, and its scales are
+    block-major [page][head][D/32][16])."""
     assert kv in ("bf16", "fp8", "mxfp4")
     kp, vp = k_pool.copy(), v_pool.copy()
     ks = None if k_scale is None else k_scale.copy()
@@ -145,7 +146,7 @@ def kv_append(*, P, W, Hkv, D, k_new_bits, v_new_bits, k_pool, v_pool, k_scale,
                     keep = np.uint8(0xF0 >> sh)
                     vp[page, h, :, slot // 2] = (vp[page, h, :, slot // 2] & keep) | (vc << sh)
                     ks[page, h, slot, :] = kscl
-                    vs[page, h, slot, :] = vscl
+                    vs[page, h, :, slot] = vscl          # V scales block-major
                 else:
                     kx = (kb.astype(np.uint32) << 16).view(np.float32)
                     vx = (vb.astype(np.uint32) << 16).view(np.float32)

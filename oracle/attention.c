@@ -40,8 +40,10 @@
  *   MXFP4 (two E2M1 codes per byte, the even element in the low nibble):
  *   k_pool   [num_pages][Hkv][16][D/2]  byte (t, i): elements 2i, 2i+1 of token t
  *   v_pool   [num_pages][Hkv][D][8]     byte (d, i): element d of tokens 2i, 2i+1
- *   k_scale, v_scale  E8M0 bytes [num_pages][Hkv][16][D/32]: block b of token t
- *            covers elements 32b .. 32b+31
+ *   k_scale  E8M0 bytes [num_pages][Hkv][16][D/32]: block b of token t covers
+ *            elements 32b .. 32b+31 of its row
+ *   v_scale  E8M0 bytes [num_pages][Hkv][D/32][16]: the same blocks, stored
+ *            block-major like the transposed value page
  *   block_table int32 [P][bt_stride], seq_lens int32 [P]
  */
 #include <math.h>
@@ -114,11 +116,14 @@ static uint8_t nibble(uint8_t b, int k)
     return k ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
 }
 
-/* MX block scale of element d of token slot in a page-head */
+/* MX block scale of element d of token slot in a page-head: K scales are
+ * token-major [16][D/32], V scales block-major [D/32][16] */
 static double mx_scale(const void *scales, const oracle_in *in, int64_t page, int kvh, int slot,
-                       int d)
+                       int d, int block_major)
 {
-    int64_t idx = ((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * (in->D / 32) + d / 32;
+    int64_t head = (page * in->Hkv + kvh) * ORACLE_PAGE * (in->D / 32);
+    int64_t idx = block_major ? head + (int64_t)(d / 32) * ORACLE_PAGE + slot
+                              : head + (int64_t)slot * (in->D / 32) + d / 32;
     return oracle_e8m0_to_double(((const uint8_t *)scales)[idx]);
 }
 
@@ -127,7 +132,7 @@ static double k_elem(const oracle_in *in, int64_t page, int kvh, int slot, int d
     if (in->kv_fmt == ORACLE_KV_MXFP4) {
         int64_t byte = ((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * (in->D / 2) + d / 2;
         uint8_t code = nibble(((const uint8_t *)in->k_pool)[byte], d & 1);
-        return oracle_e2m1_to_double(code) * mx_scale(in->k_scale, in, page, kvh, slot, d);
+        return oracle_e2m1_to_double(code) * mx_scale(in->k_scale, in, page, kvh, slot, d, 0);
     }
     int64_t idx = ((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * in->D + d;
     if (in->kv_fmt == ORACLE_KV_E4M3) {
@@ -142,7 +147,7 @@ static double v_elem(const oracle_in *in, int64_t page, int kvh, int slot, int d
     if (in->kv_fmt == ORACLE_KV_MXFP4) {
         int64_t byte = ((page * in->Hkv + kvh) * in->D + d) * (ORACLE_PAGE / 2) + slot / 2;
         uint8_t code = nibble(((const uint8_t *)in->v_pool)[byte], slot & 1);
-        return oracle_e2m1_to_double(code) * mx_scale(in->v_scale, in, page, kvh, slot, d);
+        return oracle_e2m1_to_double(code) * mx_scale(in->v_scale, in, page, kvh, slot, d, 1);
     }
     int64_t idx = ((page * in->Hkv + kvh) * in->D + d) * ORACLE_PAGE + slot;
     if (in->kv_fmt == ORACLE_KV_E4M3) {

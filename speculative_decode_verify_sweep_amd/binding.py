@@ -22,6 +22,7 @@ SMALLW_EDEVICE = -4
 SMALLW_ENOMEM = -5
 SMALLW_KV_BF16 = 0
 SMALLW_KV_FP8_E4M3 = 1
+SMALLW_KV_MXFP4 = 2
 
 
 class SmallwError(RuntimeError):
@@ -179,7 +180,7 @@ def small_w_kv_append(plan: Plan, k_new, v_new, k_pool, v_pool, k_scale, v_scale
                       block_table, seq_lens, stream=None) -> None:
     """Write the plan's W window tokens (bf16 [P][W][Hkv][D] device tensors) into
     their pool slots, quantising to e4m3 with per-(token, KV-head) scales for an
-    fp8 pool.  Tensors are device tensors in the documented layouts."""
+    fp8 or MXFP4 pool.  Tensors are device tensors in the documented layouts."""
     rc = lib().small_w_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
                                  _ptr(seq_lens), _stream(stream))

@@ -121,20 +121,21 @@ hipError_t launch_append(const smallw_plan* pl, const AppendParams& a, hipStream
 }  // namespace
 
 extern "C" int small_w_kv_append(const smallw_plan* pl, const void* k_new, const void* v_new,
-                                 void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                 void* k_pool, void* v_pool, void* k_scale, void* v_scale,
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  void* stream) {
     if (!pl || !k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens)
         return SMALLW_EINVAL;
-    const bool fp8 = pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3;
-    if (fp8 && (!k_scale || !v_scale)) return SMALLW_EINVAL;
+    const bool scaled = pl->prob.kv_dtype != SMALLW_KV_BF16;
+    if (scaled && (!k_scale || !v_scale)) return SMALLW_EINVAL;
+    if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) return SMALLW_EUNSUPPORTED;
     AppendParams a;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
     a.k_pool = static_cast<uint8_t*>(k_pool);
     a.v_pool = static_cast<uint8_t*>(v_pool);
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
+    a.k_scale = static_cast<float*>(k_scale);
+    a.v_scale = static_cast<float*>(v_scale);
     a.bt = block_table;
     a.seq = seq_lens;
     a.P = pl->prob.num_reqs;

@@ -37,13 +37,16 @@ int validate(const smallw_problem& pr, const int32_t* seq) {
         return SMALLW_EINVAL;
     if (pr.force_splits > 0 && pr.split_pages > 0) return SMALLW_EINVAL;
     if (pr.causal != 0 && pr.causal != 1) return SMALLW_EINVAL;
-    if (pr.kv_dtype != SMALLW_KV_BF16 && pr.kv_dtype != SMALLW_KV_FP8_E4M3) return SMALLW_EINVAL;
+    if (pr.kv_dtype != SMALLW_KV_BF16 && pr.kv_dtype != SMALLW_KV_FP8_E4M3 &&
+        pr.kv_dtype != SMALLW_KV_MXFP4)
+        return SMALLW_EINVAL;
     if (std::isnan(pr.scale) || std::isinf(pr.scale)) return SMALLW_EINVAL;
     if (pr.num_q_heads % pr.num_kv_heads != 0) return SMALLW_EINVAL;
     if (pr.num_reqs > SMALLW_MAX_REQS) return SMALLW_EUNSUPPORTED;
     if (pr.window > SMALLW_MAX_WINDOW) return SMALLW_EUNSUPPORTED;
     if (pr.page_size != SMALLW_PAGE_SIZE) return SMALLW_EUNSUPPORTED;
     if (pr.head_dim != 64 && pr.head_dim != 128 && pr.head_dim != 256) return SMALLW_EUNSUPPORTED;
+    if (pr.kv_dtype == SMALLW_KV_MXFP4 && pr.head_dim == 64) return SMALLW_EUNSUPPORTED;
     const int64_t rows = int64_t(pr.window) * (pr.num_q_heads / pr.num_kv_heads);
     if (rows > SMALLW_MAX_ROWS) return SMALLW_EUNSUPPORTED;
     if (!seq) return SMALLW_EINVAL;

@@ -36,6 +36,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPage = SMALLW_PAGE_SIZE;
 constexpr int kThreads = 256;
@@ -226,25 +227,99 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int D, int NS, bool FP8>
+// Byte J of w (two E2M1 codes, the low nibble first) -> 2 bf16, each times
+// 2^(e-127) for the E8M0 byte e.  The convert takes only the exponent field of
+// its fp32 scale operand, which e << 23 sets, so this is exact for every byte
+// (0 gives 2^-127, 0xFF NaN).  The pair is moved as a whole word: reading an
+// element out of the convert's 2 x bf16 result can lose its upper half.
+template <int J>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t w, uint32_t e8) {
+    return __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, __builtin_bit_cast(float, e8 << 23), J));
+}
+// byte J of w with its low code times 2^(e_lo-127) and its high code times
+// 2^(e_hi-127): both halves are converted with each scale and one of each kept
+template <int J>
+__device__ __forceinline__ uint32_t e2m1x2_two_scales(uint32_t w, uint32_t e_lo, uint32_t e_hi) {
+    return (e2m1x2_to_bf16<J>(w, e_lo) & 0xFFFFu) | (e2m1x2_to_bf16<J>(w, e_hi) & 0xFFFF0000u);
+}
+
+// Where 16-byte piece q of an MXFP4 ring stage comes from: array (0 K codes,
+// 1 V codes, 2 K scales, 3 V scales), page of the chunk (0/1) and byte offset
+// inside that page-head.  Stage layout (bytes):
+//   [0, 16D)    K codes of both pages in blocks (rg, g) of D bytes: row group
+//               rg = 8-token group (rg >> 1 = page), g = MFMA lane group, each
+//               block holding bytes [g D/8, (g+1) D/8) of the group's 8 rows.
+//               Row x of a group sits at position x ^ 4 (odd rg); at D = 256
+//               its two 16-byte halves swap for rg >= 2; at D = 128 block g of
+//               rg >= 2 holds lane group g ^ 1.  A lane's bank then depends
+//               only on its row (D = 256), and every 1 KiB of the stage is
+//               1 KiB of contiguous HBM.
+//   [16D, 32D)  V^T codes, page 0 then page 1 (8D each: row d of 8 bytes =
+//               tokens 0..15)
+//   [32D, 34D)  E8M0 scales, K page 0, K page 1 ([16 tokens][D/32 blocks]),
+//               V page 0, V page 1 ([D/32 blocks][16 tokens]), D/2 each
+template <int D>
+__device__ __forceinline__ void fp4_piece(int q, int& arr, int& pg, int& off) {
+    const int o = 16 * q;
+    if (o < 16 * D) {
+        const int b = o / D, rg = b >> 2, within = o % D;
+        pg = rg >> 1;
+        int x, byte;
+        if constexpr (D == 256) {
+            const int g = b & 3;
+            x = (within >> 5) ^ (4 * (rg & 1));
+            byte = 32 * g + 16 * (((within >> 4) & 1) ^ (rg >> 1));
+        } else {
+            const int g = (b & 3) ^ (rg >> 1);
+            x = (within >> 4) ^ (4 * (rg & 1));
+            byte = 16 * g;
+        }
+        arr = 0;
+        off = (8 * (rg & 1) + x) * (D / 2) + byte;
+    } else if (o < 32 * D) {
+        const int o2 = o - 16 * D;
+        pg = o2 / (8 * D);
+        arr = 1;
+        off = o2 % (8 * D);
+    } else {
+        const int o3 = o - 32 * D, blk = o3 / (D / 2);
+        arr = 2 + (blk >> 1);
+        pg = blk & 1;
+        off = o3 % (D / 2);
+    }
+}
+
+template <int D, int NS, int KV>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
+    constexpr bool FP8 = KV == SMALLW_KV_FP8_E4M3;
+    constexpr bool FP4 = KV == SMALLW_KV_MXFP4;
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
     constexpr int BF_PAGE = 32 * D;                // bf16 page-head of K (or V^T) in LDS
     constexpr int BF_STAGE = 4 * BF_PAGE;          // K0 K1 V0 V1, bf16
-    constexpr int ST_PAGE = FP8 ? 16 * D : BF_PAGE;    // page-head as streamed from HBM
-    constexpr int ST_STAGE = 4 * ST_PAGE;
+    // page-head codes as streamed from HBM; an MXFP4 stage also holds its scales
+    constexpr int ST_PAGE = FP4 ? 8 * D : (FP8 ? 16 * D : BF_PAGE);
+    constexpr int ST_STAGE = FP4 ? 34 * D : 4 * ST_PAGE;
     constexpr int RING = NS * ST_STAGE;            // DMA ring
-    constexpr int LDS_BYTES = RING + (FP8 ? 2 * BF_STAGE : 0);  // + fp8 decode staging
-    constexpr int REG_INST = ST_PAGE / 1024;       // DMA instructions per region
+    // + decode staging: fp8 K and V, MXFP4 V only (two chunks each, bf16)
+    constexpr int LDS_BYTES = RING + (FP8 ? 2 * BF_STAGE : 0) + (FP4 ? 4 * BF_PAGE : 0);
+    constexpr int REG_INST = FP4 ? 1 : ST_PAGE / 1024;  // DMA instructions per region
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
     constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
     constexpr int CPR = D / 8;                     // 16-byte bf16 chunks per K token row
     // chunks in flight ahead of the one being computed: fp8 frees a ring slot
     // when its chunk is decoded, one iteration before the chunk is computed
+    // (MXFP4 decodes only V then, and reads K from the ring slot itself)
     constexpr int AHEAD = FP8 ? NS : NS - 1;
     constexpr int NSS = FP8 ? NS + 1 : 1;          // fp8 scale slots: chunks c .. c+NS live
+    // MXFP4: 16-byte pieces per stage, DMA instructions per chunk (instruction
+    // i is issued by wave i mod 8) and the most any wave issues
+    constexpr int N16 = ST_STAGE / 16;
+    constexpr int NI4 = (N16 + 63) / 64;
+    constexpr int MI4 = (NI4 + kSweepWaves - 1) / kSweepWaves;
     static_assert(REG_INST >= 1 && NS >= (FP8 ? 3 : 2), "config");
+    static_assert(!FP4 || D == 128 || D == 256, "MXFP4 serves D = 128 and 256");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
     __shared__ __attribute__((aligned(16))) float scl[FP8 ? NSS : 1][64];
@@ -292,9 +367,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const int region = w & 3;
     const int region_pg = region & 1;
     const bool region_v = region >= 2;
-    const bool issues_kv = SPLIT || w < 4;
+    const bool issues_kv = !FP4 && (SPLIT || w < 4);
     const bool issues_scale = FP8 && w == kSweepWaves - 1;
-    const int nload = (issues_kv ? LPW : 0) + (issues_scale ? 1 : 0);  // per chunk
+    const int nload = FP4 ? (NI4 - w + kSweepWaves - 1) / kSweepWaves   // per chunk
+                          : (issues_kv ? LPW : 0) + (issues_scale ? 1 : 0);
     const int ibase = SPLIT ? (w >> 2) * LPW : 0;
     uint32_t goff[LPW];
 #pragma unroll
@@ -314,6 +390,16 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             goff[i] = uint32_t(d * 32 + h * 16);
         }
     }
+    // MXFP4: this wave's pieces (lane l of its j-th instruction i = w + 8j)
+    int arr4[MI4], pg4[MI4], off4[MI4];
+    bool has4[MI4];
+#pragma unroll
+    for (int j = 0; j < MI4; ++j) {
+        const int q = 64 * (w + kSweepWaves * j) + l;
+        has4[j] = FP4 && q < N16;
+        arr4[j] = pg4[j] = off4[j] = 0;
+        if (has4[j]) fp4_piece<D>(q, arr4[j], pg4[j], off4[j]);
+    }
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
     const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
     const uint8_t* const pool = region_v ? a.v : a.k;
@@ -325,6 +411,26 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     asm volatile("" : "+s"(kscale), "+s"(vscale));
 
     auto issue_chunk = [&](int c) {
+        if constexpr (FP4) {
+            int n1 = 2 * c + 1;
+            if (n1 >= npages) n1 = 2 * c;  // absent second page: reload the first, masked later
+            const int phys0 = __builtin_amdgcn_readfirstlane(ptab[2 * c - tbase]);
+            const int phys1 = __builtin_amdgcn_readfirstlane(ptab[n1 - tbase]);
+            const uint8_t* ks8 = reinterpret_cast<const uint8_t*>(kscale);
+            const uint8_t* vs8 = reinterpret_cast<const uint8_t*>(vscale);
+#pragma unroll
+            for (int j = 0; j < MI4; ++j) {
+                const int i = w + kSweepWaves * j;
+                if (i >= NI4) break;  // wave-uniform
+                const int64_t ph = (int64_t(pg4[j] ? phys1 : phys0) * a.Hkv + kvh);
+                const uint8_t* src = arr4[j] == 0 ? a.k + ph * ST_PAGE
+                                   : arr4[j] == 1 ? a.v + ph * ST_PAGE
+                                   : arr4[j] == 2 ? ks8 + ph * (D / 2) : vs8 + ph * (D / 2);
+                const uint32_t lds = smem_base + uint32_t((c % NS) * ST_STAGE + 1024 * i);
+                if (has4[j]) dma16(src + off4[j], __builtin_amdgcn_readfirstlane(lds));
+            }
+            return;
+        }
         if (issues_kv) {
             int n = 2 * c + region_pg;
             if (n >= npages) n = 2 * c;  // absent second page: reload the first, masked later
@@ -374,6 +480,33 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
 
+    // MXFP4: decode the V^T codes of ring chunk c once for the whole workgroup
+    // into bf16 staging buffer (c & 1), in the bf16 ring's V^T layout (16-row
+    // groups, tokens 8..15 of a row 256 bytes after tokens 0..7).  Item (page,
+    // token half h, row d): 8 codes (one word) and the 8 tokens' scales of the
+    // row's block (one 8-byte read, V scales being block-major).  The two
+    // tokens of a byte have their own scales, so each byte is converted twice
+    // and the halves are kept: the V scale is exact in the staged values.
+    // Straight-line (4D / 512 items per thread), so that a row-tile wave can
+    // run it between its score MFMAs and the softmax and the two overlap.
+    static_assert(!FP4 || (4 * D) % kSweepThreads == 0, "whole decode items per thread");
+    auto decode_v4 = [&](int c) {
+        const uint8_t* src = smem + (c % NS) * ST_STAGE;
+        uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
+#pragma unroll
+        for (int i = 0; i < (4 * D) / kSweepThreads; ++i) {
+            const int it = tid + kSweepThreads * i;
+            const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+            const uint32_t w4 = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
+            const uint2 sb = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) + (d >> 5) * 16 + 8 * h);
+            const u32x4 o = {e2m1x2_two_scales<0>(w4, sb.x & 0xFFu, (sb.x >> 8) & 0xFFu),
+                             e2m1x2_two_scales<1>(w4, (sb.x >> 16) & 0xFFu, sb.x >> 24),
+                             e2m1x2_two_scales<2>(w4, sb.y & 0xFFu, (sb.y >> 8) & 0xFFu),
+                             e2m1x2_two_scales<3>(w4, (sb.y >> 16) & 0xFFu, sb.y >> 24)};
+            *reinterpret_cast<u32x4*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) = o;
+        }
+    };
+
     // ---- prologue: start the ring, then load Q while the first chunks are in
     // flight (one memory round trip for both), and wait for all of it here so
     // that no compiler-visible vector load is pending inside the loop
@@ -387,11 +520,73 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+            // bf16 k-step ks, lane group g: elements 32ks + 8g ..  MXFP4: qf[4k
+            // + 2r + h] holds elements ((D/4)(2r + (g>>1)) + 32k + 16(g&1) + 8h
+            // ..), the 16-element runs r = 0, 1 of 128-deep k-step k that the
+            // scaled MFMA's B operand gives lane group g
+            const int k4 = ks >> 2, r4 = (ks >> 1) & 1, h4 = ks & 1;
+            const int d0 = FP4 ? (D / 4) * (2 * r4 + (g >> 1)) + 32 * k4 + 16 * (g & 1) + 8 * h4
+                               : 32 * ks + 8 * g;
+            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
             qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // ---- MXFP4 scores run on the scaled MFMA (E2M1 K times e4m3 Q, E8M0
+    // scales per 32 elements of the contraction).  Q is split once per unit:
+    // q = hi 2^X + lo 2^(X-4) per 32-element block, hi and lo e4m3 and X =
+    // floor(log2 amax) - 7, so |q| / 2^X < 256 and the residual fits lo.  A
+    // block's 32 elements are the runs of two lane groups (g, g ^ 1); the scale
+    // that lane group g hands the MFMA is that of contraction block g, whose
+    // elements are run g >> 1 of lane groups 2(g & 1) and 2(g & 1) + 1.
+    constexpr int KS4 = D / 128;  // 128-deep k-steps of the scaled MFMA
+    i32x8 qhi[FP4 ? KS4 : 1], qlo[FP4 ? KS4 : 1];
+    uint32_t shi = 0, slo = 0;    // byte k: E8M0 scale this lane supplies for k-step k
+    if constexpr (FP4) {
+#pragma unroll
+        for (int k = 0; k < KS4; ++k) {
+            int X[2];
+#pragma unroll
+            for (int r4 = 0; r4 < 2; ++r4) {
+                float m = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(float(qf[4 * k + 2 * r4 + h][e])));
+                m = fmaxf(m, __shfl_xor(m, 16));
+                int ex = 0;
+                (void)frexpf(m, &ex);
+                X[r4] = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
+            }
+#pragma unroll
+            for (int r4 = 0; r4 < 2; ++r4)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; e += 4) {
+                        float x[4], y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[i] = float(qf[4 * k + 2 * r4 + h][e + i]);
+                        int hw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[0], -X[r4]), ldexpf(x[1], -X[r4]), 0, false);
+                        hw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[2], -X[r4]), ldexpf(x[3], -X[r4]), hw, true);
+                        y[0] = x[0] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 0), X[r4]);
+                        y[1] = x[1] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 1), X[r4]);
+                        y[2] = x[2] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 2), X[r4]);
+                        y[3] = x[3] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 3), X[r4]);
+                        int lw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(y[0], 4 - X[r4]), ldexpf(y[1], 4 - X[r4]), 0, false);
+                        lw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(y[2], 4 - X[r4]), ldexpf(y[3], 4 - X[r4]), lw, true);
+                        const int wi = 4 * r4 + 2 * h + (e >> 2);  // byte 16 r4 + 8 h + e of the operand
+                        qhi[k][wi] = hw;
+                        qlo[k][wi] = lw;
+                    }
+            const int src = 16 * 2 * (g & 1) + ln;
+            const int x0 = __shfl(X[0], src), x1 = __shfl(X[1], src);
+            const int xs = (g >> 1) ? x1 : x0;
+            shi |= uint32_t(xs + 127) << (8 * k);
+            slo |= uint32_t(xs - 4 + 127) << (8 * k);
+        }
+    }
 
     // ---- LDS read addressing (per lane, constant over chunks), bf16 layout
     // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
@@ -411,6 +606,28 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     }
     const uint32_t vaddr = uint32_t(2 * BF_PAGE + (g >> 1) * BF_PAGE + (g & 1) * 256 + ln * 16);
+    // MXFP4 K addressing (stage layout at fp4_piece): tile t row tau = 8 rg +
+    // 4t + (ln & 3) with rg = ln >> 2; logical 16-byte half h of the lane's
+    // D/8 bytes.  K scales: the lane's first block of that row.
+    uint32_t k4addr[2][2] = {}, k4sc[2] = {};
+    if constexpr (FP4) {
+        const int rg = ln >> 2, pg = g >> 1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int pos = (4 * t + (ln & 3)) ^ (4 * (rg & 1));
+            const int tau = 8 * rg + 4 * t + (ln & 3);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                k4addr[t][h] = D == 256
+                    ? uint32_t((rg * 4 + g) * D + pos * 32 + 16 * (h ^ (rg >> 1)))
+                    : uint32_t((rg * 4 + (g ^ (rg >> 1))) * D + pos * 16);
+            k4sc[t] = uint32_t(32 * D + (tau >> 4) * (D / 2) + (tau & 15) * (D / 32) + g * (KS / 4));
+        }
+        (void)pg;
+    }
+    // where this lane's V^T operand rows start: the bf16 ring stage, or the
+    // MXFP4 V staging buffer (the two V pages only)
+    const uint32_t va = FP4 ? vaddr - 2 * BF_PAGE : vaddr;
 
     f32x4 acc[DT];
 #pragma unroll
@@ -419,27 +636,60 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 
     auto process = [&](int c, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        const uint8_t* st = FP8 ? smem + RING + (c & 1) * BF_STAGE : smem + (c % NS) * BF_STAGE;
+        const uint8_t* st = FP8 ? smem + RING + (c & 1) * BF_STAGE : smem + (c % NS) * ST_STAGE;
+        const uint8_t* vst = FP4 ? smem + RING + (c & 1) * (2 * BF_PAGE) : st;  // V^T operand rows
         const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
         // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
-        // independent accumulation chains for MFMA pipelining.  All 16 K operand
+        // independent accumulation chains for MFMA pipelining.  All K operand
         // reads are issued before the first MFMA so LDS latency overlaps.
-        bf16x8_t kop[KS][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                kop[ks][t] =
-                    *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
         f32x4 s4[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) s4[t][0] = s4[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP4) {
+            // per tile row: the lane's D/8 code bytes (16 per 128-deep k-step:
+            // one E2M1 block) and their E8M0 scales (byte k for k-step k); the
+            // hi and lo parts of Q accumulate in separate chains
+            u32x4 kw[2][2];
+            uint32_t ksb[2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int t = 0; t < 2; ++t) {
+                kw[t][0] = *reinterpret_cast<const u32x4*>(st + k4addr[t][0]);
+                if constexpr (D == 256) kw[t][1] = *reinterpret_cast<const u32x4*>(st + k4addr[t][1]);
+                ksb[t] = D == 256 ? uint32_t(*reinterpret_cast<const uint16_t*>(st + k4sc[t]))
+                                  : uint32_t(st[k4sc[t]]);
+            }
+            auto kstep = [&](auto kc) {
+                constexpr int k = decltype(kc)::value;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks][t], qf[ks],
-                                                                          s4[t][ks & 1], 0, 0, 0);
+                for (int t = 0; t < 2; ++t) {
+                    const u32x4 w = kw[t][k];
+                    const i32x8 ka = {int(w[0]), int(w[1]), int(w[2]), int(w[3]), 0, 0, 0, 0};
+                    s4[t][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka, qhi[k], s4[t][0], 4, 0, k, int(ksb[t]), k, int(shi));
+                    s4[t][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka, qlo[k], s4[t][1], 4, 0, k, int(ksb[t]), k, int(slo));
+                }
+            };
+            kstep(std::integral_constant<int, 0>{});
+            if constexpr (KS4 > 1) kstep(std::integral_constant<int, 1>{});
+            // this thread's share of the next chunk's V decode, under the MFMAs
+            // (past the last chunk it decodes a stale slot that nobody reads)
+            decode_v4(c + 1);
+        } else {
+            bf16x8_t kop[KS][2];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    kop[ks][t] =
+                        *reinterpret_cast<const bf16x8_t*>(st + kaddr[t][ks & 3] + 256 * (ks >> 2));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    s4[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks][t], qf[ks],
+                                                                              s4[t][ks & 1], 0, 0, 0);
+        }
         // V^T operands do not depend on the softmax: at D = 256 issue their reads
         // now so their latency hides behind it (smaller heads and the fp8 path,
         // which also holds the scales, keep the registers)
@@ -448,7 +698,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         if constexpr (VPRE) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                vraw[dt] = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+                vraw[dt] = *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
             __builtin_amdgcn_sched_barrier(0);
         }
         float ksc[8], vsc[8];
@@ -505,7 +755,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         for (int dt = 0; dt < DT; ++dt) {
             u32x4 raw;
             if constexpr (VPRE) raw = vraw[dt];
-            else raw = *reinterpret_cast<const u32x4*>(st + vaddr + 512 * dt);
+            else raw = *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
             if constexpr (TAIL) {
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2)
@@ -519,13 +769,19 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- ring step for iteration c.
     // bf16: wait for chunk c, then refill the slot freed by chunk c-1 with
     //       chunk c+NS-1.
+    // MXFP4: as bf16, but wait for chunk c+1, whose V every thread decodes
+    //       into staging during iteration c (row-tile waves inside process,
+    //       between the score MFMAs and the softmax); chunk c's K is read from
+    //       its ring slot.
     // fp8:  chunk c was decoded (out of its ring slot) during iteration c-1;
     //       wait for chunk c+1 (to decode it now), then refill chunk c's slot
     //       with chunk c+NS.  Either way NS-2 chunks stay in flight past the
     //       one waited for.
     auto ring_step = [&](int c) {
-        const int need = FP8 ? c + 1 : c;
-        if (need < nchunks) wait_vmcnt_dyn(min(NS - 2, nchunks - 1 - need) * nload);
+        const int need = FP8 || FP4 ? c + 1 : c;
+        // chunks younger than `need` left in flight: fp8 has issued up to
+        // c+NS-1 by now, the others up to c+NS-2
+        if (need < nchunks) wait_vmcnt_dyn(min(FP4 ? NS - 3 : NS - 2, nchunks - 1 - need) * nload);
         __syncthreads();
         const int cn = c + AHEAD;
         if (cn < nchunks) {
@@ -537,12 +793,15 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             }
             issue_chunk(cn);
         }
-        if (FP8 && c + 1 < nchunks) decode_chunk(c + 1);
+        if constexpr (FP8) {
+            if (c + 1 < nchunks) decode_chunk(c + 1);
+        }
     };
-    if (FP8 && nchunks > 0) {  // decode chunk 0 ahead of the loop
+    if ((FP8 || FP4) && nchunks > 0) {  // decode chunk 0 ahead of the loop
         wait_vmcnt_dyn(min(AHEAD - 1, nchunks - 1) * nload);
         __syncthreads();
-        decode_chunk(0);
+        if constexpr (FP8) decode_chunk(0);
+        else if constexpr (FP4) decode_v4(0);
     }
     // Chunks that need no mask come first: the masked ones (keys past the
     // unit's end, or past some row's causal limit) are always a suffix.
@@ -557,14 +816,17 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     for (; c < c_head; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::true_type{});
+        else if constexpr (FP4) decode_v4(c + 1);
     }
     for (; c < c_tail; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::false_type{});
+        else if constexpr (FP4) decode_v4(c + 1);
     }
     for (; c < nchunks; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::true_type{});
+        else if constexpr (FP4) decode_v4(c + 1);
     }
 
     // ---- epilogue: normalise, write the final output or the split partial
@@ -853,9 +1115,15 @@ int launch(K kernel, int64_t blocks, int threads, const Params& a, hipStream_t s
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* ev0, void* ev1) {
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        return launch(sweep_kernel<D, 5, true>, pl->U, kSweepThreads, a, st, ev0, ev1,
-                      "sweep kernel launch");
-    return launch(sweep_kernel<D, 4, false>, pl->U, kSweepThreads, a, st, ev0, ev1,
+        return launch(sweep_kernel<D, 5, SMALLW_KV_FP8_E4M3>, pl->U, kSweepThreads, a, st, ev0,
+                      ev1, "sweep kernel launch");
+    if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
+        if constexpr (D == 64) return SMALLW_EUNSUPPORTED;  // the planner rejects it first
+        else
+            return launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4>, pl->U, kSweepThreads, a, st, ev0,
+                          ev1, "sweep kernel launch");
+    }
+    return launch(sweep_kernel<D, 4, SMALLW_KV_BF16>, pl->U, kSweepThreads, a, st, ev0, ev1,
                   "sweep kernel launch");
 }
 
@@ -901,15 +1169,15 @@ int small_w_attention_plan(const smallw_problem* problem, const int32_t* seq_len
 }
 
 int small_w_attention_run_events(const smallw_plan* pl, const void* q, const void* k_pool,
-                                 const void* v_pool, const float* k_scale,
-                                 const float* v_scale, const int32_t* block_table,
+                                 const void* v_pool, const void* k_scale,
+                                 const void* v_scale, const int32_t* block_table,
                                  const int32_t* seq_lens, void* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* ev_start, void* ev_sweep_done, void* ev_end) {
     if (!pl || !q || !k_pool || !v_pool || !block_table || !seq_lens || !out || !lse)
         return SMALLW_EINVAL;
-    const bool fp8 = pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3;
-    if (fp8 && (!k_scale || !v_scale)) return SMALLW_EINVAL;
+    const bool scaled = pl->prob.kv_dtype != SMALLW_KV_BF16;
+    if (scaled && (!k_scale || !v_scale)) return SMALLW_EINVAL;
     if (pl->ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl->ws_bytes) return SMALLW_EWORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SMALLW_EWORKSPACE;
@@ -920,8 +1188,8 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint8_t*>(k_pool);
     a.v = static_cast<const uint8_t*>(v_pool);
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
+    a.k_scale = static_cast<const float*>(k_scale);  // MXFP4: E8M0 bytes, read as such
+    a.v_scale = static_cast<const float*>(v_scale);
     a.bt = block_table;
     a.seq = seq_lens;
     a.out = static_cast<uint16_t*>(out);
@@ -951,7 +1219,7 @@ int small_w_attention_run_events(const smallw_plan* pl, const void* q, const voi
 }
 
 int small_w_attention_run(const smallw_plan* pl, const void* q, const void* k_pool,
-                          const void* v_pool, const float* k_scale, const float* v_scale,
+                          const void* v_pool, const void* k_scale, const void* v_scale,
                           const int32_t* block_table, const int32_t* seq_lens, void* out,
                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     return small_w_attention_run_events(pl, q, k_pool, v_pool, k_scale, v_scale, block_table,

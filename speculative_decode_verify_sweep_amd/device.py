@@ -3,7 +3,7 @@
 Copies host arrays in the library's documented layouts into device tensors,
 builds a plan and enqueues calls.  PyTorch provides memory and the stream; all
 attention arithmetic happens in libsmallw.so.  Inputs are duck-typed: any
-object with the attributes P, W, Hq, Hkv, D, causal, kv ("bf16"/"fp8"),
+object with the attributes P, W, Hq, Hkv, D, causal, kv ("bf16"/"fp8"/"mxfp4"),
 scale, num_pages, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens.
 """
 from __future__ import annotations
@@ -13,10 +13,12 @@ import torch
 
 from . import binding as B
 
+KV_DTYPES = {"bf16": B.SMALLW_KV_BF16, "fp8": B.SMALLW_KV_FP8_E4M3, "mxfp4": B.SMALLW_KV_MXFP4}
+
 
 def upload(w, device: str = "cuda:0") -> dict:
     dev = torch.device(device)
-    fp8 = w.kv == "fp8"
+    raw = w.kv != "bf16"      # byte pools (e4m3 codes, MXFP4 nibbles) and their scales
 
     def t(a, dtype=None):
         x = torch.from_numpy(np.ascontiguousarray(a))
@@ -26,10 +28,10 @@ def upload(w, device: str = "cuda:0") -> dict:
 
     d = {
         "q": t(w.q.view(np.int16), torch.bfloat16),
-        "k_pool": t(w.k_pool) if fp8 else t(w.k_pool.view(np.int16), torch.bfloat16),
-        "v_pool": t(w.v_pool) if fp8 else t(w.v_pool.view(np.int16), torch.bfloat16),
-        "k_scale": t(w.k_scale) if fp8 else None,
-        "v_scale": t(w.v_scale) if fp8 else None,
+        "k_pool": t(w.k_pool) if raw else t(w.k_pool.view(np.int16), torch.bfloat16),
+        "v_pool": t(w.v_pool) if raw else t(w.v_pool.view(np.int16), torch.bfloat16),
+        "k_scale": t(w.k_scale) if raw else None,
+        "v_scale": t(w.v_scale) if raw else None,
         "block_table": t(w.block_table),
         "seq_lens": t(w.seq_lens),
     }
@@ -42,7 +44,7 @@ def plan_for(w, *, num_cus: int = 0, force_splits: int = 0, split_pages: int = 0
     pr = B.make_problem(num_reqs=w.P, window=w.W, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
                         head_dim=w.D, num_pages=w.num_pages,
                         max_pages_per_req=w.block_table.shape[1], causal=w.causal,
-                        kv_dtype=B.SMALLW_KV_FP8_E4M3 if w.kv == "fp8" else B.SMALLW_KV_BF16,
+                        kv_dtype=KV_DTYPES[w.kv],
                         scale=w.scale, num_cus=num_cus, force_splits=force_splits,
                         split_pages=split_pages, window_left=getattr(w, "window_left", 0))
     return B.small_w_attention_plan(pr, w.seq_lens)

@@ -109,7 +109,9 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         if W * G > 128:
             W = 128 // G
         D = int(rng.choice([64, 128, 256]))
-        fp8 = int(rng.integers(0, 2))
+        fp8 = int(rng.integers(0, 3))       # storage format code: bf16, e4m3, MXFP4
+        if fp8 == 2 and D == 64:
+            fp8 = 0                          # MXFP4 serves D = 128 and 256
         causal = int(rng.integers(0, 2))
         force = int(rng.choice([0, 0, 0, 1, 2, 5, 64]))
         spg = int(rng.choice([0, 0, 0, 1, 7, 64])) if force == 0 else 0
@@ -126,7 +128,7 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
                             window_left=win)
         plan = sw.small_w_attention_plan(pr, seq)
         mine = sw.small_w_attention_plan_export(plan)
-        pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=bool(fp8), seq_lens=seq, num_cus=cus,
+        pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=fp8 == 1, seq_lens=seq, num_cus=cus,
                          force_splits=force, split_pages=spg, W=W, causal=bool(causal),
                          window_left=win)
         np.testing.assert_array_equal(mine, oracle.plan_export(pl, R=W * G))
@@ -178,12 +180,21 @@ def test_kv_append_rejects_null_pointers_before_any_launch():
     assert lib.small_w_kv_append(fp8.handle, *args[1:]) == B.SMALLW_EINVAL   # scales missing
 
 
-def test_fp8_run_requires_scales():
-    plan = sw.small_w_attention_plan(base_problem(kv_dtype=1), [260])
+@pytest.mark.parametrize("kv", [B.SMALLW_KV_FP8_E4M3, B.SMALLW_KV_MXFP4])
+def test_scaled_formats_require_scales(kv):
+    plan = sw.small_w_attention_plan(base_problem(kv_dtype=kv, head_dim=128), [260])
     fake = 1 << 40
     rc = B.lib().small_w_attention_run(plan.handle, fake, fake, fake, None, None, fake, fake,
                                        fake, fake, None, 0, None)
     assert rc == B.SMALLW_EINVAL
+
+
+def test_mxfp4_needs_head_dim_128_or_256():
+    with pytest.raises(B.SmallwError) as e:
+        sw.small_w_attention_plan(base_problem(kv_dtype=B.SMALLW_KV_MXFP4, head_dim=64), [260])
+    assert e.value.code == B.SMALLW_EUNSUPPORTED
+    for D in (128, 256):
+        sw.small_w_attention_plan(base_problem(kv_dtype=B.SMALLW_KV_MXFP4, head_dim=D), [260])
 
 
 def test_strerror_names_every_code():

@@ -190,7 +190,7 @@ def test_oracle_append_mxfp4_writes_only_the_window_nibbles():
                 np.testing.assert_array_equal(kcodes, kc)
                 np.testing.assert_array_equal(vcodes, vc)
                 np.testing.assert_array_equal(ks[pg, h, sl], ksc)
-                np.testing.assert_array_equal(vs[pg, h, sl], vsc)
+                np.testing.assert_array_equal(vs[pg, h, :, sl], vsc)
                 # the stored values are the quantised row
                 deq = table[kcodes] * np.repeat(2.0 ** (ksc.astype(int) - 127), 32)
                 assert np.abs(deq - kx).max() <= np.abs(kx).max() / 4 + 1e-30
@@ -198,7 +198,8 @@ def test_oracle_append_mxfp4_writes_only_the_window_nibbles():
     # other token's nibble of every value byte
     np.testing.assert_array_equal(kp[~touched], w.k_pool[~touched])
     np.testing.assert_array_equal(ks[~touched], w.k_scale[~touched])
-    np.testing.assert_array_equal(vs[~touched], w.v_scale[~touched])
+    np.testing.assert_array_equal(vs.transpose(0, 1, 3, 2)[~touched],
+                                  w.v_scale.transpose(0, 1, 3, 2)[~touched])
     for sl in range(16):
         keep = ~touched[:, :, sl]                                       # [pages][Hkv]
         old = (w.v_pool[:, :, :, sl // 2] >> (4 * (sl % 2))) & 15

@@ -82,7 +82,7 @@ def dense_mxfp4(w, phys, slot):
         return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e8m0fnu).double().numpy()
 
     ks = np.repeat(e8m0(w.k_scale[phys, :, slot, :]), 32, axis=-1)   # [L][Hkv][D]
-    vs = np.repeat(e8m0(w.v_scale[phys, :, slot, :]), 32, axis=-1)
+    vs = np.repeat(e8m0(w.v_scale[phys, :, :, slot]), 32, axis=-1)   # block-major V scales
     return table[kn] * ks, table[vn] * vs
 
 

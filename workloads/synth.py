@@ -9,8 +9,8 @@ Storage layout (the library's documented layout):
   MXFP4 (kv = "mxfp4"): uint8, two E2M1 codes per byte, the even element in the
   low nibble; k_pool [num_pages][Hkv][16][D/2] (byte i of token t: elements 2i,
   2i+1), v_pool [num_pages][Hkv][D][8] (byte i of row d: tokens 2i, 2i+1),
-  k_scale / v_scale E8M0 bytes [num_pages][Hkv][16][D/32], one per 32-element
-  block of a token's row
+  E8M0 bytes, one per 32-element block of a token's row: k_scale
+  [num_pages][Hkv][16][D/32], v_scale block-major [num_pages][Hkv][D/32][16]
   block_table int32 [P][max_pages_per_req]   (-1 past a request's last page)
   seq_lens    int32 [P]   (context + window: the window's own K/V rows are
               already in the pool, so a verify row i sits at position L - W + i)
@@ -160,7 +160,7 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
         k_pool = np.full((pool_pages, Hkv, PAGE, D // 2), 0x77, dtype=np.uint8)
         v_pool = np.full((pool_pages, Hkv, D, PAGE // 2), 0x77, dtype=np.uint8)
         k_scale = np.full((pool_pages, Hkv, PAGE, D // 32), 0xFF, dtype=np.uint8)
-        v_scale = np.full((pool_pages, Hkv, PAGE, D // 32), 0xFF, dtype=np.uint8)
+        v_scale = np.full((pool_pages, Hkv, D // 32, PAGE), 0xFF, dtype=np.uint8)
     elif fp8:
         k_pool = np.full((pool_pages, Hkv, PAGE, D), 0x7F, dtype=np.uint8)
         v_pool = np.full((pool_pages, Hkv, D, PAGE), 0x7F, dtype=np.uint8)
@@ -195,7 +195,7 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
                 phys = bt[p, n]
                 k_pool[phys, :, :t1 - t0, :] = kc[:, t0:t1, 0::2] | (kc[:, t0:t1, 1::2] << 4)
                 k_scale[phys, :, :t1 - t0, :] = ksc[:, t0:t1]
-                v_scale[phys, :, :t1 - t0, :] = vsc[:, t0:t1]
+                v_scale[phys, :, :, :t1 - t0] = vsc[:, t0:t1].transpose(0, 2, 1)
                 for t in range(t0, t1):
                     slot = t - t0
                     sh = 4 * (slot & 1)
