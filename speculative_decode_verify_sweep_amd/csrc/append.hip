@@ -11,7 +11,14 @@
 // slot of the transposed (d-major) value page.  For e4m3 pools each (token,
 // KV head) row gets scale = amax|x| / 448 (1 when the row is all zero) and
 // codes = round-to-nearest-even of x / scale on the OCP e4m3fn grid, all in
-// fp32 (IEEE division), so the codes are exactly reproducible.
+// fp32 (IEEE division), so the codes are exactly reproducible.  For MXFP4
+// pools (OCP Microscaling Formats v1.0 conversion, E2M1 elements and an E8M0
+// scale per 32 elements of a row) each block gets X = floor(log2 amax) - 2,
+// clamped to [-127, 127] (an all-zero block -127), stored as X + 127, and each
+// element the E2M1 code nearest x / 2^X, ties to the even code, past 6
+// saturating to 6, with the sign bit of x.  Two tokens share each byte of the
+// transposed value page, so V nibbles are written with word atomics (clear,
+// then set) and waves writing the two halves of a byte cannot race.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -46,8 +53,31 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 // One wave per (p, i, kvh); lane l owns elements [E*l, E*l + E) of the row.
-template <int D, bool FP8>
+// E2M1 code of y (|y| < 8 after the block scaling): count the rounding
+// boundaries passed.  A tie between codes c and c+1 goes to the even one, so
+// the boundary above an even code is strict and the one above an odd code is
+// not.  The sign bit is the sign of y (so of x), also when y rounds to 0.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+    const float v = fabsf(y);
+    const uint32_t c = uint32_t(v > 0.25f) + uint32_t(v >= 0.75f) + uint32_t(v > 1.25f) +
+                       uint32_t(v >= 1.75f) + uint32_t(v > 2.5f) + uint32_t(v >= 3.5f) +
+                       uint32_t(v > 5.0f);
+    return c | ((__builtin_bit_cast(uint32_t, y) >> 31) << 3);
+}
+
+// Shared exponent X of an MX block with largest magnitude m: floor(log2 m) - 2
+// (2 is E2M1's largest exponent), clamped to E8M0's range; -127 for m = 0.
+__device__ __forceinline__ int mx_exponent(float m) {
+    if (!(m > 0.f)) return -127;
+    int e = 0;
+    (void)frexpf(m, &e);  // m = f 2^e, f in [0.5, 1): floor(log2 m) = e - 1
+    return min(max(e - 3, -127), 127);
+}
+
+template <int D, int KV>
 __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
+    constexpr bool FP8 = KV == SMALLW_KV_FP8_E4M3;
+    constexpr bool FP4 = KV == SMALLW_KV_MXFP4;
     constexpr int E = D / 64;
     const int b = blockIdx.x;
     const int kvh = b % a.Hkv;
@@ -70,7 +100,46 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
         kx[e] = bf16_to_f32(a.k_new[row + e]);
         vx[e] = bf16_to_f32(a.v_new[row + e]);
     }
-    if constexpr (!FP8) {
+    if constexpr (FP4) {
+        // lane l holds elements E l .. E l + E - 1; a 32-element block is 32/E lanes
+        constexpr int BL = 32 / E;
+        float km = 0.f, vm = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            km = fmaxf(km, fabsf(kx[e]));
+            vm = fmaxf(vm, fabsf(vx[e]));
+        }
+#pragma unroll
+        for (int off = 1; off < BL; off <<= 1) {
+            km = fmaxf(km, __shfl_xor(km, off));
+            vm = fmaxf(vm, __shfl_xor(vm, off));
+        }
+        const int kX = mx_exponent(km), vX = mx_exponent(vm);
+        uint32_t kc = 0;
+        uint8_t* kp = a.k_pool + (ph * 16 + slot) * (D / 2) + (E * l) / 2;
+#pragma unroll
+        for (int e = 0; e < E; ++e) kc |= e2m1_code(ldexpf(kx[e], -kX)) << (4 * e);
+#pragma unroll
+        for (int e = 0; e < E / 2; ++e) kp[e] = uint8_t(kc >> (8 * e));
+        // V^T byte (d, slot / 2), nibble slot & 1; as a word: word 2d + slot / 8,
+        // bits 8 ((slot / 2) & 3) + 4 (slot & 1)
+        uint32_t* vw = reinterpret_cast<uint32_t*>(a.v_pool + ph * D * 8);
+        const int sh = 8 * ((slot >> 1) & 3) + 4 * (slot & 1);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int d = E * l + e;
+            uint32_t* w = vw + 2 * d + (slot >> 3);
+            atomicAnd(w, ~(0xFu << sh));
+            atomicOr(w, e2m1_code(ldexpf(vx[e], -vX)) << sh);
+        }
+        if (l % BL == 0) {
+            const int blk = (E * l) / 32;
+            uint8_t* ks8 = reinterpret_cast<uint8_t*>(a.k_scale);
+            uint8_t* vs8 = reinterpret_cast<uint8_t*>(a.v_scale);
+            ks8[(ph * 16 + slot) * (D / 32) + blk] = uint8_t(kX + 127);
+            vs8[(ph * (D / 32) + blk) * 16 + slot] = uint8_t(vX + 127);  // block-major
+        }
+    } else if constexpr (!FP8) {
         uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pool) + (ph * 16 + slot) * D + E * l;
         uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool) + ph * D * 16 + slot;
 #pragma unroll
@@ -112,9 +181,12 @@ template <int D>
 hipError_t launch_append(const smallw_plan* pl, const AppendParams& a, hipStream_t st) {
     const unsigned blocks = unsigned(int64_t(a.P) * a.W * a.Hkv);
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        hipLaunchKernelGGL((append_kernel<D, true>), dim3(blocks), dim3(64), 0, st, a);
-    else
-        hipLaunchKernelGGL((append_kernel<D, false>), dim3(blocks), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((append_kernel<D, SMALLW_KV_FP8_E4M3>), dim3(blocks), dim3(64), 0, st, a);
+    else if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
+        if constexpr (D != 64)  // the planner rejects MXFP4 at D = 64
+            hipLaunchKernelGGL((append_kernel<D, SMALLW_KV_MXFP4>), dim3(blocks), dim3(64), 0, st, a);
+    } else
+        hipLaunchKernelGGL((append_kernel<D, SMALLW_KV_BF16>), dim3(blocks), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 
@@ -128,7 +200,6 @@ extern "C" int small_w_kv_append(const smallw_plan* pl, const void* k_new, const
         return SMALLW_EINVAL;
     const bool scaled = pl->prob.kv_dtype != SMALLW_KV_BF16;
     if (scaled && (!k_scale || !v_scale)) return SMALLW_EINVAL;
-    if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) return SMALLW_EUNSUPPORTED;
     AppendParams a;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);

@@ -224,15 +224,22 @@ def _append_case(kv, D=128, W=16, ctx=(700, 45, 0), seed=72, Hq=8):
     kn = to_bf16_bits(rng.normal(0, 1, size=shape).astype(np.float32))   # same draw as the
     vn = to_bf16_bits(rng.normal(0, 1, size=shape).astype(np.float32))   # workloads' K and V
     kn[0, 3, 1] = 0                              # an all-zero row: scale 1
+    if kv == "mxfp4":
+        # blocks the MX exponent must clamp: bf16 denormals and the smallest normals
+        kn[0, 4, 2, :32] = np.arange(1, 33, dtype=np.uint16)                  # 2^-133 ..
+        vn[0, 4, 2, 32:64] = (0x0080 + np.arange(32)).astype(np.uint16)       # 2^-126 ..
+        vn[0, 5, 3, :] = 0x8000                                                # all -0.0
     return w, kn, vn
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_append_kernel_matches_oracle_bitwise(kv, D):
     from speculative_decode_verify_sweep_amd import device as dv
     import speculative_decode_verify_sweep_amd as sw
+    if kv == "mxfp4" and D == 64:
+        pytest.skip("MXFP4 pools serve head_dim 128 and 256")
     w, kn, vn = _append_case(kv, D=D)
     print(f"[case] append {kv} D={D}", flush=True)
     d = dv.upload(w)
@@ -242,18 +249,68 @@ def test_append_kernel_matches_oracle_bitwise(kv, D):
     sw.small_w_kv_append(plan, kt, vt, d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
                          d["block_table"], d["seq_lens"])
     torch.cuda.synchronize()
-    fp8 = kv == "fp8"
+    scaled = kv != "bf16"
     kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=D, kv=kv, k_new_bits=kn,
                                       v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
-                                      k_scale=w.k_scale if fp8 else None,
-                                      v_scale=w.v_scale if fp8 else None,
+                                      k_scale=w.k_scale if scaled else None,
+                                      v_scale=w.v_scale if scaled else None,
                                       block_table=w.block_table, seq_lens=w.seq_lens,
                                       num_pages=w.num_pages)
     np.testing.assert_array_equal(host_bits(d["k_pool"]), kp)
     np.testing.assert_array_equal(host_bits(d["v_pool"]), vp)
-    if fp8:
+    if scaled:
         np.testing.assert_array_equal(d["k_scale"].cpu().numpy(), ks)
         np.testing.assert_array_equal(d["v_scale"].cpu().numpy(), vs)
+
+
+@pytest.mark.gpu
+def test_append_mxfp4_rounds_every_tie_to_even_and_saturates():
+    """Blocks holding 4.0 have X = 0, so the codes are the E2M1 rounding of the
+    bf16 inputs themselves: every value, every midpoint and their bf16
+    neighbours, and values past 6 up to just under 8 (saturation)."""
+    from speculative_decode_verify_sweep_amd import device as dv
+    import speculative_decode_verify_sweep_amd as sw
+    grid = np.array(E2M1, np.float32)
+    mids = (grid[:-1] + grid[1:]) / 2
+    cand = np.concatenate([grid, mids, [6.5, 7.0, 7.5, 7.96875]]).astype(np.float32)
+    bits = to_bf16_bits(np.concatenate([cand, -cand]))
+    near = np.concatenate([bits, bits + 1, bits - 1]).astype(np.uint16)
+    vals = (near.astype(np.uint32) << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) < 8)]
+    per_block = 31
+    nblk = -(-vals.size // per_block)
+    D, W = 256, 16
+    blocks = np.zeros((nblk, 32), np.float32)
+    blocks[:, 0] = 4.0                                           # amax in [4, 8): X = 0
+    flat = np.zeros(nblk * per_block, np.float32)
+    flat[:vals.size] = vals
+    blocks[:, 1:] = flat.reshape(nblk, per_block)
+    rows = -(-nblk // (D // 32))
+    assert rows <= W * 4
+    full = np.zeros((W * 4 * (D // 32), 32), np.float32)
+    full[:, 0] = 4.0
+    full[:nblk] = blocks
+    full = full.reshape(1, W, 4, D)
+    w = make_workload(None, P=1, Hq=4, Hkv=4, D=D, ctx=(48,), W=W, causal=True, kv="mxfp4",
+                      placement="in_order", pool_pages=5, seed=76)
+    kn = to_bf16_bits(full)
+    d = dv.upload(w)
+    plan = dv.plan_for(w)
+    kt = torch.from_numpy(kn.view(np.int16)).cuda()
+    print("[case] append MXFP4 ties", flush=True)
+    sw.small_w_kv_append(plan, kt, kt, d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
+                         d["block_table"], d["seq_lens"])
+    torch.cuda.synchronize()
+    kp, vp, ks, vs = oracle.kv_append(P=1, W=W, Hkv=4, D=D, kv="mxfp4", k_new_bits=kn,
+                                      v_new_bits=kn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                      k_scale=w.k_scale, v_scale=w.v_scale,
+                                      block_table=w.block_table, seq_lens=w.seq_lens,
+                                      num_pages=w.num_pages)
+    assert np.all(ks[3] == 127)                                  # X = 0 everywhere
+    np.testing.assert_array_equal(host_bits(d["k_pool"]), kp)
+    np.testing.assert_array_equal(host_bits(d["v_pool"]), vp)
+    np.testing.assert_array_equal(d["k_scale"].cpu().numpy(), ks)
+    np.testing.assert_array_equal(d["v_scale"].cpu().numpy(), vs)
 
 
 @pytest.mark.gpu
@@ -302,14 +359,14 @@ def test_append_kernel_rounds_every_tie_to_even():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_append_then_verify_matches_oracle(kv):
     """The step pair a verify does: append the window's K/V, then attend."""
     from speculative_decode_verify_sweep_amd import device as dv
     import speculative_decode_verify_sweep_amd as sw
-    from test_gpu_parity import check
+    from test_gpu_parity import check, few_key_tolerance
     w, kn, vn = _append_case(kv, D=256, W=16, ctx=(3000, 200, 0), seed=74, Hq=24)
-    fp8 = kv == "fp8"
+    scaled = kv != "bf16"
     d = dv.upload(w)
     plan = dv.plan_for(w)
     ws = dv.workspace_for(plan)
@@ -321,12 +378,13 @@ def test_append_then_verify_matches_oracle(kv):
     torch.cuda.synchronize()
     kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=w.D, kv=kv, k_new_bits=kn,
                                       v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
-                                      k_scale=w.k_scale if fp8 else None,
-                                      v_scale=w.v_scale if fp8 else None,
+                                      k_scale=w.k_scale if scaled else None,
+                                      v_scale=w.v_scale if scaled else None,
                                       block_table=w.block_table, seq_lens=w.seq_lens,
                                       num_pages=w.num_pages)
-    w2 = dataclasses.replace(w, k_pool=kp, v_pool=vp, k_scale=ks if fp8 else w.k_scale,
-                             v_scale=vs if fp8 else w.v_scale)
+    w2 = dataclasses.replace(w, k_pool=kp, v_pool=vp, k_scale=ks if scaled else w.k_scale,
+                             v_scale=vs if scaled else w.v_scale)
     o = d["out"].float().cpu().numpy().astype(np.float64)
     l = d["lse"].cpu().numpy().astype(np.float64)
-    check(w2, o, l, *oracle.attention(w2))
+    tol = few_key_tolerance(w2) if kv == "mxfp4" else 1e-2
+    check(w2, o, l, *oracle.attention(w2), o_max_abs=tol)
