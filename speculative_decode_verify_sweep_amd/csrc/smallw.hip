@@ -303,22 +303,23 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     constexpr int ST_STAGE = FP4 ? 34 * D : 4 * ST_PAGE;
     constexpr int RING = NS * ST_STAGE;            // DMA ring
     // + decode staging: fp8 K and V, MXFP4 V only (two chunks each, bf16)
-    constexpr int LDS_BYTES = RING + (FP8 ? 2 * BF_STAGE : 0) + (FP4 ? 4 * BF_PAGE : 0);
+    constexpr int LDS_BYTES = RING + (FP8 || FP4 ? 4 * BF_PAGE : 0);
     constexpr int REG_INST = FP4 ? 1 : ST_PAGE / 1024;  // DMA instructions per region
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
     constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
     constexpr int CPR = D / 8;                     // 16-byte bf16 chunks per K token row
-    // chunks in flight ahead of the one being computed: fp8 frees a ring slot
-    // when its chunk is decoded, one iteration before the chunk is computed
-    // (MXFP4 decodes only V then, and reads K from the ring slot itself)
-    constexpr int AHEAD = FP8 ? NS : NS - 1;
-    constexpr int NSS = FP8 ? NS + 1 : 1;          // fp8 scale slots: chunks c .. c+NS live
+    // chunks in flight ahead of the one being computed (the 8- and 4-bit
+    // formats decode V one iteration ahead, but read K from the ring slot)
+    constexpr int AHEAD = NS - 1;
+    constexpr int NSS = FP8 ? NS + 1 : 1;          // fp8 scale slots: chunks c .. c+NS-1 live
+    constexpr bool LOWP = FP8 || FP4;              // scores on the scaled MFMA, V staged
+    constexpr int SPR8 = D / 16;                   // 16-byte slots per fp8 K row
     // MXFP4: 16-byte pieces per stage, DMA instructions per chunk (instruction
     // i is issued by wave i mod 8) and the most any wave issues
     constexpr int N16 = ST_STAGE / 16;
     constexpr int NI4 = (N16 + 63) / 64;
     constexpr int MI4 = (NI4 + kSweepWaves - 1) / kSweepWaves;
-    static_assert(REG_INST >= 1 && NS >= (FP8 ? 3 : 2), "config");
+    static_assert(REG_INST >= 1 && NS >= (LOWP ? 3 : 2), "config");
     static_assert(!FP4 || D == 128 || D == 256, "MXFP4 serves D = 128 and 256");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -350,7 +351,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);  // this row's last key
     const int hi_tok = min(jend - 1, hi_row);
     const int lo_tok = a.window_left > 0 ? hi_row - a.window_left + 1 : INT_MIN;
-    bf16x8_t qf[KS];
+    // Q fragments: KS bf16 k-steps, or for the scaled MFMA (8- and 4-bit K)
+    // qf[4k + 2r + h], the 16-element runs r of 128-deep k-step k (>= 4 entries)
+    bf16x8_t qf[LOWP && KS < 4 ? 4 : KS];
 
     // ---- pool page ids of this unit, staged in LDS (window of kPtab pages)
     int tbase = 0;  // unit-relative page index of ptab[0]
@@ -377,7 +380,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     for (int i = 0; i < LPW; ++i) {
         const int qc = 64 * (ibase + i) + l;  // 16-byte chunk index inside the page-head
         if (FP8) {
-            goff[i] = uint32_t(qc * 16);  // raw codes land unpermuted; the decoder swizzles
+            // K rows (D bytes) get the bf16 rows' 16-byte-slot swizzle; V^T raw
+            const int tr = qc / SPR8, slot = qc % SPR8;
+            const int hsw = (((16 * region_pg + tr) >> 1) & 12 | ((16 * region_pg + tr) & 3)) & (SPR8 - 1);
+            goff[i] = region_v ? uint32_t(qc * 16) : uint32_t(tr * D + (slot ^ hsw) * 16);
         } else if (!region_v) {
             const int tr = qc / CPR, slot = qc % CPR;
             const int tau = 16 * region_pg + tr;
@@ -454,29 +460,21 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
 
-    // fp8: decode ring chunk c once for the whole workgroup into bf16 staging
-    // buffer (c & 1), in the same swizzled layout the bf16 ring uses
-    auto decode_chunk = [&](int c) {
-        const uint8_t* src = smem + (c % NS) * ST_STAGE;
-        uint8_t* dst = smem + RING + (c & 1) * BF_STAGE;
-        for (int q = tid; q < 4 * D; q += kSweepThreads) {
-            const int reg = q / D, within = q % D, pg = reg & 1;
-            const u32x4 raw = *reinterpret_cast<const u32x4*>(src + reg * ST_PAGE + within * 16);
-            const bf16x8_t lo = e4m3x8_to_bf16(raw[0], raw[1]);
-            const bf16x8_t hi = e4m3x8_to_bf16(raw[2], raw[3]);
-            if (reg < 2) {  // K: 16 codes = elements 16cp .. 16cp+15 of token row tr
-                const int tr = within / (D / 16), cp = within % (D / 16);
-                const int tau = 16 * pg + tr;
-                const int h = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
-                uint8_t* row = dst + pg * BF_PAGE + tr * (2 * D);
-                *reinterpret_cast<bf16x8_t*>(row + ((2 * cp) ^ h) * 16) = lo;
-                *reinterpret_cast<bf16x8_t*>(row + ((2 * cp + 1) ^ h) * 16) = hi;
-            } else {        // V^T: 16 codes = tokens 0..15 of d-row `within`
-                uint8_t* row = dst + 2 * BF_PAGE + pg * BF_PAGE + 512 * (within >> 4) +
-                               16 * (within & 15);
-                *reinterpret_cast<bf16x8_t*>(row) = lo;
-                *reinterpret_cast<bf16x8_t*>(row + 256) = hi;
-            }
+    // fp8: decode the V^T codes of ring chunk c once for the whole workgroup
+    // into bf16 staging buffer (c & 1), in the bf16 ring's V^T layout; the V
+    // scales stay out (they multiply P).  Item (page, token half h, row d): 8
+    // codes, one 8-byte read, one 16-byte write.  Straight-line like decode_v4.
+    auto decode_v8 = [&](int c) {
+        const uint8_t* src = smem + (c % NS) * ST_STAGE + 2 * ST_PAGE;
+        uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
+#pragma unroll
+        for (int i = 0; i < (4 * D + kSweepThreads - 1) / kSweepThreads; ++i) {
+            const int it = tid + kSweepThreads * i;
+            if ((4 * D) % kSweepThreads != 0 && it >= 4 * D) break;
+            const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+            const uint2 w8 = *reinterpret_cast<const uint2*>(src + pg * ST_PAGE + d * 16 + 8 * h);
+            *reinterpret_cast<bf16x8_t*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) =
+                e4m3x8_to_bf16(w8.x, w8.y);
         }
     };
 
@@ -489,13 +487,13 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // and the halves are kept: the V scale is exact in the staged values.
     // Straight-line (4D / 512 items per thread), so that a row-tile wave can
     // run it between its score MFMAs and the softmax and the two overlap.
-    static_assert(!FP4 || (4 * D) % kSweepThreads == 0, "whole decode items per thread");
     auto decode_v4 = [&](int c) {
         const uint8_t* src = smem + (c % NS) * ST_STAGE;
         uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
 #pragma unroll
-        for (int i = 0; i < (4 * D) / kSweepThreads; ++i) {
+        for (int i = 0; i < (4 * D + kSweepThreads - 1) / kSweepThreads; ++i) {
             const int it = tid + kSweepThreads * i;
+            if ((4 * D) % kSweepThreads != 0 && it >= 4 * D) break;
             const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
             const uint32_t w4 = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
             const uint2 sb = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) + (d >> 5) * 16 + 8 * h);
@@ -517,33 +515,41 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         const int gq = r - qi * a.G;
         const uint16_t* qrow =
             a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
+        constexpr int NQ = LOWP && KS < 4 ? 4 : KS;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < NQ; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            // bf16 k-step ks, lane group g: elements 32ks + 8g ..  MXFP4: qf[4k
-            // + 2r + h] holds elements ((D/4)(2r + (g>>1)) + 32k + 16(g&1) + 8h
-            // ..), the 16-element runs r = 0, 1 of 128-deep k-step k that the
-            // scaled MFMA's B operand gives lane group g
+            // bf16 k-step ks, lane group g: elements 32ks + 8g ..  Scaled MFMA:
+            // qf[4k + 2r + h] holds run r of k-step k, contraction positions
+            // 64r + 16g + 8h .., which are elements 128k + 64r + 16g + 8h .. of
+            // an fp8 K row (zero past D) and ((D/4)(2r + (g>>1)) + 32k + 16(g&1)
+            // + 8h ..) of an MXFP4 one (its K LDS layout gives lane group g the
+            // row's D/4-element slice)
             const int k4 = ks >> 2, r4 = (ks >> 1) & 1, h4 = ks & 1;
-            const int d0 = FP4 ? (D / 4) * (2 * r4 + (g >> 1)) + 32 * k4 + 16 * (g & 1) + 8 * h4
-                               : 32 * ks + 8 * g;
-            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+            const int d0 = FP4   ? (D / 4) * (2 * r4 + (g >> 1)) + 32 * k4 + 16 * (g & 1) + 8 * h4
+                           : FP8 ? 128 * k4 + 64 * r4 + 16 * g + 8 * h4
+                                 : 32 * ks + 8 * g;
+            if (valid && d0 < D) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
             qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-    // ---- MXFP4 scores run on the scaled MFMA (E2M1 K times e4m3 Q, E8M0
-    // scales per 32 elements of the contraction).  Q is split once per unit:
+    // ---- 8- and 4-bit scores run on the scaled MFMA (e4m3 or E2M1 K times e4m3
+    // Q, E8M0 scales per 32 elements of the contraction: the MXFP4 block scales
+    // for K, 1 for e4m3 K, whose per-token scale multiplies S instead).  The
+    // MFMA's fp4 and fp8 operands put contraction positions 64r + 16g .. 64r +
+    // 16g + 15 (runs r = 0, 1) or 32g .. 32g + 31 in lane group g.  Q is split
+    // once per unit:
     // q = hi 2^X + lo 2^(X-4) per 32-element block, hi and lo e4m3 and X =
     // floor(log2 amax) - 7, so |q| / 2^X < 256 and the residual fits lo.  A
     // block's 32 elements are the runs of two lane groups (g, g ^ 1); the scale
     // that lane group g hands the MFMA is that of contraction block g, whose
     // elements are run g >> 1 of lane groups 2(g & 1) and 2(g & 1) + 1.
-    constexpr int KS4 = D / 128;  // 128-deep k-steps of the scaled MFMA
-    i32x8 qhi[FP4 ? KS4 : 1], qlo[FP4 ? KS4 : 1];
+    constexpr int KS4 = D < 128 ? 1 : D / 128;  // 128-deep k-steps of the scaled MFMA
+    i32x8 qhi[LOWP ? KS4 : 1], qlo[LOWP ? KS4 : 1];
     uint32_t shi = 0, slo = 0;    // byte k: E8M0 scale this lane supplies for k-step k
-    if constexpr (FP4) {
+    if constexpr (LOWP) {
 #pragma unroll
         for (int k = 0; k < KS4; ++k) {
             int X[2];
@@ -625,9 +631,26 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
         (void)pg;
     }
+    // fp8 K: tile t row tau, run r of k-step k = bytes 128k + 64r + 16g .. of
+    // the row, i.e. 16-byte slot 8k + 4r + g, stored at slot ^ h(tau)
+    uint32_t k8addr[2][LOWP ? KS4 : 1][2] = {};
+    if constexpr (FP8) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
+            const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (SPR8 - 1);
+#pragma unroll
+            for (int k = 0; k < KS4; ++k)
+#pragma unroll
+                for (int r4 = 0; r4 < 2; ++r4) {
+                    const int slot = (8 * k + 4 * r4 + g) & (SPR8 - 1);  // D = 64: run 1 unused
+                    k8addr[t][k][r4] = uint32_t((tau >> 4) * ST_PAGE + (tau & 15) * D + 16 * (slot ^ hsw));
+                }
+        }
+    }
     // where this lane's V^T operand rows start: the bf16 ring stage, or the
-    // MXFP4 V staging buffer (the two V pages only)
-    const uint32_t va = FP4 ? vaddr - 2 * BF_PAGE : vaddr;
+    // V staging buffer of the 8- and 4-bit formats (the two V pages only)
+    const uint32_t va = LOWP ? vaddr - 2 * BF_PAGE : vaddr;
 
     f32x4 acc[DT];
 #pragma unroll
@@ -636,8 +659,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 
     auto process = [&](int c, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        const uint8_t* st = FP8 ? smem + RING + (c & 1) * BF_STAGE : smem + (c % NS) * ST_STAGE;
-        const uint8_t* vst = FP4 ? smem + RING + (c & 1) * (2 * BF_PAGE) : st;  // V^T operand rows
+        const uint8_t* st = smem + (c % NS) * ST_STAGE;
+        const uint8_t* vst = LOWP ? smem + RING + (c & 1) * (2 * BF_PAGE) : st;  // V^T operand rows
         const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
         // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
         // independent accumulation chains for MFMA pipelining.  All K operand
@@ -645,7 +668,31 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         f32x4 s4[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) s4[t][0] = s4[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP4) {
+        if constexpr (FP8) {
+            // per tile row and k-step: the lane's two 16-byte runs of e4m3 codes
+            // (run 1 is zero at D = 64); K block scales 1 (byte 127)
+            i32x8 ka[2][KS4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int k = 0; k < KS4; ++k) {
+                    const u32x4 r0 = *reinterpret_cast<const u32x4*>(st + k8addr[t][k][0]);
+                    u32x4 r1 = {0u, 0u, 0u, 0u};
+                    if constexpr (D >= 128) r1 = *reinterpret_cast<const u32x4*>(st + k8addr[t][k][1]);
+                    ka[t][k] = i32x8{int(r0[0]), int(r0[1]), int(r0[2]), int(r0[3]),
+                                     int(r1[0]), int(r1[1]), int(r1[2]), int(r1[3])};
+                }
+#pragma unroll
+            for (int k = 0; k < KS4; ++k)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    s4[t][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka[t][k], qhi[k], s4[t][0], 0, 0, 0, 0x7F7F7F7F, 0, int(shi >> (8 * k)));
+                    s4[t][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka[t][k], qlo[k], s4[t][1], 0, 0, 0, 0x7F7F7F7F, 0, int(slo >> (8 * k)));
+                }
+            decode_v8(c + 1);   // this thread's share of the next chunk's V, under the MFMAs
+        } else if constexpr (FP4) {
             // per tile row: the lane's D/8 code bytes (16 per 128-deep k-step:
             // one E2M1 block) and their E8M0 scales (byte k for k-step k); the
             // hi and lo parts of Q accumulate in separate chains
@@ -693,7 +740,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         // V^T operands do not depend on the softmax: at D = 256 issue their reads
         // now so their latency hides behind it (smaller heads and the fp8 path,
         // which also holds the scales, keep the registers)
-        constexpr bool VPRE = D == 256 && !FP8;
+        constexpr bool VPRE = D == 256;
         u32x4 vraw[VPRE ? DT : 1];
         if constexpr (VPRE) {
 #pragma unroll
@@ -769,19 +816,14 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- ring step for iteration c.
     // bf16: wait for chunk c, then refill the slot freed by chunk c-1 with
     //       chunk c+NS-1.
-    // MXFP4: as bf16, but wait for chunk c+1, whose V every thread decodes
-    //       into staging during iteration c (row-tile waves inside process,
-    //       between the score MFMAs and the softmax); chunk c's K is read from
-    //       its ring slot.
-    // fp8:  chunk c was decoded (out of its ring slot) during iteration c-1;
-    //       wait for chunk c+1 (to decode it now), then refill chunk c's slot
-    //       with chunk c+NS.  Either way NS-2 chunks stay in flight past the
-    //       one waited for.
+    // fp8 and MXFP4: as bf16, but wait for chunk c+1, whose V every thread
+    //       decodes into staging during iteration c (row-tile waves inside
+    //       process, between the score MFMAs and the softmax); chunk c's K is
+    //       read from its ring slot.
     auto ring_step = [&](int c) {
-        const int need = FP8 || FP4 ? c + 1 : c;
-        // chunks younger than `need` left in flight: fp8 has issued up to
-        // c+NS-1 by now, the others up to c+NS-2
-        if (need < nchunks) wait_vmcnt_dyn(min(FP4 ? NS - 3 : NS - 2, nchunks - 1 - need) * nload);
+        const int need = LOWP ? c + 1 : c;
+        // chunks younger than `need` left in flight: all issued up to c+NS-2
+        if (need < nchunks) wait_vmcnt_dyn(min(LOWP ? NS - 3 : NS - 2, nchunks - 1 - need) * nload);
         __syncthreads();
         const int cn = c + AHEAD;
         if (cn < nchunks) {
@@ -793,15 +835,15 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             }
             issue_chunk(cn);
         }
-        if constexpr (FP8) {
-            if (c + 1 < nchunks) decode_chunk(c + 1);
-        }
     };
-    if ((FP8 || FP4) && nchunks > 0) {  // decode chunk 0 ahead of the loop
+    auto decode_v = [&](int c) {
+        if constexpr (FP8) decode_v8(c);
+        else if constexpr (FP4) decode_v4(c);
+    };
+    if (LOWP && nchunks > 0) {  // decode chunk 0's V ahead of the loop
         wait_vmcnt_dyn(min(AHEAD - 1, nchunks - 1) * nload);
         __syncthreads();
-        if constexpr (FP8) decode_chunk(0);
-        else if constexpr (FP4) decode_v4(0);
+        decode_v(0);
     }
     // Chunks that need no mask come first: the masked ones (keys past the
     // unit's end, or past some row's causal limit) are always a suffix.
@@ -816,17 +858,17 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     for (; c < c_head; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::true_type{});
-        else if constexpr (FP4) decode_v4(c + 1);
+        else if constexpr (LOWP) decode_v(c + 1);
     }
     for (; c < c_tail; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::false_type{});
-        else if constexpr (FP4) decode_v4(c + 1);
+        else if constexpr (LOWP) decode_v(c + 1);
     }
     for (; c < nchunks; ++c) {
         ring_step(c);
         if (has_tile) process(c, std::true_type{});
-        else if constexpr (FP4) decode_v4(c + 1);
+        else if constexpr (LOWP) decode_v(c + 1);
     }
 
     // ---- epilogue: normalise, write the final output or the split partial
@@ -1115,7 +1157,7 @@ int launch(K kernel, int64_t blocks, int threads, const Params& a, hipStream_t s
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* ev0, void* ev1) {
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        return launch(sweep_kernel<D, 5, SMALLW_KV_FP8_E4M3>, pl->U, kSweepThreads, a, st, ev0,
+        return launch(sweep_kernel<D, 7, SMALLW_KV_FP8_E4M3>, pl->U, kSweepThreads, a, st, ev0,
                       ev1, "sweep kernel launch");
     if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
         if constexpr (D == 64) return SMALLW_EUNSUPPORTED;  // the planner rejects it first
