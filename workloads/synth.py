@@ -55,6 +55,9 @@ CONFIGS = {
     # KV, pages in order
     "fp4_16k": dict(P=1, Hq=24, Hkv=4, D=256, ctx=(16384,), W=16, causal=True, kv="mxfp4",
                     placement="in_order", pool_pages=None),
+    # the same at 64K context, pages a seeded permutation of a 5000-page pool
+    "fp4_64k": dict(P=1, Hq=24, Hkv=4, D=256, ctx=(65536,), W=16, causal=True, kv="mxfp4",
+                    placement="permuted", pool_pages=5000),
 }
 
 CONFIG_SEED_BASE = 20261202
