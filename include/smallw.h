@@ -49,9 +49,12 @@
  *                                                  2i, 2i+1 of its row
  *   v_pool       uint8 [num_pages][Hkv][D][8]      byte i of row d: element d
  *                                                  of tokens 2i, 2i+1
- *   k_scale      uint8 E8M0 [num_pages][Hkv][16][D/32]: block b of token t
- *   v_scale      uint8 E8M0 [num_pages][Hkv][16][D/32]  scales elements
- *                32b .. 32b+31 of that token's row by 2^(e-127)
+ *   k_scale      uint8 E8M0 [num_pages][Hkv][16][D/32]: byte b of token t
+ *                scales elements 32b .. 32b+31 of that token's K row by
+ *                2^(e-127)
+ *   v_scale      uint8 E8M0 [num_pages][Hkv][D/32][16]: block-major like the
+ *                transposed value page; byte [b][t] scales elements
+ *                32b .. 32b+31 of token t's V row
  * ("ChunkedSmallT re-streams full KV per query chunk", section Measurement,
  * times a 4-bit KV cache; the format here is OCP MXFP4: E2M1 values
  * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, 32-element blocks, E8M0 scales.)
