@@ -318,15 +318,16 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         w = calls[16].w
+        # repeat the whole call for about 10 s of CPU work (at least 3 runs)
         times = []
-        for _ in range(3):
+        while len(times) < 3 or sum(times) < 10.0:
             t = time.perf_counter()
             oracle.attention(w)
             times.append(time.perf_counter() - t)
         cpu = {"value": round(statistics.median(times) * 1e6, 1), "unit": "us/layer-call",
                "cores": oracle.oracle_threads(), "kind": "oracle",
                "sample": "the full 64K W=16 layer call (all 16 rows x 24 heads), fp64, "
-                         "median of 3 runs"}
+                         f"median of {len(times)} runs ({sum(times):.1f} s of oracle time)"}
         log(f"oracle: {cpu['value']/1e3:.1f} ms on {cpu['cores']} threads")
 
     line = {

@@ -129,6 +129,9 @@ __device__ __forceinline__ int phys_page(const Params& a, int p, int n) {
 // Issued through inline asm so the compiler does not guard every later LDS
 // read with a full vmcnt(0) wait; completion is tracked by hand with vmcnt.
 // The s_nop is the wait state an M0 write needs before an LDS DMA reads it.
+// M0 is written inside the statement but not listed as clobbered (the
+// compiler reserves it and ignores such a clobber); no compiled code of these
+// kernels reads M0 apart from these statements, so no compiler value is lost.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
