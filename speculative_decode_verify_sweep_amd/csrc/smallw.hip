@@ -293,7 +293,7 @@ __device__ __forceinline__ void fp4_piece(int q, int& arr, int& pg, int& off) {
     }
 }
 
-template <int D, int NS, int KV>
+template <int D, int NS, int KV, bool DECH>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     constexpr bool FP8 = KV == SMALLW_KV_FP8_E4M3;
     constexpr bool FP4 = KV == SMALLW_KV_MXFP4;
@@ -349,6 +349,13 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- this wave's query rows (tile w)
     const int T = (a.R + 15) >> 4;
     const bool has_tile = w < T;
+    // V decode (8- and 4-bit formats).  Wave w runs on SIMD w mod 4, so five or
+    // six row tiles put two on SIMDs 0 and 1 and one on SIMDs 2 and 3.  Then
+    // (DECH, chosen at launch) only the four waves on SIMDs 2 and 3 decode, as
+    // threads dec_id = 0..255 with 4D/256 items each, the row-tile ones after
+    // their chunk's PV; otherwise every thread decodes its 4D/512 items, a
+    // row-tile wave under its score MFMAs.
+    const int dec_id = (w >> 2) * 128 + (w & 1) * 64 + l;
     const int r = 16 * w + ln;
     const int qi = r / a.G;
     const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);  // this row's last key
@@ -467,17 +474,27 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // into bf16 staging buffer (c & 1), in the bf16 ring's V^T layout; the V
     // scales stay out (they multiply P).  Item (page, token half h, row d): 8
     // codes, one 8-byte read, one 16-byte write.  Straight-line like decode_v4.
+    auto v8_item = [&](const uint8_t* src, uint8_t* dst, int it) {
+        const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+        const uint2 w8 = *reinterpret_cast<const uint2*>(src + pg * ST_PAGE + d * 16 + 8 * h);
+        *reinterpret_cast<bf16x8_t*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) =
+            e4m3x8_to_bf16(w8.x, w8.y);
+    };
     auto decode_v8 = [&](int c) {
         const uint8_t* src = smem + (c % NS) * ST_STAGE + 2 * ST_PAGE;
         uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
+        if constexpr (DECH) {
+            if (w & 2) {
+#pragma unroll
+                for (int i = 0; i < 4 * D / 256; ++i) v8_item(src, dst, dec_id + 256 * i);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < (4 * D + kSweepThreads - 1) / kSweepThreads; ++i) {
             const int it = tid + kSweepThreads * i;
             if ((4 * D) % kSweepThreads != 0 && it >= 4 * D) break;
-            const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-            const uint2 w8 = *reinterpret_cast<const uint2*>(src + pg * ST_PAGE + d * 16 + 8 * h);
-            *reinterpret_cast<bf16x8_t*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) =
-                e4m3x8_to_bf16(w8.x, w8.y);
+            v8_item(src, dst, it);
         }
     };
 
@@ -488,23 +505,34 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // row's block (one 8-byte read, V scales being block-major).  The two
     // tokens of a byte have their own scales, so each byte is converted twice
     // and the halves are kept: the V scale is exact in the staged values.
-    // Straight-line (4D / 512 items per thread), so that a row-tile wave can
-    // run it between its score MFMAs and the softmax and the two overlap.
+    // Straight-line (4D / 512 items per thread, or 4D / 256 on the waves of
+    // SIMDs 2 and 3 with DECH), so that a row-tile wave can run it between its
+    // score MFMAs and the softmax and the two overlap.
+    auto v4_item = [&](const uint8_t* src, uint8_t* dst, int it) {
+        const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+        const uint32_t w4 = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
+        const uint2 sb = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) + (d >> 5) * 16 + 8 * h);
+        const u32x4 o = {e2m1x2_two_scales<0>(w4, sb.x & 0xFFu, (sb.x >> 8) & 0xFFu),
+                         e2m1x2_two_scales<1>(w4, (sb.x >> 16) & 0xFFu, sb.x >> 24),
+                         e2m1x2_two_scales<2>(w4, sb.y & 0xFFu, (sb.y >> 8) & 0xFFu),
+                         e2m1x2_two_scales<3>(w4, (sb.y >> 16) & 0xFFu, sb.y >> 24)};
+        *reinterpret_cast<u32x4*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) = o;
+    };
     auto decode_v4 = [&](int c) {
         const uint8_t* src = smem + (c % NS) * ST_STAGE;
         uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
+        if constexpr (DECH) {
+            if (w & 2) {
+#pragma unroll
+                for (int i = 0; i < 4 * D / 256; ++i) v4_item(src, dst, dec_id + 256 * i);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < (4 * D + kSweepThreads - 1) / kSweepThreads; ++i) {
             const int it = tid + kSweepThreads * i;
             if ((4 * D) % kSweepThreads != 0 && it >= 4 * D) break;
-            const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-            const uint32_t w4 = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
-            const uint2 sb = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) + (d >> 5) * 16 + 8 * h);
-            const u32x4 o = {e2m1x2_two_scales<0>(w4, sb.x & 0xFFu, (sb.x >> 8) & 0xFFu),
-                             e2m1x2_two_scales<1>(w4, (sb.x >> 16) & 0xFFu, sb.x >> 24),
-                             e2m1x2_two_scales<2>(w4, sb.y & 0xFFu, (sb.y >> 8) & 0xFFu),
-                             e2m1x2_two_scales<3>(w4, (sb.y >> 16) & 0xFFu, sb.y >> 24)};
-            *reinterpret_cast<u32x4*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) = o;
+            v4_item(src, dst, it);
         }
     };
 
@@ -694,7 +722,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
                     s4[t][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         ka[t][k], qlo[k], s4[t][1], 0, 0, 0, 0x7F7F7F7F, 0, int(slo >> (8 * k)));
                 }
-            decode_v8(c + 1);   // this thread's share of the next chunk's V, under the MFMAs
+            // this thread's share of the next chunk's V, under the MFMAs (with
+            // DECH the row-tile waves of SIMDs 2 and 3 decode after their PV)
+            if constexpr (!DECH) decode_v8(c + 1);
         } else if constexpr (FP4) {
             // per tile row: the lane's D/8 code bytes (16 per 128-deep k-step:
             // one E2M1 block) and their E8M0 scales (byte k for k-step k); the
@@ -724,7 +754,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             if constexpr (KS4 > 1) kstep(std::integral_constant<int, 1>{});
             // this thread's share of the next chunk's V decode, under the MFMAs
             // (past the last chunk it decodes a stale slot that nobody reads)
-            decode_v4(c + 1);
+            if constexpr (!DECH) decode_v4(c + 1);
         } else {
             bf16x8_t kop[KS][2];
 #pragma unroll
@@ -860,18 +890,30 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     int c = 0;
     for (; c < c_head; ++c) {
         ring_step(c);
-        if (has_tile) process(c, std::true_type{});
-        else if constexpr (LOWP) decode_v(c + 1);
+        if (has_tile) {
+            process(c, std::true_type{});
+            if constexpr (DECH) decode_v(c + 1);
+        } else if constexpr (LOWP) {
+            decode_v(c + 1);
+        }
     }
     for (; c < c_tail; ++c) {
         ring_step(c);
-        if (has_tile) process(c, std::false_type{});
-        else if constexpr (LOWP) decode_v(c + 1);
+        if (has_tile) {
+            process(c, std::false_type{});
+            if constexpr (DECH) decode_v(c + 1);
+        } else if constexpr (LOWP) {
+            decode_v(c + 1);
+        }
     }
     for (; c < nchunks; ++c) {
         ring_step(c);
-        if (has_tile) process(c, std::true_type{});
-        else if constexpr (LOWP) decode_v(c + 1);
+        if (has_tile) {
+            process(c, std::true_type{});
+            if constexpr (DECH) decode_v(c + 1);
+        } else if constexpr (LOWP) {
+            decode_v(c + 1);
+        }
     }
 
     // ---- epilogue: normalise, write the final output or the split partial
@@ -1159,16 +1201,23 @@ int launch(K kernel, int64_t blocks, int threads, const Params& a, hipStream_t s
 
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* ev0, void* ev1) {
+    // five or six row tiles: the V decode moves to the waves on SIMDs 2 and 3
+    const int T = (pl->R + 15) / 16;
+    const bool dech = T == 5 || T == 6;
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        return launch(sweep_kernel<D, 7, SMALLW_KV_FP8_E4M3>, pl->U, kSweepThreads, a, st, ev0,
-                      ev1, "sweep kernel launch");
+        return dech ? launch(sweep_kernel<D, 7, SMALLW_KV_FP8_E4M3, true>, pl->U, kSweepThreads, a,
+                             st, ev0, ev1, "sweep kernel launch")
+                    : launch(sweep_kernel<D, 7, SMALLW_KV_FP8_E4M3, false>, pl->U, kSweepThreads, a,
+                             st, ev0, ev1, "sweep kernel launch");
     if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
         if constexpr (D == 64) return SMALLW_EUNSUPPORTED;  // the planner rejects it first
         else
-            return launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4>, pl->U, kSweepThreads, a, st, ev0,
-                          ev1, "sweep kernel launch");
+            return dech ? launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4, true>, pl->U, kSweepThreads,
+                                 a, st, ev0, ev1, "sweep kernel launch")
+                        : launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4, false>, pl->U, kSweepThreads,
+                                 a, st, ev0, ev1, "sweep kernel launch");
     }
-    return launch(sweep_kernel<D, 4, SMALLW_KV_BF16>, pl->U, kSweepThreads, a, st, ev0, ev1,
+    return launch(sweep_kernel<D, 4, SMALLW_KV_BF16, false>, pl->U, kSweepThreads, a, st, ev0, ev1,
                   "sweep kernel launch");
 }
 

@@ -56,8 +56,9 @@ def test_every_kernel_is_present(asm):
     names = [n for n, _ in kernels(asm["smallw.hip"])]
     for k in ("sweep_kernel", "combine_kernel", "trace_kernel"):
         assert any(k in n for n in names), (k, names)
-    # bf16, fp8 and MXFP4 sweeps at D = 64 / 128 / 256 (no MXFP4 at D = 64)
-    assert sum("sweep_kernel" in n for n in names) == 8
+    # bf16, fp8 and MXFP4 sweeps at D = 64 / 128 / 256 (no MXFP4 at D = 64); the
+    # 8- and 4-bit ones in both V-decode placements
+    assert sum("sweep_kernel" in n for n in names) == 3 + 2 * 3 + 2 * 2
     assert any("append_kernel" in n for n, _ in kernels(asm["append.hip"]))
 
 
