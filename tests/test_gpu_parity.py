@@ -345,6 +345,33 @@ def test_mxfp4_edge_shapes(case, force):
     check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
 
 
+# Five or six row tiles (W*G in 65..96): the 8- and 4-bit V decode runs only on
+# the four waves of SIMDs 2 and 3; the row-tile waves among them decode after
+# their chunk's PV.  T = ceil(W*G / 16) noted per case.
+DECH_CASES = [
+    ("fp8", dict(P=2, Hq=5, Hkv=1, D=64, ctx=(37, 300), W=16, causal=True)),        # T = 5
+    ("fp8", dict(P=1, Hq=12, Hkv=2, D=128, ctx=(1000,), W=16, causal=False)),      # T = 6
+    ("fp8", dict(P=3, Hq=20, Hkv=4, D=256, ctx=(0, 90, 777), W=13, causal=True)),  # T = 5
+    ("mxfp4", dict(P=2, Hq=10, Hkv=2, D=128, ctx=(5, 640), W=16, causal=True)),    # T = 5
+    ("mxfp4", dict(P=2, Hq=14, Hkv=2, D=256, ctx=(129, 2000), W=11, causal=True)), # T = 5
+    ("mxfp4", dict(P=1, Hq=6, Hkv=1, D=256, ctx=(300,), W=16, causal=False)),      # T = 6
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECH_CASES)))
+@pytest.mark.parametrize("force", [0, 3])
+def test_v_decode_on_simds_2_and_3(case, force):
+    kv, spec = DECH_CASES[case]
+    G = spec["Hq"] // spec["Hkv"]
+    assert -(-spec["W"] * G // 16) in (5, 6)
+    npg = sum(-(-(c + spec["W"]) // 16) for c in spec["ctx"])
+    w = make_workload(None, kv=kv, placement="permuted", pool_pages=npg + 5,
+                      seed=700 + case, **spec)
+    announce(f"{kv} five/six row tiles {case} {spec} force={force}")
+    o, l = gpu_run(w, force_splits=force)
+    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+
+
 def test_mxfp4_poison_and_determinism():
     kw = dict(P=2, Hq=24, Hkv=4, D=256, ctx=(501, 77), W=16, causal=True, kv="mxfp4",
               placement="permuted", pool_pages=60, seed=64)
