@@ -300,7 +300,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
     constexpr int BF_PAGE = 32 * D;                // bf16 page-head of K (or V^T) in LDS
-    constexpr int BF_STAGE = 4 * BF_PAGE;          // K0 K1 V0 V1, bf16
     // page-head codes as streamed from HBM; an MXFP4 stage also holds its scales
     constexpr int ST_PAGE = FP4 ? 8 * D : (FP8 ? 16 * D : BF_PAGE);
     constexpr int ST_STAGE = FP4 ? 34 * D : 4 * ST_PAGE;
@@ -392,7 +391,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         if (FP8) {
             // K rows (D bytes) get the bf16 rows' 16-byte-slot swizzle; V^T raw
             const int tr = qc / SPR8, slot = qc % SPR8;
-            const int hsw = (((16 * region_pg + tr) >> 1) & 12 | ((16 * region_pg + tr) & 3)) & (SPR8 - 1);
+            const int hsw = ((((16 * region_pg + tr) >> 1) & 12) | ((16 * region_pg + tr) & 3)) & (SPR8 - 1);
             goff[i] = region_v ? uint32_t(qc * 16) : uint32_t(tr * D + (slot ^ hsw) * 16);
         } else if (!region_v) {
             const int tr = qc / CPR, slot = qc % CPR;
