@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     constexpr int ST_PAGE = FP4 ? 8 * D : (FP8 ? 16 * D : BF_PAGE);
     constexpr int ST_STAGE = FP4 ? 34 * D : 4 * ST_PAGE;
     constexpr int RING = NS * ST_STAGE;            // DMA ring
-    // + decode staging: fp8 K and V, MXFP4 V only (two chunks each, bf16)
+    // + V decode staging for the 8- and 4-bit formats: two chunks of V^T, bf16
     constexpr int LDS_BYTES = RING + (FP8 || FP4 ? 4 * BF_PAGE : 0);
     constexpr int REG_INST = FP4 ? 1 : ST_PAGE / 1024;  // DMA instructions per region
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // D/8 bytes.  K scales: the lane's first block of that row.
     uint32_t k4addr[2][2] = {}, k4sc[2] = {};
     if constexpr (FP4) {
-        const int rg = ln >> 2, pg = g >> 1;
+        const int rg = ln >> 2;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int pos = (4 * t + (ln & 3)) ^ (4 * (rg & 1));
@@ -659,7 +659,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
                     : uint32_t((rg * 4 + (g ^ (rg >> 1))) * D + pos * 16);
             k4sc[t] = uint32_t(32 * D + (tau >> 4) * (D / 2) + (tau & 15) * (D / 32) + g * (KS / 4));
         }
-        (void)pg;
     }
     // fp8 K: tile t row tau, run r of k-step k = bytes 128k + 64r + 16g .. of
     // the row, i.e. 16-byte slot 8k + 4r + g, stored at slot ^ h(tau)
@@ -770,8 +769,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
                                                                               s4[t][ks & 1], 0, 0, 0);
         }
         // V^T operands do not depend on the softmax: at D = 256 issue their reads
-        // now so their latency hides behind it (smaller heads and the fp8 path,
-        // which also holds the scales, keep the registers)
+        // now so their latency hides behind it (at smaller heads the registers
+        // are worth more: D = 128 would drop to one workgroup per CU)
         constexpr bool VPRE = D == 256;
         u32x4 vraw[VPRE ? DT : 1];
         if constexpr (VPRE) {
@@ -886,34 +885,21 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     int c_head = 0;
     while (c_head < c_tail && (un.pb + 2 * c_head) * kPage < win_hi) ++c_head;
 
+    // one iteration: the ring step, then the row-tile waves' scores, softmax
+    // and PV of chunk c and everyone's share of the V decode of chunk c+1
+    auto step = [&](int c, auto tail_tag) {
+        ring_step(c);
+        if (has_tile) {
+            process(c, tail_tag);
+            if constexpr (DECH) decode_v(c + 1);
+        } else if constexpr (LOWP) {
+            decode_v(c + 1);
+        }
+    };
     int c = 0;
-    for (; c < c_head; ++c) {
-        ring_step(c);
-        if (has_tile) {
-            process(c, std::true_type{});
-            if constexpr (DECH) decode_v(c + 1);
-        } else if constexpr (LOWP) {
-            decode_v(c + 1);
-        }
-    }
-    for (; c < c_tail; ++c) {
-        ring_step(c);
-        if (has_tile) {
-            process(c, std::false_type{});
-            if constexpr (DECH) decode_v(c + 1);
-        } else if constexpr (LOWP) {
-            decode_v(c + 1);
-        }
-    }
-    for (; c < nchunks; ++c) {
-        ring_step(c);
-        if (has_tile) {
-            process(c, std::true_type{});
-            if constexpr (DECH) decode_v(c + 1);
-        } else if constexpr (LOWP) {
-            decode_v(c + 1);
-        }
-    }
+    for (; c < c_head; ++c) step(c, std::true_type{});
+    for (; c < c_tail; ++c) step(c, std::false_type{});
+    for (; c < nchunks; ++c) step(c, std::true_type{});
 
     // ---- epilogue: normalise, write the final output or the split partial
     if (!has_tile) return;
