@@ -60,7 +60,15 @@
  * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, 32-element blocks, E8M0 scales.)
  *   block_table  int32 [P][max_pages_per_req]; entry n of row p is the pool
  *                page holding tokens [16n, 16n+16) of request p
- *   seq_lens     int32 [P]; must equal the host lengths given to the plan
+ *   seq_lens     int32 [P], the lengths this call attends with.  The plan
+ *                fixes only the split counts; the kernels recompute every
+ *                page range from these device lengths.  So a plan (or a
+ *                captured graph of a call) stays valid when lengths change
+ *                between calls, provided each length still obeys the plan's
+ *                host rules (0 <= L_p <= 16*max_pages_per_req; causal:
+ *                L_p == 0 or L_p >= W) and its block-table row covers it.
+ *                Split balance follows the plan's lengths.  The row-exact
+ *                bitwise guarantee holds when they equal the device lengths.
  *   out          bf16   [P][W][Hq][D]
  *   lse          fp32   [P][W][Hq]   natural log
  * Pages are 16 tokens.  e4m3fn is the OCP 8-bit format (bias 7, max 448,
