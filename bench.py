@@ -288,6 +288,41 @@ def main():
             log(f"{label}: {t_us:.1f} us (sweep {s_us:.1f}), {others[label]['kv_GBps']} GB/s")
             del dd, wsb
 
+    # the paged KV append that precedes a verify call: W window rows of K and V
+    # into their pool slots, back-to-back calls between two events (per call)
+    appends = {}
+    if not args.only_w16:
+        aspecs = [("verify W=16, 4 KV heads, D=256, bf16", dict(P=1, Hq=24, Hkv=4, D=256, W=16, kv="bf16")),
+                  ("verify W=16, 4 KV heads, D=256, fp8", dict(P=1, Hq=24, Hkv=4, D=256, W=16, kv="fp8")),
+                  ("verify W=16, 4 KV heads, D=256, MXFP4", dict(P=1, Hq=24, Hkv=4, D=256, W=16, kv="mxfp4")),
+                  ("draft P=8 W=9, 8 KV heads, D=128, bf16", dict(P=8, Hq=32, Hkv=8, D=128, W=9, kv="bf16"))]
+        for label, spec in aspecs:
+            wl = make_workload(None, ctx=tuple([1024] * spec["P"]), causal=True,
+                               placement="permuted", seed=77, **spec)
+            dd = dv.upload(wl)
+            pl = dv.plan_for(wl)
+            kn = torch.randn((wl.P, wl.W, wl.Hkv, wl.D), device="cuda").to(torch.bfloat16)
+            vn = torch.randn((wl.P, wl.W, wl.Hkv, wl.D), device="cuda").to(torch.bfloat16)
+
+            def ap_call(pl=pl, dd=dd, kn=kn, vn=vn):
+                B.small_w_kv_append(pl, kn, vn, dd["k_pool"], dd["v_pool"], dd["k_scale"],
+                                    dd["v_scale"], dd["block_table"], dd["seq_lens"])
+
+            for _ in range(args.warmup):
+                ap_call()
+            a0, a1 = B.hip_event_create(), B.hip_event_create()
+            B.hip_event_record(a0, stream)
+            for _ in range(args.steps):
+                ap_call()
+            B.hip_event_record(a1, stream)
+            torch.cuda.synchronize()
+            a_us = B.hip_event_elapsed_ms(a0, a1) * 1e3 / args.steps
+            B.hip_event_destroy(a0)
+            B.hip_event_destroy(a1)
+            appends[label] = round(a_us, 2)
+            log(f"append {label}: {a_us:.2f} us per call (back-to-back)")
+            del dd
+
     # the same cold W=16 call between ordinary event markers (includes their cost)
     marker_us = statistics.median(timed_markers(calls[16], args.steps)) * 1e3
     log(f"W=16 cold between event markers: median {marker_us:.1f} us")
@@ -365,6 +400,7 @@ def main():
                      "bytes_per_launch": kvb},
         "cpu_baseline": cpu,
         "other_workloads": others,
+        "kv_append_us": appends,
         "reference_context": {"pages_gpu_unnamed_64K_bf16": {"W8_us": 201, "W8_GBps": 1338,
                                                              "W16_us": 393, "W16_GBps": 683}},
     }

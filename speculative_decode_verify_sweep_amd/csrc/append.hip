@@ -83,6 +83,22 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
     const int kvh = b % a.Hkv;
     const int i = (b / a.Hkv) % a.W;
     const int p = b / (a.Hkv * a.W);
+    const int l = threadIdx.x;
+    // the window row first: its address does not depend on the slot, so its
+    // load overlaps the dependent length -> block-table -> slot lookup
+    const int64_t row = ((int64_t(p) * a.W + i) * a.Hkv + kvh) * D + E * l;
+    uint16_t kb[E], vb[E];  // raw bf16 bits, loaded once before any store
+    float kx[E], vx[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kb[e] = a.k_new[row + e];
+        vb[e] = a.v_new[row + e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kx[e] = bf16_to_f32(kb[e]);
+        vx[e] = bf16_to_f32(vb[e]);
+    }
     int L = a.seq[p];
     const int cap = a.bt_stride * SMALLW_PAGE_SIZE;
     L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -91,15 +107,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
     int page = a.bt[int64_t(p) * a.bt_stride + (pos >> 4)];
     page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
     const int slot = pos & 15;
-    const int l = threadIdx.x;
-    const int64_t row = ((int64_t(p) * a.W + i) * a.Hkv + kvh) * D + E * l;
     const int64_t ph = int64_t(page) * a.Hkv + kvh;  // page-head index
-    float kx[E], vx[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        kx[e] = bf16_to_f32(a.k_new[row + e]);
-        vx[e] = bf16_to_f32(a.v_new[row + e]);
-    }
     if constexpr (FP4) {
         // lane l holds elements E l .. E l + E - 1; a 32-element block is 32/E lanes
         constexpr int BL = 32 / E;
@@ -144,8 +152,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
         uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool) + ph * D * 16 + slot;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            kp[e] = a.k_new[row + e];
-            vp[int64_t(E * l + e) * 16] = a.v_new[row + e];
+            kp[e] = kb[e];
+            vp[int64_t(E * l + e) * 16] = vb[e];
         }
     } else {
         float km = 0.f, vm = 0.f;
