@@ -473,27 +473,44 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // into bf16 staging buffer (c & 1), in the bf16 ring's V^T layout; the V
     // scales stay out (they multiply P).  Item (page, token half h, row d): 8
     // codes, one 8-byte read, one 16-byte write.  Straight-line like decode_v4.
-    auto v8_item = [&](const uint8_t* src, uint8_t* dst, int it) {
-        const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-        const uint2 w8 = *reinterpret_cast<const uint2*>(src + pg * ST_PAGE + d * 16 + 8 * h);
-        *reinterpret_cast<bf16x8_t*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) =
-            e4m3x8_to_bf16(w8.x, w8.y);
-    };
+    // Decoders run in two phases, every item's reads and then every item's
+    // converts and staging writes: the compiler cannot tell the staging tile
+    // from the ring slot, so a read placed after a write would wait for it and
+    // the items' LDS round trips would add up.
     auto decode_v8 = [&](int c) {
         const uint8_t* src = smem + (c % NS) * ST_STAGE + 2 * ST_PAGE;
         uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
-        if constexpr (DECH) {
-            if (w & 2) {
+        // items it0, it0 + step, ... (N of them, those below 4D real)
+        auto run = [&](int it0, int step, auto n_tag, auto full_tag) {
+            constexpr int N = decltype(n_tag)::value;
+            constexpr bool FULL = decltype(full_tag)::value;  // every item below 4D
+            uint2 w8[N];
 #pragma unroll
-                for (int i = 0; i < 4 * D / 256; ++i) v8_item(src, dst, dec_id + 256 * i);
+            for (int i = 0; i < N; ++i) {
+                const int it = it0 + step * i;
+                if (FULL || it < 4 * D) {
+                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+                    w8[i] = *reinterpret_cast<const uint2*>(src + pg * ST_PAGE + d * 16 + 8 * h);
+                }
             }
-            return;
-        }
 #pragma unroll
-        for (int i = 0; i < (4 * D + kSweepThreads - 1) / kSweepThreads; ++i) {
-            const int it = tid + kSweepThreads * i;
-            if ((4 * D) % kSweepThreads != 0 && it >= 4 * D) break;
-            v8_item(src, dst, it);
+            for (int i = 0; i < N; ++i) {
+                const int it = it0 + step * i;
+                if (FULL || it < 4 * D) {
+                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+                    *reinterpret_cast<bf16x8_t*>(dst + pg * BF_PAGE + 512 * (d >> 4) +
+                                                 16 * (d & 15) + 256 * h) =
+                        e4m3x8_to_bf16(w8[i].x, w8[i].y);
+                }
+            }
+        };
+        if constexpr (DECH) {
+            if (w & 2)
+                run(dec_id, 256, std::integral_constant<int, 4 * D / 256>{}, std::true_type{});
+        } else {
+            run(tid, kSweepThreads,
+                std::integral_constant<int, (4 * D + kSweepThreads - 1) / kSweepThreads>{},
+                std::integral_constant<bool, (4 * D) % kSweepThreads == 0>{});
         }
     };
 
@@ -507,31 +524,46 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // Straight-line (4D / 512 items per thread, or 4D / 256 on the waves of
     // SIMDs 2 and 3 with DECH), so that a row-tile wave can run it between its
     // score MFMAs and the softmax and the two overlap.
-    auto v4_item = [&](const uint8_t* src, uint8_t* dst, int it) {
-        const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-        const uint32_t w4 = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
-        const uint2 sb = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) + (d >> 5) * 16 + 8 * h);
-        const u32x4 o = {e2m1x2_two_scales<0>(w4, sb.x & 0xFFu, (sb.x >> 8) & 0xFFu),
-                         e2m1x2_two_scales<1>(w4, (sb.x >> 16) & 0xFFu, sb.x >> 24),
-                         e2m1x2_two_scales<2>(w4, sb.y & 0xFFu, (sb.y >> 8) & 0xFFu),
-                         e2m1x2_two_scales<3>(w4, (sb.y >> 16) & 0xFFu, sb.y >> 24)};
-        *reinterpret_cast<u32x4*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) + 256 * h) = o;
-    };
     auto decode_v4 = [&](int c) {
         const uint8_t* src = smem + (c % NS) * ST_STAGE;
         uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
-        if constexpr (DECH) {
-            if (w & 2) {
+        auto run = [&](int it0, int step, auto n_tag, auto full_tag) {
+            constexpr int N = decltype(n_tag)::value;
+            constexpr bool FULL = decltype(full_tag)::value;  // every item below 4D
+            uint32_t w4[N];
+            uint2 sb[N];
 #pragma unroll
-                for (int i = 0; i < 4 * D / 256; ++i) v4_item(src, dst, dec_id + 256 * i);
+            for (int i = 0; i < N; ++i) {
+                const int it = it0 + step * i;
+                if (FULL || it < 4 * D) {
+                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+                    w4[i] = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
+                    sb[i] = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) +
+                                                            (d >> 5) * 16 + 8 * h);
+                }
             }
-            return;
-        }
 #pragma unroll
-        for (int i = 0; i < (4 * D + kSweepThreads - 1) / kSweepThreads; ++i) {
-            const int it = tid + kSweepThreads * i;
-            if ((4 * D) % kSweepThreads != 0 && it >= 4 * D) break;
-            v4_item(src, dst, it);
+            for (int i = 0; i < N; ++i) {
+                const int it = it0 + step * i;
+                if (FULL || it < 4 * D) {
+                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
+                    const uint2 b = sb[i];
+                    const u32x4 o = {e2m1x2_two_scales<0>(w4[i], b.x & 0xFFu, (b.x >> 8) & 0xFFu),
+                                     e2m1x2_two_scales<1>(w4[i], (b.x >> 16) & 0xFFu, b.x >> 24),
+                                     e2m1x2_two_scales<2>(w4[i], b.y & 0xFFu, (b.y >> 8) & 0xFFu),
+                                     e2m1x2_two_scales<3>(w4[i], (b.y >> 16) & 0xFFu, b.y >> 24)};
+                    *reinterpret_cast<u32x4*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) +
+                                              256 * h) = o;
+                }
+            }
+        };
+        if constexpr (DECH) {
+            if (w & 2)
+                run(dec_id, 256, std::integral_constant<int, 4 * D / 256>{}, std::true_type{});
+        } else {
+            run(tid, kSweepThreads,
+                std::integral_constant<int, (4 * D + kSweepThreads - 1) / kSweepThreads>{},
+                std::integral_constant<bool, (4 * D) % kSweepThreads == 0>{});
         }
     };
 
