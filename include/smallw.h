@@ -170,11 +170,14 @@ size_t small_w_attention_workspace_bytes(const smallw_plan* plan);
  * is split, the log-sum-exp combine kernel.  No host synchronisation and no
  * allocation, so the call can be captured in a HIP graph.  All pointers are
  * device pointers in the layouts above; k_scale / v_scale (fp32 for fp8,
- * E8M0 bytes for MXFP4) are required for those formats and ignored for bf16.  workspace must be 256-byte aligned and hold
+ * E8M0 bytes for MXFP4) are required for those formats and ignored for
+ * bf16.  workspace must be 256-byte aligned and hold
  * small_w_attention_workspace_bytes(plan) bytes (may be NULL when that is 0);
  * it is scratch owned by the caller and may be reused between calls on the
- * same stream.  Returns SMALLW_EINVAL (null pointer / plan), SMALLW_EWORKSPACE,
- * or SMALLW_EDEVICE (launch failure).
+ * same stream.  A plan is immutable and may be shared by threads and streams;
+ * calls that overlap (other streams) need their own workspace and outputs.
+ * Returns SMALLW_EINVAL (null pointer / plan), SMALLW_EWORKSPACE, or
+ * SMALLW_EDEVICE (launch failure).
  */
 int small_w_attention_run(const smallw_plan* plan, const void* q, const void* k_pool,
                           const void* v_pool, const void* k_scale, const void* v_scale,

@@ -95,3 +95,30 @@ def test_graph_replays_follow_the_device_lengths(kv):
             torch.cuda.synchronize()
             o, l = _result(d)
             check(wl, o, l, *oracle.attention(wl), o_max_abs=few_key_tolerance(wl))
+
+
+def test_calls_on_two_streams_overlap_safely():
+    """One plan shared by two streams, each call with its own workspace and
+    outputs, plus a second plan of another format on a third stream; all
+    enqueued interleaved, then checked against the oracle."""
+    wa = _workload("bf16")
+    wb = _workload("fp8", causal=False)
+    da, da2, db = dv.upload(wa), dv.upload(wa), dv.upload(wb)
+    pa, pb = _plan(wa, HOST), _plan(wb, HOST)
+    wsa, wsa2, wsb = dv.workspace_for(pa), dv.workspace_for(pa), dv.workspace_for(pb)
+    for d, w in ((da, wa), (da2, wa), (db, wb)):
+        d["seq_lens"].copy_(torch.from_numpy(np.asarray(HOST, dtype=np.int32)))
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    torch.cuda.synchronize()
+    announce("three streams, two plans, separate workspaces")
+    for _ in range(5):
+        for s, (pl, d, ws) in zip(streams, ((pa, da, wsa), (pa, da2, wsa2), (pb, db, wsb))):
+            with torch.cuda.stream(s):
+                dv.run(pl, d, ws)
+    torch.cuda.synchronize()
+    for d, w in ((da, wa), (da2, wa), (db, wb)):
+        wl = dataclasses.replace(w, seq_lens=np.asarray(HOST, dtype=np.int32))
+        o, l = _result(d)
+        check(wl, o, l, *oracle.attention(wl), o_max_abs=few_key_tolerance(wl))
+    np.testing.assert_array_equal(da["out"].view(torch.int16).cpu().numpy(),
+                                  da2["out"].view(torch.int16).cpu().numpy())
