@@ -59,6 +59,8 @@ def test_every_kernel_is_present(asm):
     # bf16, fp8 and MXFP4 sweeps at D = 64 / 128 / 256 (no MXFP4 at D = 64); the
     # 8- and 4-bit ones in both V-decode placements
     assert sum("sweep_kernel" in n for n in names) == 3 + 2 * 3 + 2 * 2
+    # the combine with clamped and with skipped loads, at D = 64 / 128 / 256
+    assert sum("combine_kernel" in n for n in names) == 2 * 3
     assert any("append_kernel" in n for n, _ in kernels(asm["append.hip"]))
 
 
