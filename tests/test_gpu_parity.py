@@ -177,6 +177,42 @@ def test_empty_request_in_batch():
     check(w, o, l, *oracle.attention(w))
 
 
+@pytest.mark.parametrize("kv,force", [("bf16", 0), ("bf16", 3), ("fp8", 0), ("fp8", 5),
+                                      ("mxfp4", 2)])
+def test_largest_batch(kv, force):
+    """The most requests one call takes (SMALLW_MAX_REQS = 256), with ragged
+    contexts of 0..600 keys and eight empty requests.  The plans have 520 work
+    units, and 1002 to 2406 with forced splits: up to several times what the GPU
+    holds at once, so the grid runs in rounds."""
+    P, W = 256, 4
+    rng = np.random.default_rng(977)
+    seq = rng.integers(0, 601, size=P) + W
+    seq[rng.choice(P, size=8, replace=False)] = 0
+    npg = int(sum(-(-int(L) // 16) for L in seq))
+    w = make_workload(None, P=P, Hq=8, Hkv=2, D=128, ctx=tuple([0] * P), W=W, causal=True,
+                      kv=kv, placement="permuted", pool_pages=npg + 11, seed=978,
+                      seq_lens=tuple(int(L) for L in seq))
+    announce(f"largest batch: P={P} {kv} force={force}")
+    o, l = gpu_run(w, force_splits=force)
+    empty = seq == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
+    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_most_rows_at_the_largest_head_dim(kv, causal):
+    """W * G = 128 rows per KV head (eight 16-row tiles, one per wave) at
+    D = 256, the largest register and LDS footprint, with a ragged pair of
+    requests and forced splits."""
+    w = make_workload(None, P=2, Hq=8, Hkv=1, D=256, ctx=(40, 900), W=16, causal=causal,
+                      kv=kv, placement="permuted", pool_pages=70, seed=979)
+    for force in (0, 3):
+        announce(f"W*G=128 D=256 {kv} causal={causal} force={force}")
+        o, l = gpu_run(w, force_splits=force)
+        check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+
+
 # ------------------------------------------------------------------ invariants
 def test_page_relabelling_is_bitwise_invariant():
     w = make_workload(None, P=2, Hq=24, Hkv=4, D=256, ctx=(700, 333), W=16, causal=True,
