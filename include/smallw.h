@@ -140,10 +140,15 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  *   seq_lens_host  host int32 [P]: L_p >= 0, L_p <= 16*max_pages_per_req, and
  *                  for causal calls L_p == 0 or L_p >= W.
  *   out            receives a new plan; release it with ..._plan_destroy.
- * Splits: n_p = ceil(L_p/16) pages; slots = num_cus * (1 if D == 256 else 2)
- * (work units resident per compute unit); S_p = max(1, min(floor(n_p * slots /
- * (Hkv * sum_q n_q)), floor(n_p / 8))) (or min(force_splits, n_p)), S_p = 1 for
- * an empty request.  Work unit
+ * Splits: n_p = ceil(L_p/16) pages, n_eff of them streamed (fewer with a
+ * sliding window); slots = num_cus * (1 if D == 256 else 2) (work units
+ * resident per compute unit); a round holds max(1, floor(slots / Hkv)) splits.
+ * S_p = 1 for an empty request, min(force_splits, n_eff) when forced, else
+ * apportioned: every request starts at one split, and one more at a time goes
+ * to the request with the most pages per split (n_eff / S_p; the lower index on
+ * ties) that keeps 8 pages a split, until the splits reach the budget: one
+ * round when P fits in it (no second round), else P plus one round.  This
+ * makes the largest split as small as the budget allows.  Work unit
  * u = unit_off[p] + kvh*S_p + s covers pages [floor(s n/S), floor((s+1) n/S)).
  * Row-exact mode (split_pages = B > 0): S_p = max(1, ceil(n_p / B)) and split
  * s covers pages [s*B, min((s+1)*B, n_p)) (the last split takes every page up

@@ -16,6 +16,7 @@ Everything here is restated from written definitions, in plain Python/numpy:
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -43,13 +44,16 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
     n_pg(p)     = ceil(L_p / 16);  n_lo(p) = first page any row needs (0 without a
                   sliding window);  n_eff(p) = n_pg - n_lo  pages streamed
     slots       = num_cus * (1 if D == 256 else 2)          units resident per CU
-    total       = Hkv * sum_p n_eff(p)
+    round       = max(1, floor(slots / Hkv))     splits that one round of units holds
     S_p         = 1                          if n_pg(p) == 0
                 = ceil(n_pg/B) - floor(n_lo/B) if split_pages = B > 0 (row-exact mode)
                 = min(force_splits, n_eff)   if force_splits > 0
-                = max(1, min(floor(n_eff * slots / total), floor(n_eff / 8)))
-                  otherwise (a request's share of the slots, at least 8 pages a split;
-                  the floors keep sum_p Hkv*S_p <= slots whenever P*Hkv <= slots)
+                  otherwise apportioned: every request starts with one split; then,
+                  while the splits number fewer than the budget (round if P <= round,
+                  so one round and no second; else P + round), the request with the
+                  most pages per split, n_eff / S_p, gets one more (the lowest index
+                  among equals), as long as that leaves it 8 pages a split
+                  (S_p < floor(n_eff / 8)); stop early when no request may grow
     unit_off[p] = Hkv * sum_{q<p} S_q;  unit u = unit_off[p] + kvh*S_p + s
     split s covers pages n_lo + [floor(s*n_eff/S), floor((s+1)*n_eff/S)), or in
     row-exact mode the s-th piece of the absolute grid [k*B, (k+1)*B), the last
@@ -62,7 +66,6 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
     n_lo = [first_page(L, W, causal, window_left) for L in seq]
     n_eff = [n - lo for n, lo in zip(n_pg, n_lo)]
     slots = num_cus * (1 if D == 256 else 2)
-    total = Hkv * sum(n_eff)
     splits = []
     for n, lo, ne in zip(n_pg, n_lo, n_eff):
         if n == 0:
@@ -72,7 +75,20 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
         elif force_splits > 0:
             splits.append(min(force_splits, ne))
         else:
-            splits.append(max(1, min((ne * slots) // total, ne // PLAN_MIN_PAGES)))
+            splits.append(1)            # apportioned below
+    if split_pages == 0 and force_splits == 0:
+        rnd = max(1, slots // Hkv)
+        budget = rnd if P <= rnd else P + rnd
+        while sum(splits) < budget:
+            may_grow = [p for p in range(P)
+                        if n_pg[p] > 0 and splits[p] < max(1, n_eff[p] // PLAN_MIN_PAGES)]
+            if not may_grow:
+                break
+            best = may_grow[0]
+            for p in may_grow[1:]:
+                if Fraction(n_eff[p], splits[p]) > Fraction(n_eff[best], splits[best]):
+                    best = p
+            splits[best] += 1
     unit_off = [0]
     for s in splits:
         unit_off.append(unit_off[-1] + Hkv * s)

@@ -3,22 +3,32 @@
 // The pages name key splitting with a reduce step ("ChunkedSmallT re-streams
 // full KV per query chunk", section Finding) and a capacity function that
 // throws past the tile width (section Why no PR yet); they give no formula.
-// This planner gives each request a share of the GPU's resident work-unit
-// slots proportional to its pages, so one call fills the compute units once
-// without a second round, with at least 8 pages per split so the per-split
-// pipeline start and the partial traffic stay small against the KV stream:
-//   n_p   = ceil(L_p / 16)
+// A call ends with its longest work unit, so this planner hands the splits of
+// one round of resident work-unit slots to the requests so that the largest
+// pages-per-split is as small as it can be, with at least 8 pages per split so
+// the per-split pipeline start and the partial traffic stay small against the
+// KV stream:
+//   n_p   = ceil(L_p / 16), n_eff = pages streamed (n_p less a window's skip)
 //   slots = num_cus * (1 if D == 256 else 2)   (units resident per CU: a D=256
 //           unit needs one CU's VGPRs and LDS; smaller heads fit two)
-//   S_p   = 1 (empty request) | min(force_splits, n_p) |
-//           max(1, min(floor(n_p * slots / (Hkv * sum_q n_q)), floor(n_p / 8)))
+//   round = max(1, floor(slots / Hkv))         (splits one round of units holds)
+//   S_p   = 1 (empty request) | min(force_splits, n_eff) | apportioned:
+//           every request starts at 1; while sum S < budget, the request with
+//           the largest n_eff / S_p (ties: the lower index) whose next split
+//           keeps 8 pages (S_p < floor(n_eff / 8)) gets one more.  budget =
+//           round when P <= round (one round, no second), else P + round.
 //   unit  u = unit_off[p] + kvh*S_p + s,  pages [floor(s n/S), floor((s+1) n/S))
+// Giving each next split to the largest pages-per-split (the D'Hondt
+// apportionment) minimises the largest n_eff / S_p for every total: a
+// proportional share with floors can leave it up to twice as large.
 // Row-exact mode (split_pages = B > 0): S_p = max(1, ceil(n_p / B)), split s covers [s B, min((s+1) B, n_p)),
 // and every row goes through the combine, so split boundaries sit at fixed
 // page indices whatever W, P or the other lengths are.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "plan_internal.h"
 
@@ -27,6 +37,32 @@ namespace {
 constexpr int kMinPagesPerSplit = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Automatic split counts (S starts at 1 for every request): one split at a time
+// to the request with the most streamed pages per split, ties to the lower
+// index, while the budget lasts and the split keeps kMinPagesPerSplit pages.
+void apportion(const std::vector<int64_t>& ne, int64_t budget, std::vector<int64_t>& S) {
+    const int P = int(ne.size());
+    auto cap = [&](int p) { return std::max<int64_t>(1, ne[p] / kMinPagesPerSplit); };
+    // heap order: a below b when ne[a]/S[a] < ne[b]/S[b], or equal and a > b
+    auto below = [&](int a, int b) {
+        const int64_t l = ne[a] * S[b], r = ne[b] * S[a];
+        return l != r ? l < r : a > b;
+    };
+    std::vector<int> heap;
+    for (int p = 0; p < P; ++p)
+        if (ne[p] > 0 && S[p] < cap(p)) heap.push_back(p);
+    std::make_heap(heap.begin(), heap.end(), below);
+    for (int64_t used = P; used < budget && !heap.empty(); ++used) {
+        std::pop_heap(heap.begin(), heap.end(), below);
+        const int p = heap.back();
+        heap.pop_back();
+        if (++S[p] < cap(p)) {
+            heap.push_back(p);
+            std::push_heap(heap.begin(), heap.end(), below);
+        }
+    }
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -76,27 +112,25 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
         pl->seq.assign(seq, seq + P);
         pl->npg.resize(P);
         pl->nlo.resize(P);
-        int64_t total = 0;
+        std::vector<int64_t> ne(P), Sv(P, 1);
         for (int p = 0; p < P; ++p) {
             pl->npg[p] = int32_t(ceil_div(seq[p], SMALLW_PAGE_SIZE));
             pl->nlo[p] = int32_t(smallw::first_page(seq[p], in.window, in.causal, in.window_left));
-            total += pl->npg[p] - pl->nlo[p];
+            const int64_t n = pl->npg[p], lo = pl->nlo[p];
+            ne[p] = n - lo;
+            if (n == 0) Sv[p] = 1;
+            else if (in.split_pages > 0) Sv[p] = ceil_div(n, in.split_pages) - lo / in.split_pages;
+            else if (in.force_splits > 0) Sv[p] = std::min<int64_t>(in.force_splits, ne[p]);
         }
-        total *= Hkv;
-        const int64_t slots = int64_t(in.num_cus) * (D == 256 ? 1 : 2);
+        if (in.split_pages == 0 && in.force_splits == 0) {
+            const int64_t slots = int64_t(in.num_cus) * (D == 256 ? 1 : 2);
+            const int64_t round = std::max<int64_t>(1, slots / Hkv);
+            apportion(ne, P <= round ? round : P + round, Sv);
+        }
         pl->splits.resize(P);
         pl->unit_off.assign(P + 1, 0);
         for (int p = 0; p < P; ++p) {
-            const int64_t n = pl->npg[p], lo = pl->nlo[p], ne = n - lo;
-            int64_t S;
-            if (n == 0) S = 1;
-            else if (in.split_pages > 0) S = ceil_div(n, in.split_pages) - lo / in.split_pages;
-            else if (in.force_splits > 0) S = in.force_splits < ne ? in.force_splits : ne;
-            else {
-                S = ne * slots / total;                      // share of the slots (floor)
-                if (S > ne / kMinPagesPerSplit) S = ne / kMinPagesPerSplit;
-                if (S < 1) S = 1;
-            }
+            const int64_t n = pl->npg[p], lo = pl->nlo[p], S = Sv[p];
             pl->splits[p] = int32_t(S);
             if (S > 1) pl->any_split = true;
             const int64_t next = int64_t(pl->unit_off[p]) + Hkv * S;

@@ -11,8 +11,10 @@
 * numbers the pages print (tests/golden/).
 """
 import dataclasses
+import itertools
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -477,21 +479,65 @@ def test_plan_partitions_every_request_into_balanced_splits():
 
 
 def test_plan_at_the_long_context_shapes():
-    # 64K verify: total = 4*4097 = 16388 page-heads, 256 slots (D=256: one per
-    # CU) -> S = floor(4097*256/16388) = 64 -> 256 units, one per compute unit.
+    # 64K verify: 256 slots (D=256: one per CU), 4 heads -> a round holds 64
+    # splits, all for the one request (floor(4097/8) = 512 does not bind) ->
+    # 256 units, one per compute unit.
     pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[65552], num_cus=256)
     assert pl["splits"] == [64] and pl["U"] == 256
-    # 16K verify: S = floor(1025*256/4100) = 64, and floor(1025/8) = 128 does not bind
+    # 16K verify: the same 64, and floor(1025/8) = 128 does not bind
     pl = oracle.plan(P=1, Hkv=4, D=256, kv_fp8=False, seq_lens=[16400], num_cus=256)
     assert pl["splits"] == [64]
-    # fp8 batch: pages 513/1025/2049/4097 (sum 7684), 4 heads, 256 slots ->
-    # floor(n*256/30736) = 4, 8, 17, 34 -> 252 units, no second round
+    # fp8 batch: pages 513/1025/2049/4097, 64 splits.  Pages per split at most
+    # x needs S_p >= n_p / x: x = 4097/33 = 124.15 needs 5 + 9 + 17 + 33 = 64
+    # splits, and any x below it needs S_4 = 34 and still 5 + 9 + 17, 65 in all.
+    # So [5, 9, 17, 33] is the one allocation with the smallest largest split.
     pl = oracle.plan(P=4, Hkv=4, D=256, kv_fp8=True, seq_lens=[8208, 16400, 32784, 65552],
                      num_cus=256)
-    assert pl["splits"] == [4, 8, 17, 34] and pl["U"] == 252
+    assert pl["splits"] == [5, 9, 17, 33] and pl["U"] == 256
     # tiny: 17 pages, one head, 512 slots (D=64) -> the 8-page floor: floor(17/8) = 2
     pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256)
     assert pl["splits"] == [2] and [u[3:] for u in pl["units"]] == [(0, 8), (8, 17)]
+
+
+def test_plan_minimises_the_largest_split_by_brute_force():
+    """On tiny problems, the automatic split counts reach the smallest possible
+    largest pages-per-split over every allocation that fits the budget (found by
+    enumeration), and they spend the budget while any request may still grow."""
+    rng = np.random.default_rng(17)
+    checked = 0
+    for trial in range(300):
+        P = int(rng.integers(1, 5))
+        Hkv = int(rng.choice([1, 2]))
+        cus = int(rng.integers(1, 7))
+        seq = [int(x) for x in rng.integers(0, 16 * 70, size=P)]
+        pl = oracle.plan(P=P, Hkv=Hkv, D=256, kv_fp8=False, seq_lens=seq, num_cus=cus)
+        n = [-(-L // 16) for L in seq]
+        cap = [max(1, x // 8) if x > 0 else 1 for x in n]
+        rnd = max(1, cus // Hkv)
+        budget = rnd if P <= rnd else P + rnd
+        best = None
+        for S in itertools.product(*[range(1, c + 1) for c in cap]):
+            if sum(S) <= budget:
+                worst = max(Fraction(a, b) for a, b in zip(n, S))
+                best = worst if best is None or worst < best else best
+        got = pl["splits"]
+        assert all(1 <= g <= c for g, c in zip(got, cap))
+        assert max(Fraction(a, b) for a, b in zip(n, got)) == best, (seq, cus, Hkv, got)
+        assert sum(got) == min(budget, sum(cap)), (seq, cus, Hkv, got)
+        checked += 1
+    assert checked == 300
+
+
+def test_plan_with_more_requests_than_one_round_holds():
+    # 2 slots, one head: a round holds 2 splits; 5 requests exceed it, so the
+    # budget is 5 + 2 = 7.  Request 0 has 100 pages (up to 12 splits), the others
+    # 8 pages (one split each): both extra splits go to request 0 -> [3, 1, 1, 1, 1].
+    pl = oracle.plan(P=5, Hkv=1, D=256, kv_fp8=False, seq_lens=[1600, 128, 128, 128, 128],
+                     num_cus=2)
+    assert pl["splits"] == [3, 1, 1, 1, 1] and pl["U"] == 7
+    # equal requests take the extra splits in index order: 4 x 64 pages, 3 slots -> [2, 2, 2, 1]
+    pl = oracle.plan(P=4, Hkv=1, D=256, kv_fp8=False, seq_lens=[1024] * 4, num_cus=3)
+    assert pl["splits"] == [2, 2, 2, 1]
 
 
 def test_row_exact_plan_splits_at_fixed_page_multiples():
