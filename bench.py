@@ -115,7 +115,7 @@ def main():
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) into the traffic record the roofline block reads")
     ap.add_argument("--profile-workload", metavar="NAME",
-                    help="only run NAME (tiny, verify16k, verify64k, draft, fp8, fp4_16k, fp4_64k; W from "
+                    help="only run NAME (tiny, verify16k, verify64k, draft, fp8, fp4_16k, fp4_64k, mixed; W from "
                          "--profile-window) --steps times, each after a cold flush, for "
                          "counter collection; prints nothing else")
     ap.add_argument("--profile-window", type=int, default=None)
@@ -257,6 +257,7 @@ def main():
                  ("verify16k W=1", dict(name="verify16k", W=1)),
                  ("draft P=8 W=9 non-causal", dict(name="draft")),
                  ("fp8 P=4 8K..64K W=16", dict(name="fp8")),
+                 ("mixed P=16 100..24K W=16", dict(name="mixed")),
                  ("MXFP4 16K W=16", dict(name="fp4_16k", W=16)),
                  ("MXFP4 16K W=8", dict(name="fp4_16k", W=8)),
                  ("MXFP4 16K W=1", dict(name="fp4_16k", W=1)),

@@ -142,6 +142,18 @@ def test_draft_block_batched():
     check(w, o, l, *oracle.attention(w))
 
 
+def test_mixed_length_batch():
+    """16 requests of 100..24K keys in the launch configuration bench.py times
+    (apportioned splits: 1 to 7 per request), three heads sampled per row."""
+    w = make_workload("mixed")
+    announce(f"mixed P=16 lengths {list(w.seq_lens)} (sampled rows)")
+    o, l = gpu_run(w)
+    rows = sampled_rows(w, [0, 13, 31])
+    ro, rl = oracle.attention(w, rows=np.array(rows))
+    check(w, o, l, ro, rl, rows=rows)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
 # ------------------------------------------------------------------ edge shapes
 EDGE = [
     dict(P=1, Hq=4, Hkv=1, D=64, ctx=(0,), W=4, causal=True),          # L == W: one page

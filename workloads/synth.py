@@ -58,6 +58,11 @@ CONFIGS = {
     # the same at 64K context, pages a seeded permutation of a 5000-page pool
     "fp4_64k": dict(P=1, Hq=24, Hkv=4, D=256, ctx=(65536,), W=16, causal=True, kv="mxfp4",
                     placement="permuted", pool_pages=5000),
+    # a mixed-length verify batch: 16 requests, contexts ~ U[100, 24000], W=16
+    # causal, 32 q / 8 KV heads, D 128, bf16, pages a seeded permutation of the
+    # pool (the varlen batching the split planner has to balance)
+    "mixed": dict(P=16, Hq=32, Hkv=8, D=128, ctx=("uniform", 100, 24000), W=16, causal=True,
+                  kv="bf16", placement="permuted", pool_pages=None),
 }
 
 CONFIG_SEED_BASE = 20261202
