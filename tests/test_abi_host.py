@@ -142,6 +142,28 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         assert sw.small_w_attention_workspace_bytes(plan) == want
 
 
+def test_plan_export_matches_oracle_on_large_batches():
+    """Batches of 64..256 requests (the request limit), with repeated lengths so
+    the apportionment meets many equal pages-per-split ties, one round or more."""
+    rng = np.random.default_rng(2025)
+    for trial in range(24):
+        P = int(rng.choice([64, 200, 256]))
+        Hkv = int(rng.choice([1, 2, 8]))
+        D = int(rng.choice([128, 256]))
+        cus = int(rng.choice([8, 80, 256]))
+        seq = rng.choice([0, 16, 160, 1600, 16000, int(rng.integers(1, 30000))], size=P)
+        seq = seq.astype(np.int32)
+        maxp = int(-(-int(seq.max()) // 16)) or 1
+        pr = B.make_problem(num_reqs=P, window=1, num_q_heads=Hkv, num_kv_heads=Hkv,
+                            head_dim=D, num_pages=100000, max_pages_per_req=maxp, causal=0,
+                            kv_dtype=0, num_cus=cus)
+        plan = sw.small_w_attention_plan(pr, seq)
+        pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=False, seq_lens=seq, num_cus=cus, W=1,
+                         causal=False)
+        np.testing.assert_array_equal(sw.small_w_attention_plan_export(plan),
+                                      oracle.plan_export(pl, R=1))
+
+
 def test_run_rejects_null_pointers_and_bad_workspace_before_any_launch():
     pr = base_problem(force_splits=3)
     plan = sw.small_w_attention_plan(pr, [260])
