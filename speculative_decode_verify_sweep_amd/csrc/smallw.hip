@@ -158,16 +158,29 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-__device__ __forceinline__ float wave_max_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) by the
+// VALU lane swaps: swapping a register with itself across 16-lane rows (or
+// 32-lane halves) leaves every lane its own value in one result and its
+// partner's in the other, so a commutative max or sum of the pair is the
+// butterfly step with no LDS permute on the path.
+__device__ __forceinline__ float pair16(float x, bool take_max) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    const float a = __uint_as_float(s[0]), b = __uint_as_float(s[1]);
+    return take_max ? fmaxf(a, b) : a + b;
 }
 
+__device__ __forceinline__ float pair32(float x, bool take_max) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    const float a = __uint_as_float(s[0]), b = __uint_as_float(s[1]);
+    return take_max ? fmaxf(a, b) : a + b;
+}
+
+__device__ __forceinline__ float wave_max_groups(float x) { return pair32(pair16(x, true), true); }
+
 __device__ __forceinline__ float wave_sum_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    return pair32(pair16(x, false), false);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {

@@ -7,6 +7,10 @@
 * M0 is written only by the DMA statements (an M0 write, its wait state and
   the LDS DMA load that reads it), so the inline asm that sets M0 without
   declaring it clobbered cannot overwrite a value the compiler keeps there.
+* The softmax's reductions across the four 16-lane groups use the VALU lane
+  swaps, not LDS permutes: every sweep has v_permlane16_swap and
+  v_permlane32_swap, and the bf16 sweeps no ds_bpermute at all (the 8- and
+  4-bit ones keep a few in their Q quantisation, before the loop).
 """
 import os
 import re
@@ -93,3 +97,14 @@ def test_m0_written_only_by_the_dma_statements(asm):
                 assert i.startswith("s_mov_b32 m0,"), (name, i)
                 assert ins[k + 1] == "s_nop 0", (name, ins[k:k + 3])
                 assert ins[k + 2].startswith("global_load_lds_dword"), (name, ins[k:k + 3])
+
+
+def test_group_reductions_use_lane_swaps(asm):
+    for name, body in kernels(asm["smallw.hip"]):
+        if "sweep_kernel" not in name:
+            continue
+        ins = [i.split()[0] for i in instructions(body)]
+        assert any(i.startswith("v_permlane16_swap_b32") for i in ins), name
+        assert any(i.startswith("v_permlane32_swap_b32") for i in ins), name
+        if "ELi4ELi0E" in name:     # bf16 sweeps: <D, 4, 0, false>
+            assert not any(i.startswith("ds_bpermute") for i in ins), name
