@@ -1021,6 +1021,21 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 // both are in flight together (one memory round trip when S <= 64).  The
 // waves' sums meet in LDS in a fixed order: repeated calls are bitwise equal.
 // ----------------------------------------------------------------------------
+// Value of another lane of the same 16-lane row, by DPP: step 0 rotates the
+// row by 8, step 1 by 4, step 2 swaps lanes at distance 2 in each quad, step 3
+// at distance 1 (dpp_ctrl row_ror:8, row_ror:4, quad_perm [2,3,0,1], [1,0,3,2]).
+__device__ __forceinline__ float dpp_row_step(float x, int step) {
+    const int v = __float_as_int(x);
+    int r;
+    switch (step) {
+        case 0: r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false); break;
+        case 1: r = __builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false); break;
+        case 2: r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); break;
+        default: r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); break;
+    }
+    return __int_as_float(r);
+}
+
 __device__ __forceinline__ void lse_fold(float& m, float& sm, float v) {
     if (v == -INFINITY) return;
     if (v > m) {
@@ -1098,9 +1113,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params a) {
             if (pj + 16 * q < S) lse_fold(m, sm, rv[q].x);
         for (int s = pj + BATCH; s < S; s += 16) lse_fold(m, sm, prow[s].x);
     }
+    // merge the row's 16 lanes with DPP moves inside each 16-lane row (VALU,
+    // no LDS permute): rotate by 8 (the lane l^8), by 4, then swap lane pairs
+    // at distance 2 and 1 within quads.  The merge is commutative, so after
+    // each step the lanes that hold the same set of records agree bitwise, and
+    // after the last one all 16 do.
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
+    for (int step = 0; step < 4; ++step) {
+        const float m2 = dpp_row_step(m, step), s2 = dpp_row_step(sm, step);
         const float mn = fmaxf(m, m2);
         if (mn != -INFINITY) {
             sm = (m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f(m - mn)) +

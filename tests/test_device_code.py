@@ -10,7 +10,9 @@
 * The softmax's reductions across the four 16-lane groups use the VALU lane
   swaps, not LDS permutes: every sweep has v_permlane16_swap and
   v_permlane32_swap, and the bf16 sweeps no ds_bpermute at all (the 8- and
-  4-bit ones keep a few in their Q quantisation, before the loop).
+  4-bit ones keep a few in their Q quantisation, before the loop).  The
+  combine merges each row's 16 lanes with DPP row moves, also without LDS
+  permutes.
 """
 import os
 import re
@@ -108,3 +110,13 @@ def test_group_reductions_use_lane_swaps(asm):
         assert any(i.startswith("v_permlane32_swap_b32") for i in ins), name
         if "ELi4ELi0E" in name:     # bf16 sweeps: <D, 4, 0, false>
             assert not any(i.startswith("ds_bpermute") for i in ins), name
+
+
+def test_combine_merges_rows_with_dpp(asm):
+    for name, body in kernels(asm["smallw.hip"]):
+        if "combine_kernel" not in name:
+            continue
+        ins = list(instructions(body))
+        assert not any(i.startswith("ds_bpermute") for i in ins), name
+        assert sum("row_ror:8" in i for i in ins) >= 2, name
+        assert sum("row_ror:4" in i for i in ins) >= 2, name
