@@ -46,10 +46,38 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __builtin_bit_cast(float, uint32_t(b) << 16);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+// A DPP move inside 16-lane rows (VALU, no LDS permute): 0xB1 and 0x4E swap
+// lanes at distance 1 and 2 within each quad, 0x141 mirrors each 8-lane half,
+// 0x140 each 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned groups of N lanes (N = 2, 4, 8 or 16).  After the quad
+// swaps a lane holds its quad's max; the half mirror pairs it with a lane of
+// the other quad of its 8, the row mirror with one of the other half of its
+// 16.  max is exact and ignores NaN in any order, so the tree's shape does not
+// change the result.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));
+    if constexpr (N >= 4) x = fmaxf(x, dpp_mov<0x4E>(x));
+    if constexpr (N >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+    if constexpr (N >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
     return x;
+}
+
+// Max over the wave: 16-lane rows by DPP, then rows and halves by the VALU
+// lane swaps (a register swapped with itself leaves each lane its own value
+// and its partner's).
+__device__ __forceinline__ float wave_max(float x) {
+    x = group_max<16>(x);
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
 // One wave per (p, i, kvh); lane l owns elements [E*l, E*l + E) of the row.
@@ -117,11 +145,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
             km = fmaxf(km, fabsf(kx[e]));
             vm = fmaxf(vm, fabsf(vx[e]));
         }
-#pragma unroll
-        for (int off = 1; off < BL; off <<= 1) {
-            km = fmaxf(km, __shfl_xor(km, off));
-            vm = fmaxf(vm, __shfl_xor(vm, off));
-        }
+        km = group_max<BL>(km);
+        vm = group_max<BL>(vm);
         const int kX = mx_exponent(km), vX = mx_exponent(vm);
         uint32_t kc = 0;
         uint8_t* kp = a.k_pool + (ph * 16 + slot) * (D / 2) + (E * l) / 2;
