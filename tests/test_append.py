@@ -388,3 +388,58 @@ def test_append_then_verify_matches_oracle(kv):
     l = d["lse"].cpu().numpy().astype(np.float64)
     tol = few_key_tolerance(w2) if kv == "mxfp4" else 1e-2
     check(w2, o, l, *oracle.attention(w2), o_max_abs=tol)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
+def test_append_in_a_replayed_graph_matches_oracle_bitwise(kv):
+    """The append captured in a HIP graph, as a caller capturing a decode step
+    does (bench.py times it that way), replayed three times.  Before each replay
+    the pools go back to their state before the append and eager work runs, so a
+    replay that wrote nothing, or wrote stale values, would fail."""
+    from speculative_decode_verify_sweep_amd import device as dv
+    import speculative_decode_verify_sweep_amd as sw
+    w, kn, vn = _append_case(kv, D=256, seed=75)
+    d = dv.upload(w)
+    plan = dv.plan_for(w)
+    kt = torch.from_numpy(kn.view(np.int16)).cuda()
+    vt = torch.from_numpy(vn.view(np.int16)).cuda()
+    names = [n for n in ("k_pool", "v_pool", "k_scale", "v_scale") if d.get(n) is not None]
+    fresh = {n: d[n].clone() for n in names}
+
+    def call():
+        sw.small_w_kv_append(plan, kt, vt, d["k_pool"], d["v_pool"], d["k_scale"],
+                             d["v_scale"], d["block_table"], d["seq_lens"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                                  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    scaled = kv != "bf16"
+    kp, vp, ks, vs = oracle.kv_append(P=w.P, W=w.W, Hkv=w.Hkv, D=w.D, kv=kv, k_new_bits=kn,
+                                      v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                      k_scale=w.k_scale if scaled else None,
+                                      v_scale=w.v_scale if scaled else None,
+                                      block_table=w.block_table, seq_lens=w.seq_lens,
+                                      num_pages=w.num_pages)
+    assert not np.array_equal(host_bits(fresh["k_pool"]), kp)   # the append changes the pool
+    scratch = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        for n in names:
+            d[n].copy_(fresh[n])
+        scratch.mul_(0.5).add_(1.0)             # eager work between the replays
+        torch.cuda.synchronize()
+        print(f"[case] append {kv} graph replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(d["k_pool"]), kp)
+        np.testing.assert_array_equal(host_bits(d["v_pool"]), vp)
+        if scaled:
+            np.testing.assert_array_equal(d["k_scale"].cpu().numpy(), ks)
+            np.testing.assert_array_equal(d["v_scale"].cpu().numpy(), vs)
