@@ -45,6 +45,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def pct(xs, q):
+    """q-th percentile (0..100) of xs by linear interpolation between order statistics."""
+    ys = sorted(xs)
+    k = (len(ys) - 1) * q / 100.0
+    lo = int(k)
+    hi = min(lo + 1, len(ys) - 1)
+    return ys[lo] + (ys[hi] - ys[lo]) * (k - lo)
+
+
 def kv_bytes(seq_lens, hkv, d, kv="bf16"):
     """K and V bytes of one sweep over every visible token (the pages' GB/s
     numerator), with the scales of the 8-bit (one fp32 per token and head for
@@ -229,6 +238,7 @@ def main():
     tot16 = [r[0] for r in main_res]
     sw16 = [r[1] for r in main_res]
     us16 = statistics.median(tot16) * 1e3
+    p10_16, p90_16 = pct(tot16, 10) * 1e3, pct(tot16, 90) * 1e3
     sweep_us = statistics.mean(sw16) * 1e3
     log(f"W=16 cold: median {us16:.1f} us, mean {statistics.mean(tot16)*1e3:.1f} us, "
         f"sweep kernel mean {sweep_us:.1f} us")
@@ -359,7 +369,29 @@ def main():
     B.hip_event_destroy(e0)
     B.hip_event_destroy(e1)
 
+    # the practical read ceiling: a plain 16-byte streaming-read kernel, cold,
+    # over 1 GiB and over exactly the call's KV bytes, kernel-timestamped
     kvb = kv_bytes([CTX + 16], base.Hkv, base.D)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ceiling = {}
+    for label, nbytes in (("1GiB", 1 << 30), ("kv_bytes", kvb - kvb % 16)):
+        rbuf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        for _ in range(args.warmup):
+            flush()
+            B.small_w_stream_read(rbuf, sink)
+        ts = []
+        for _ in range(args.steps):
+            flush()
+            e0, e1 = B.hip_event_create(), B.hip_event_create()
+            B.small_w_stream_read(rbuf, sink, events=(e0, e1))
+            ts.append(B.hip_event_elapsed_ms(e0, e1) * 1e3)
+            B.hip_event_destroy(e0)
+            B.hip_event_destroy(e1)
+        med = statistics.median(ts)
+        ceiling[label] = {"bytes": nbytes, "us": round(med, 2),
+                          "GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
+        log(f"stream read {label}: {med:.1f} us, {ceiling[label]['GBps']} GB/s")
+        del rbuf
     gbps = kvb / (us16 * 1e-6) / 1e9
     sweep_gbps = kvb / (sweep_us * 1e-6) / 1e9
 
@@ -406,6 +438,11 @@ def main():
         "kv_GBps": round(gbps, 1),
         "kv_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "kv_bytes_per_call": kvb,
+        "us_p10_p90": [round(p10_16, 2), round(p90_16, 2)],
+        "stream_read_ceiling": {**ceiling, "kernel": "plain 16-byte streaming read, cold, "
+                                                    "kernel-timestamped (small_w_stream_read)"},
+        "kv_frac_of_ceiling": round(gbps / ceiling["1GiB"]["GBps"], 4),
+        "us_over_ceiling_us_same_bytes": round(us16 / ceiling["kv_bytes"]["us"], 4),
         "us_per_layer_call_by_W": {str(k): round(v, 2) for k, v in per_w.items()},
         "sweep_us_by_W": {str(k): round(v, 2) for k, v in sweep_w.items()},
         "ratio_W16_over_W1": round(us16 / per_w[1], 3) if 1 in per_w else None,

@@ -31,7 +31,8 @@
  *                                              row i sits at position L-W+i)
  *                 and j >= h - N + 1 with window_left = N > 0, h the row's
  *                 last visible key ("DFlash2 leaves the paged graph fast path
- *                 ...", section Scope, names a sliding window as its own case)
+ *                 ...", section The cost, notes that the draft path does not
+ *                 apply a window and leaves it to a separate issue)
  *   s_j = scale * <q, k_j>;  out = softmax(s) . V;  lse = ln sum_j exp(s_j)
  *   A row with no visible key (only when L == 0) gets out = 0, lse = -inf.
  *
@@ -255,6 +256,20 @@ size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan);
 int small_w_kv_append(const smallw_plan* plan, const void* k_new, const void* v_new,
                       void* k_pool, void* v_pool, void* k_scale, void* v_scale,
                       const int32_t* block_table, const int32_t* seq_lens, void* stream);
+
+/*
+ * Bandwidth reference: on `stream`, read `bytes` of device memory at `buf` once
+ * with 16-byte loads and nothing else (bytes a multiple of 16, buf 16-byte
+ * aligned).  Its bytes / time is the practical HBM read ceiling that the
+ * attention call's KV bandwidth is set against: "ChunkedSmallT re-streams full
+ * KV per query chunk", section Measurement, rates the call by one sweep's K and
+ * V bytes over its time on a cold cache.  sink: device uint32, written only for
+ * one XOR value of the data (it keeps the loads alive).  ev_start / ev_end:
+ * optional hipEvent_t handles set from the kernel dispatch itself.  Returns
+ * SMALLW_EINVAL (null, unaligned or zero size) or SMALLW_EDEVICE.
+ */
+int small_w_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream,
+                        void* ev_start, void* ev_end);
 
 /* Release a plan (NULL is allowed). */
 void small_w_attention_plan_destroy(smallw_plan* plan);

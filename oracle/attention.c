@@ -18,8 +18,9 @@
  *    never looked at); section Exactness: rows are independent.
  *  - causal verify alignment: window row i sits at absolute position
  *    L - W + i and sees keys at positions <= L - W + i (bottom-right mask).
- *  - "DFlash2 leaves the paged graph fast path ...", section Scope, lists a
- *    sliding window that a path did not apply: with window_left = N > 0 a row
+ *  - "DFlash2 leaves the paged graph fast path ...", section The cost, notes
+ *    that the draft path does not apply a window and defers it to a separate
+ *    issue.  The sliding window read here: with window_left = N > 0 a row
  *    whose last visible key is at position h sees only keys h - N + 1 .. h.
  *  - "ChunkedSmallT re-streams full KV per query chunk", section Measurement,
  *    times a 4-bit KV cache ("nvfp4") without defining it.  The 4-bit format

@@ -74,6 +74,8 @@ def lib():
         L.small_w_attention_trace_pages.restype = ctypes.c_int
         L.small_w_attention_plan_destroy.argtypes = [vp]
         L.small_w_attention_plan_destroy.restype = None
+        L.small_w_stream_read.argtypes = [vp, sz, vp, vp, vp, vp]
+        L.small_w_stream_read.restype = ctypes.c_int
         L.small_w_attention_strerror.argtypes = [ctypes.c_int]
         L.small_w_attention_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -149,13 +151,83 @@ def _stream(stream):
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check(t, name, dtypes, numel=None, min_bytes=None, device=None):
+    """Raise ValueError unless tensor t has one of `dtypes` (names such as
+    "bfloat16"), exactly `numel` elements or at least `min_bytes` bytes, and
+    sits on `device`.  Raw integer device pointers pass unchecked: the caller
+    vouches for them."""
+    if t is None or isinstance(t, int):
+        return
+    dt = str(t.dtype).replace("torch.", "")
+    if dt not in dtypes:
+        raise ValueError(f"{name}: dtype {dt}, expected {' or '.join(dtypes)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_bytes is not None and _nbytes(t) < min_bytes:
+        raise ValueError(f"{name}: {_nbytes(t)} bytes, the plan needs at least {min_bytes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device} (the current device)")
+
+
+# bf16 tensors may also arrive as 16-bit integer tensors holding the bits
+BF16_BITS = ("bfloat16", "int16", "uint16")
+
+
+def _page_head_bytes(pr) -> tuple[int, int, tuple]:
+    """(pool bytes per page-head, scale bytes per page-head, scale dtypes)."""
+    D = pr.head_dim
+    if pr.kv_dtype == SMALLW_KV_FP8_E4M3:
+        return 16 * D, 16 * 4, ("float32",)
+    if pr.kv_dtype == SMALLW_KV_MXFP4:
+        return 8 * D, 16 * (D // 32), ("uint8",)
+    return 32 * D, 0, ()
+
+
+def _check_pools(pr, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, dev):
+    pool_b, scale_b, scale_dt = _page_head_bytes(pr)
+    heads = pr.num_pages * pr.num_kv_heads
+    pool_dt = BF16_BITS if pr.kv_dtype == SMALLW_KV_BF16 else \
+        ("uint8", "int8", "float8_e4m3fn")
+    _check(k_pool, "k_pool", pool_dt, min_bytes=heads * pool_b, device=dev)
+    _check(v_pool, "v_pool", pool_dt, min_bytes=heads * pool_b, device=dev)
+    if scale_b:
+        if k_scale is None or v_scale is None:
+            raise ValueError("k_scale and v_scale are required for this KV format")
+        _check(k_scale, "k_scale", scale_dt, min_bytes=heads * scale_b, device=dev)
+        _check(v_scale, "v_scale", scale_dt, min_bytes=heads * scale_b, device=dev)
+    _check(block_table, "block_table", ("int32",), numel=pr.num_reqs * pr.max_pages_per_req,
+           device=dev)
+    _check(seq_lens, "seq_lens", ("int32",), numel=pr.num_reqs, device=dev)
+
+
+def _current_device():
+    import torch
+    return torch.device("cuda", torch.cuda.current_device())
+
+
 def small_w_attention_run(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table,
                           seq_lens, out, lse, workspace=None, stream=None, events=None) -> None:
     """Enqueue one attention call.  Tensors are device tensors in the documented
     layouts; `workspace` is a uint8 device tensor of at least
     small_w_attention_workspace_bytes(plan) bytes (or None when that is 0).
-    `events`: optional 3 raw hipEvent_t handles (ints) recorded around the kernels."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    `events`: optional 3 raw hipEvent_t handles (ints) recorded around the kernels.
+    Raises ValueError when a tensor's dtype, size or device does not fit the
+    plan (an int32 table read as int64 pairs, or a short pool, would otherwise
+    give wrong numbers or out-of-bounds reads on the device)."""
+    pr = plan.problem
+    dev = _current_device()
+    rows = pr.num_reqs * pr.window * pr.num_q_heads
+    _check(q, "q", BF16_BITS, numel=rows * pr.head_dim, device=dev)
+    _check(out, "out", BF16_BITS, numel=rows * pr.head_dim, device=dev)
+    _check(lse, "lse", ("float32",), numel=rows, device=dev)
+    _check_pools(pr, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, dev)
+    _check(workspace, "workspace", ("uint8",), device=dev)
+    ws_bytes = 0 if workspace is None else _nbytes(workspace) if not isinstance(workspace, int) \
+        else small_w_attention_workspace_bytes(plan)
     args = [plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
             _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
             _stream(stream)]
@@ -169,7 +241,16 @@ def small_w_attention_run(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block
 
 def small_w_attention_trace_pages(plan: Plan, block_table, seq_lens, pages_out,
                                   stream=None) -> None:
+    pr = plan.problem
+    dev = _current_device()
+    _check(block_table, "block_table", ("int32",), numel=pr.num_reqs * pr.max_pages_per_req,
+           device=dev)
+    _check(seq_lens, "seq_lens", ("int32",), numel=pr.num_reqs, device=dev)
     maxp = pages_out.shape[-1]
+    units = int(small_w_attention_plan_export(plan)[2])
+    _check(pages_out, "pages_out", ("int32",), numel=units * maxp, device=dev)
+    if maxp < small_w_attention_plan_max_unit_pages(plan):
+        raise ValueError("pages_out: fewer columns than the plan's largest unit")
     rc = lib().small_w_attention_trace_pages(plan.handle, _ptr(block_table), _ptr(seq_lens),
                                              _ptr(pages_out), maxp, _stream(stream))
     if rc != SMALLW_OK:
@@ -179,13 +260,32 @@ def small_w_attention_trace_pages(plan: Plan, block_table, seq_lens, pages_out,
 def small_w_kv_append(plan: Plan, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
                       block_table, seq_lens, stream=None) -> None:
     """Write the plan's W window tokens (bf16 [P][W][Hkv][D] device tensors) into
-    their pool slots, quantising to e4m3 with per-(token, KV-head) scales for an
-    fp8 or MXFP4 pool.  Tensors are device tensors in the documented layouts."""
+    their pool slots: copied for a bf16 pool, quantised to e4m3 with a
+    per-(token, KV-head) fp32 scale for an fp8 pool, or to E2M1 codes with an
+    E8M0 scale per 32 elements for an MXFP4 pool.  Tensors are device tensors
+    in the documented layouts; ValueError when one does not fit the plan."""
+    pr = plan.problem
+    dev = _current_device()
+    n_new = pr.num_reqs * pr.window * pr.num_kv_heads * pr.head_dim
+    _check(k_new, "k_new", BF16_BITS, numel=n_new, device=dev)
+    _check(v_new, "v_new", BF16_BITS, numel=n_new, device=dev)
+    _check_pools(pr, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, dev)
     rc = lib().small_w_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
                                  _ptr(seq_lens), _stream(stream))
     if rc != SMALLW_OK:
         raise SmallwError(rc, "small_w_kv_append")
+
+
+def small_w_stream_read(buf, sink, stream=None, events=None) -> None:
+    """Read the whole device tensor `buf` once with 16-byte loads (the HBM read
+    ceiling reference); `sink` is a device uint32 tensor of at least one element;
+    `events`: optional 2 raw hipEvent_t handles (start, end of the kernel)."""
+    _check(sink, "sink", ("uint32", "int32"), device=buf.device)
+    ev = events or (None, None)
+    rc = lib().small_w_stream_read(_ptr(buf), _nbytes(buf), _ptr(sink), _stream(stream), *ev)
+    if rc != SMALLW_OK:
+        raise SmallwError(rc, "small_w_stream_read")
 
 
 def small_w_attention_strerror(code: int) -> str:

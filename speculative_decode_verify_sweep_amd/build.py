@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsmallw.so")
-SOURCES = ["smallw.hip", "append.hip", "plan.cpp"]
+SOURCES = ["smallw.hip", "append.hip", "stream_read.hip", "plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

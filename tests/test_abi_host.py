@@ -230,3 +230,71 @@ def test_package_has_no_fallback_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(OSError):
         B.lib()
+
+
+def _cpu_call_tensors(pr, kv="bf16"):
+    """CPU stand-ins with the shapes and dtypes a call with problem pr takes."""
+    import torch
+    P, W, Hq, Hkv, D, n = (pr.num_reqs, pr.window, pr.num_q_heads, pr.num_kv_heads,
+                           pr.head_dim, pr.num_pages)
+    if kv == "bf16":
+        pool = torch.zeros((n, Hkv, 16, D), dtype=torch.bfloat16)
+        sc = None
+    elif kv == "fp8":
+        pool = torch.zeros((n, Hkv, 16, D), dtype=torch.uint8)
+        sc = torch.zeros((n, Hkv, 16), dtype=torch.float32)
+    else:
+        pool = torch.zeros((n, Hkv, 16, D // 2), dtype=torch.uint8)
+        sc = torch.zeros((n, Hkv, 16, D // 32), dtype=torch.uint8)
+    return dict(q=torch.zeros((P, W, Hq, D), dtype=torch.bfloat16), k_pool=pool,
+                v_pool=pool.clone(), k_scale=sc, v_scale=None if sc is None else sc.clone(),
+                block_table=torch.zeros((P, pr.max_pages_per_req), dtype=torch.int32),
+                seq_lens=torch.zeros((P,), dtype=torch.int32),
+                out=torch.zeros((P, W, Hq, D), dtype=torch.bfloat16),
+                lse=torch.zeros((P, W, Hq), dtype=torch.float32))
+
+
+@pytest.mark.parametrize("kv,code", [("bf16", 0), ("fp8", 1), ("mxfp4", 2)])
+def test_binding_rejects_tensors_that_do_not_fit_the_plan(monkeypatch, kv, code):
+    """Wrong dtypes (an int64 table, fp32 queries), wrong element counts and
+    short pools raise ValueError in the binding, before the library is called."""
+    import torch
+    monkeypatch.setattr(B, "_current_device", lambda: torch.device("cpu"))
+    called = []
+    monkeypatch.setattr(B, "lib", lambda: called.append(1))
+    pr = base_problem(kv_dtype=code, head_dim=128, num_pages=30)
+    plan = B.Plan(0, pr)
+    good = _cpu_call_tensors(pr, kv)
+    bad_cases = {
+        "seq_lens": good["seq_lens"].long(),
+        "block_table": good["block_table"].long(),
+        "q": good["q"].float(),
+        "out": good["out"][:, :1].contiguous(),
+        "lse": good["lse"].double(),
+        "k_pool": good["k_pool"][:-1].contiguous(),
+        "v_pool": good["v_pool"][:-1].contiguous(),
+    }
+    if kv != "bf16":
+        bad_cases["k_scale"] = good["k_scale"][:-1].contiguous()
+    for name, t in bad_cases.items():
+        args = dict(good)
+        args[name] = t
+        with pytest.raises(ValueError, match=name):
+            B.small_w_attention_run(plan, args["q"], args["k_pool"], args["v_pool"],
+                                    args["k_scale"], args["v_scale"], args["block_table"],
+                                    args["seq_lens"], args["out"], args["lse"], stream=0)
+    if kv != "bf16":
+        with pytest.raises(ValueError, match="scale"):
+            B.small_w_attention_run(plan, good["q"], good["k_pool"], good["v_pool"], None, None,
+                                    good["block_table"], good["seq_lens"], good["out"],
+                                    good["lse"], stream=0)
+    kn = torch.zeros((pr.num_reqs, pr.window, pr.num_kv_heads, pr.head_dim), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k_new"):
+        B.small_w_kv_append(plan, kn[:, :1].contiguous(), kn, good["k_pool"], good["v_pool"],
+                            good["k_scale"], good["v_scale"], good["block_table"],
+                            good["seq_lens"], stream=0)
+    with pytest.raises(ValueError, match="seq_lens"):
+        B.small_w_kv_append(plan, kn, kn, good["k_pool"], good["v_pool"], good["k_scale"],
+                            good["v_scale"], good["block_table"], good["seq_lens"].long(),
+                            stream=0)
+    assert not called, "the library was called despite a bad argument"

@@ -40,35 +40,41 @@ def gpu_run(w, force_splits=0, num_cus=0, repeats=1, split_pages=0):
     return outs if repeats > 1 else outs[0]
 
 
-def v_abs_max(w):
-    """Largest |V| stored in the pool (poison excluded)."""
-    if w.kv == "mxfp4":
-        codes = np.stack([w.v_pool & 15, w.v_pool >> 4], axis=-1).reshape(
-            w.num_pages, w.Hkv, w.D, 16)                      # [page][h][d][token]
-        sc = oracle.decode_e8m0(w.v_scale)                     # [page][h][D/32][token]
-        sc = np.repeat(sc, 32, axis=2)                         # [page][h][d][token]
-        v = oracle.decode_e2m1(codes) * sc
-        return float(np.nanmax(np.abs(v)))
-    if w.kv == "fp8":
-        v = oracle.decode_e4m3(w.v_pool.reshape(-1)).reshape(w.v_pool.shape)
-        v = v * w.v_scale[:, :, None, :]
-    else:
-        v = oracle.decode_bf16(w.v_pool.reshape(-1))
-    return float(np.nanmax(np.abs(v)))
+# Unit roundoff of bf16 (8 significant bits, round to nearest even).
+BF16_U = 2.0 ** -8
 
 
-def few_key_tolerance(w):
-    """Max-abs bound when rows see only a handful of keys, so outputs are not
-    averages of many values: P rounded to bf16 (2^-9 relative) and the bf16
-    output (2^-9 relative) each move o by at most 2^-9 max|V|; 2^-7 max|V|
-    leaves a factor-2 margin.  Never below the stated 1e-2.  (The MXFP4
-    workloads' uniform codes spread the scores 1.7 times wider than N(0, 1)
-    keys, so a row's softmax rests on few keys even at hundreds of tokens.)"""
-    return max(O_MAX_ABS, 2.0 ** -7 * v_abs_max(w))
+def magnitude_workload(w):
+    """The same workload with every stored V element replaced by its magnitude:
+    the sign bit of each bf16 value, e4m3 code or E2M1 nibble cleared (fp8 and
+    MXFP4 scales are never negative, and NaN poison stays NaN).  The oracle's
+    output for it is, per (row, d), A = sum_j p_j |v_j[d]|, the row's
+    softmax-weighted mean magnitude of V."""
+    mask = {"bf16": 0x7FFF, "fp8": 0x7F, "mxfp4": 0x77}[w.kv]
+    return dataclasses.replace(w, v_pool=w.v_pool & w.v_pool.dtype.type(mask))
 
 
-def check(w, o, l, ro, rl, rows=None, o_max_abs=O_MAX_ABS):
-    """Compare GPU (o, l) to oracle (ro, rl); rows selects sampled (p, i, h)."""
+def o_bound(w, rows=None):
+    """Per-element bound on |o_gpu - o_oracle|: max(1e-2, 2 u A), u = 2^-8.
+
+    The kernels round each weight p_j to bf16 before the PV product (relative
+    error <= u per weight, normalised by the unrounded sum), which moves o[d]
+    by at most u * sum_j p_j |v_j[d]| / sum_j p_j = u A[d]; the bf16 output
+    rounding moves it by at most u |o[d]| <= u A[d].  Together 2 u A = 2^-7 A.
+    Rows that average many N(0, 1) values have A < 1.28 and keep the stated
+    1e-2; rows resting on a few large values (a handful of keys, a narrow
+    sliding window, wide MXFP4 codes) get the rounding bound of their own
+    values.  fp32 accumulation and the fp16 split partials add errors far below
+    these two roundings."""
+    A, _ = oracle.attention(magnitude_workload(w), rows=rows)
+    return np.maximum(O_MAX_ABS, 2.0 * BF16_U * A)
+
+
+def check(w, o, l, ro, rl, rows=None):
+    """Compare GPU (o, l) to oracle (ro, rl); rows selects sampled (p, i, h).
+    Outputs: every element within o_bound, relative RMS <= 4e-3 per request;
+    LSE within 1e-3 with the same infinities."""
+    bound = o_bound(w, rows=None if rows is None else np.array(rows))
     if rows is not None:
         o = np.stack([o[p, i, h] for p, i, h in rows])
         l = np.array([l[p, i, h] for p, i, h in rows])
@@ -81,8 +87,13 @@ def check(w, o, l, ro, rl, rows=None, o_max_abs=O_MAX_ABS):
     rr_all = np.sqrt(((o - ro) ** 2).sum()) / nr if nr > 0 else 0.0
     fin_ = np.isfinite(rl)
     lerr_all = np.abs(l[fin_] - rl[fin_]).max() if fin_.any() else 0.0
-    print(f"[err] max|dO|={err:.2e} relRMS={rr_all:.2e} max|dLSE|={lerr_all:.2e}", flush=True)
-    assert err <= o_max_abs, f"max |dO| = {err:.3e}"
+    ratio = np.abs(o - ro) / bound
+    worst = float(ratio.max()) if ratio.size else 0.0
+    at = np.unravel_index(ratio.argmax(), ratio.shape) if ratio.size else ()
+    print(f"[err] max|dO|={err:.2e} worst|dO|/bound={worst:.3f} relRMS={rr_all:.2e} "
+          f"max|dLSE|={lerr_all:.2e}", flush=True)
+    assert worst <= 1.0, (f"|dO| / bound = {worst:.3f} at {at}: |dO| {np.abs(o - ro)[at]:.3e}, "
+                          f"bound {bound[at]:.3e}")
     for p in range(w.P):
         a = o[groups[p]] if groups is not None else o[p]
         b = ro[groups[p]] if groups is not None else ro[p]
@@ -119,20 +130,12 @@ def test_verify_16k(W):
     check(w, o, l, *oracle.attention(w))
 
 
-def sampled_rows(w, heads):
-    return [(p, i, h) for p in range(w.P) for i in range(w.W) for h in heads]
-
-
 @pytest.mark.parametrize("W", [1, 8, 12, 16])
 def test_verify_64k_fragmented(W):
     w = make_workload("verify64k", W=W)
-    announce(f"verify64k W={W} (sampled rows)")
+    announce(f"verify64k W={W} (every row)")
     o, l = gpu_run(w)
-    rows = sampled_rows(w, [0, 5, 6, 13, 18, 23])
-    ro, rl = oracle.attention(w, rows=np.array(rows))
-    check(w, o, l, ro, rl, rows=rows)
-    # every row: LSE within the bound is cheap to demand as a whole-output property
-    assert np.isfinite(o).all() and np.isfinite(l).all()
+    check(w, o, l, *oracle.attention(w))
 
 
 def test_draft_block_batched():
@@ -144,14 +147,11 @@ def test_draft_block_batched():
 
 def test_mixed_length_batch():
     """16 requests of 100..24K keys in the launch configuration bench.py times
-    (apportioned splits: 1 to 7 per request), three heads sampled per row."""
+    (apportioned splits: 1 to 7 per request), every row of every head."""
     w = make_workload("mixed")
-    announce(f"mixed P=16 lengths {list(w.seq_lens)} (sampled rows)")
+    announce(f"mixed P=16 lengths {list(w.seq_lens)} (every row)")
     o, l = gpu_run(w)
-    rows = sampled_rows(w, [0, 13, 31])
-    ro, rl = oracle.attention(w, rows=np.array(rows))
-    check(w, o, l, ro, rl, rows=rows)
-    assert np.isfinite(o).all() and np.isfinite(l).all()
+    check(w, o, l, *oracle.attention(w))
 
 
 # ------------------------------------------------------------------ edge shapes
@@ -208,7 +208,7 @@ def test_largest_batch(kv, force):
     o, l = gpu_run(w, force_splits=force)
     empty = seq == 0
     assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
@@ -222,7 +222,7 @@ def test_most_rows_at_the_largest_head_dim(kv, causal):
     for force in (0, 3):
         announce(f"W*G=128 D=256 {kv} causal={causal} force={force}")
         o, l = gpu_run(w, force_splits=force)
-        check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+        check(w, o, l, *oracle.attention(w))
 
 
 # ------------------------------------------------------------------ invariants
@@ -296,12 +296,9 @@ def _num_cus():
 # ------------------------------------------------------------------ fp8-e4m3 KV
 def test_fp8_verify_batched_contexts():
     w = make_workload("fp8")
-    announce("fp8 P=4 8K..64K W=16 (sampled rows)")
+    announce("fp8 P=4 8K..64K W=16 (every row)")
     o, l = gpu_run(w)
-    rows = sampled_rows(w, [0, 7, 12, 23])
-    ro, rl = oracle.attention(w, rows=np.array(rows))
-    check(w, o, l, ro, rl, rows=rows)
-    assert np.isfinite(o).all() and np.isfinite(l).all()
+    check(w, o, l, *oracle.attention(w))
 
 
 FP8_EDGE = [
@@ -390,7 +387,7 @@ def test_mxfp4_edge_shapes(case, force):
                       seed=600 + case, **spec)
     announce(f"MXFP4 edge {case} {spec} force={force}")
     o, l = gpu_run(w, force_splits=force)
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
 
 
 # Five or six row tiles (W*G in 65..96): the 8- and 4-bit V decode runs only on
@@ -417,7 +414,7 @@ def test_v_decode_on_simds_2_and_3(case, force):
                       seed=700 + case, **spec)
     announce(f"{kv} five/six row tiles {case} {spec} force={force}")
     o, l = gpu_run(w, force_splits=force)
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
 
 
 def test_mxfp4_poison_and_determinism():
@@ -432,7 +429,7 @@ def test_mxfp4_poison_and_determinism():
     np.testing.assert_array_equal(oa, ob)
     np.testing.assert_array_equal(oa, oa2)
     np.testing.assert_array_equal(la, la2)
-    check(a, oa, la, *oracle.attention(a), o_max_abs=few_key_tolerance(a))
+    check(a, oa, la, *oracle.attention(a))
 
 
 def _mxfp4_as_bf16(w):
@@ -462,7 +459,8 @@ def test_mxfp4_equals_the_bf16_path_on_the_same_values(spec):
     MFMA with Q split into two e4m3 parts.  That MFMA sums its 128 products
     with about 13 significant bits of the largest one (measured), which moves
     a logit by at most ~3e-4 here (|q_d k_d| <= 4 * 6, two k-steps, scale
-    1/16).  So the LSEs agree to 2e-4 and the outputs to the few-key bound."""
+    1/16).  So the LSEs agree to 2e-4.  Each output is within o_bound of the
+    oracle (checked), so the two differ by at most twice that bound."""
     npg = sum(-(-(c + spec["W"]) // 16) for c in spec["ctx"])
     w = make_workload(None, kv="mxfp4", placement="permuted", pool_pages=npg + 7, seed=69,
                       **spec)
@@ -475,7 +473,9 @@ def test_mxfp4_equals_the_bf16_path_on_the_same_values(spec):
     do = np.abs(of - ob).max()
     print(f"[mxfp4-vs-bf16] max|dLSE|={dl:.3e} max|dO|={do:.3e} frac_diff={(of != ob).mean():.3f}",
           flush=True)
-    assert dl <= 2e-4 and do <= few_key_tolerance(w)
+    assert dl <= 2e-4
+    assert np.all(np.abs(of - ob) <= 2.0 * o_bound(w))
+    check(w, of, lf, *oracle.attention(w))
 
 
 @pytest.mark.parametrize("D", [128, 256])
@@ -518,7 +518,7 @@ def test_mxfp4_key_codes_and_scales_reach_the_scores(D):
     announce(f"MXFP4 key path D={D}")
     o, l = gpu_run(w)
     ro, rl = oracle.attention(w)
-    check(w, o, l, ro, rl, o_max_abs=few_key_tolerance(w))
+    check(w, o, l, ro, rl)
 
 
 def test_mxfp4_long_unit_slides_the_page_table_window():
@@ -526,9 +526,7 @@ def test_mxfp4_long_unit_slides_the_page_table_window():
                       kv="mxfp4", placement="permuted", pool_pages=5000, seed=67)
     announce("MXFP4 long unit force_splits=1")
     o, l = gpu_run(w, force_splits=1)
-    rows = sampled_rows(w, [0, 11, 23])
-    ro, rl = oracle.attention(w, rows=np.array(rows))
-    check(w, o, l, ro, rl, rows=rows)
+    check(w, o, l, *oracle.attention(w))
 
 
 @pytest.mark.parametrize("mode", ["exact", "window"])
@@ -538,7 +536,7 @@ def test_mxfp4_row_exact_and_window(mode):
                       window_left=300 if mode == "window" else 0)
     announce(f"MXFP4 {mode}")
     o, l = gpu_run(w, split_pages=16 if mode == "exact" else 0)
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
 
 
 # ------------------------------------------------------------------ workspace reuse
@@ -569,9 +567,7 @@ def test_long_unit_slides_the_page_table_window(kv):
                       placement="permuted", pool_pages=5000, seed=56)
     announce(f"long unit {kv} force_splits=1")
     o, l = gpu_run(w, force_splits=1)
-    rows = sampled_rows(w, [0, 11, 23])
-    ro, rl = oracle.attention(w, rows=np.array(rows))
-    check(w, o, l, ro, rl, rows=rows)
+    check(w, o, l, *oracle.attention(w))
 
 
 # ------------------------------------------------------------------ row-exact mode
@@ -645,7 +641,7 @@ def test_sliding_window_matches_oracle(case, mode):
     announce(f"window {case} {WINDOW[case]} {mode}")
     o, l = gpu_run(w, force_splits=2 if mode == "force2" else 0,
                    split_pages=13 if mode == "exact" else 0)
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
 
 
 @pytest.mark.parametrize("case", [2, 3])
@@ -653,7 +649,7 @@ def test_sliding_window_fp8(case):
     w = _window_workload(WINDOW[case], kv="fp8", seed=95 + case)
     announce(f"window fp8 {case}")
     o, l = gpu_run(w)
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
 
 
 def test_sliding_window_trace_pages_skip_the_early_pages():
@@ -672,10 +668,8 @@ def test_sliding_window_trace_pages_skip_the_early_pages():
     got = pages.cpu().numpy()
     for u, lst in enumerate(oracle.gather_unit_pages(pl, w.block_table)):
         np.testing.assert_array_equal(got[u, :len(lst)], np.array(lst, dtype=np.int32))
-    rows = sampled_rows(w, [0, 13, 23])
     o, l = gpu_run(w)
-    ro, rl = oracle.attention(w, rows=np.array(rows))
-    check(w, o, l, ro, rl, rows=rows)
+    check(w, o, l, *oracle.attention(w))
 
 
 def test_row_exact_with_window_rows_do_not_depend_on_the_window_rows():

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from test_gpu_parity import announce, check, few_key_tolerance, gpu_run
+from test_gpu_parity import announce, check, gpu_run
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -43,4 +43,4 @@ def test_random_configuration_matches_oracle(seed):
     w, force, spg, desc = random_case(seed)
     announce(f"random {seed}: {desc} force={force} split_pages={spg}")
     o, l = gpu_run(w, force_splits=force, split_pages=spg)
-    check(w, o, l, *oracle.attention(w), o_max_abs=few_key_tolerance(w))
+    check(w, o, l, *oracle.attention(w))
