@@ -102,6 +102,8 @@ extern "C" {
 #define SMALLW_MAX_WINDOW    16
 #define SMALLW_MAX_REQS      256
 #define SMALLW_MAX_ROWS      128  /* W * (Hq / Hkv) */
+/* device scratch the library holds per GPU for small_w_attention_run_noalloc */
+#define SMALLW_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum { SMALLW_KV_BF16 = 0, SMALLW_KV_FP8_E4M3 = 1, SMALLW_KV_MXFP4 = 2 } smallw_kv_dtype;
 
@@ -189,6 +191,26 @@ int small_w_attention_run(const smallw_plan* plan, const void* q, const void* k_
                           const void* v_pool, const void* k_scale, const void* v_scale,
                           const int32_t* block_table, const int32_t* seq_lens, void* out,
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As small_w_attention_run, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument.  The split partials go to a scratch
+ * array of SMALLW_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on
+ * every GPU it runs on, from module load until the process ends; this call
+ * allocates nothing, neither on the device nor through any library routine.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (other streams, concurrent threads) race and give undefined results;
+ * serialise them, or use small_w_attention_run with separate workspaces.
+ * Nothing in the scratch needs to start at any value: each call writes every
+ * byte it reads.  Returns SMALLW_EWORKSPACE when the plan needs more than the
+ * scratch holds (small_w_attention_workspace_bytes(plan) >
+ * SMALLW_NOALLOC_SCRATCH_BYTES), otherwise as small_w_attention_run.
+ */
+int small_w_attention_run_noalloc(const smallw_plan* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, const void* k_scale, const void* v_scale,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                  float* lse, void* stream);
 
 /*
  * As small_w_attention_run, and additionally sets caller-created hipEvent_t

@@ -66,6 +66,8 @@ def lib():
         L.small_w_attention_run.argtypes = run_args
         L.small_w_attention_run.restype = ctypes.c_int
         L.small_w_attention_run_events.argtypes = run_args + [vp, vp, vp]
+        L.small_w_attention_run_noalloc.argtypes = [vp] * 11
+        L.small_w_attention_run_noalloc.restype = ctypes.c_int
         L.small_w_attention_run_events.restype = ctypes.c_int
         L.small_w_attention_plan_export.argtypes = [vp, i32p, sz, ctypes.POINTER(sz)]
         L.small_w_attention_plan_export.restype = ctypes.c_int
@@ -237,6 +239,25 @@ def small_w_attention_run(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block
         rc = lib().small_w_attention_run_events(*args, *events)
     if rc != SMALLW_OK:
         raise SmallwError(rc, "small_w_attention_run")
+
+
+def small_w_attention_run_noalloc(plan: Plan, q, k_pool, v_pool, k_scale, v_scale,
+                                  block_table, seq_lens, out, lse, stream=None) -> None:
+    """small_w_attention_run without a workspace: the library's own per-GPU
+    scratch holds the split partials (calls that overlap on one GPU race)."""
+    pr = plan.problem
+    dev = _current_device()
+    rows = pr.num_reqs * pr.window * pr.num_q_heads
+    _check(q, "q", BF16_BITS, numel=rows * pr.head_dim, device=dev)
+    _check(out, "out", BF16_BITS, numel=rows * pr.head_dim, device=dev)
+    _check(lse, "lse", ("float32",), numel=rows, device=dev)
+    _check_pools(pr, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, dev)
+    rc = lib().small_w_attention_run_noalloc(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                             _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                             _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                             _stream(stream))
+    if rc != SMALLW_OK:
+        raise SmallwError(rc, "small_w_attention_run_noalloc")
 
 
 def small_w_attention_trace_pages(plan: Plan, block_table, seq_lens, pages_out,

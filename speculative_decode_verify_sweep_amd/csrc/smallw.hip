@@ -27,6 +27,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "plan_internal.h"
@@ -1210,6 +1211,45 @@ thread_local char g_err[256] = "";
 
 }  // namespace
 
+// Scratch for small_w_attention_run_noalloc: the split partials and their
+// records of one call, in device memory the library owns from module load to
+// process end (each GPU holds its own copy).  In host code `scratch` names a
+// host-side stand-in, not the device address: the address is fetched once per
+// device with hipGetSymbolAddress and only that value is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[SMALLW_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (nullptr and a device error
+// on failure); resolved on the first call made with that device current.
+void* scratch_address() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        smallw::set_device_error("hipGetDevice", int(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        smallw::set_device_error("device index beyond the scratch table", int(hipErrorInvalidDevice));
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            smallw::set_device_error("hipGetSymbolAddress(scratch)", int(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
 namespace smallw {
 void set_device_error(const char* what, int hip_status) {
     snprintf(g_err, sizeof g_err, "%s: %s", what, hipGetErrorString(hipError_t(hip_status)));
@@ -1389,6 +1429,22 @@ int small_w_attention_run(const smallw_plan* pl, const void* q, const void* k_po
     return small_w_attention_run_events(pl, q, k_pool, v_pool, k_scale, v_scale, block_table,
                                         seq_lens, out, lse, workspace, workspace_bytes, stream,
                                         nullptr, nullptr, nullptr);
+}
+
+int small_w_attention_run_noalloc(const smallw_plan* pl, const void* q, const void* k_pool,
+                                  const void* v_pool, const void* k_scale, const void* v_scale,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                  float* lse, void* stream) {
+    if (!pl) return SMALLW_EINVAL;
+    if (pl->ws_bytes > SMALLW_NOALLOC_SCRATCH_BYTES) return SMALLW_EWORKSPACE;
+    void* ws = nullptr;
+    if (pl->ws_bytes > 0) {
+        ws = scratch_address();
+        if (!ws) return SMALLW_EDEVICE;
+    }
+    return small_w_attention_run_events(pl, q, k_pool, v_pool, k_scale, v_scale, block_table,
+                                        seq_lens, out, lse, ws, ws ? SMALLW_NOALLOC_SCRATCH_BYTES : 0,
+                                        stream, nullptr, nullptr, nullptr);
 }
 
 int small_w_attention_trace_pages(const smallw_plan* pl, const int32_t* block_table,

@@ -298,3 +298,17 @@ def test_binding_rejects_tensors_that_do_not_fit_the_plan(monkeypatch, kv, code)
                             good["v_scale"], good["block_table"], good["seq_lens"].long(),
                             stream=0)
     assert not called, "the library was called despite a bad argument"
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch_before_any_launch():
+    """A plan whose partials exceed the library's scratch gets SMALLW_EWORKSPACE
+    from the allocation-free entry point; a null plan gets SMALLW_EINVAL."""
+    lib = B.lib()
+    fake = 1 << 40  # never dereferenced
+    pr = base_problem(num_reqs=1, window=16, num_q_heads=24, num_kv_heads=4, head_dim=256,
+                      num_pages=1100, max_pages_per_req=1100, force_splits=1025)
+    plan = sw.small_w_attention_plan(pr, [16400])
+    assert sw.small_w_attention_workspace_bytes(plan) > 32 << 20
+    args = [fake, fake, fake, None, None, fake, fake, fake, fake, None]
+    assert lib.small_w_attention_run_noalloc(plan.handle, *args) == B.SMALLW_EWORKSPACE
+    assert lib.small_w_attention_run_noalloc(None, *args) == B.SMALLW_EINVAL

@@ -45,7 +45,10 @@ def asm(tmp_path_factory):
 def kernels(text):
     """(name, body) of every kernel in a device assembly file."""
     found = []
+    funcs = set(re.findall(r"\.type\s+(_Z\w+),@function", text))
     for m in re.finditer(r"^(_Z\w+):", text, re.M):
+        if m.group(1) not in funcs:      # a device variable, not a kernel
+            continue
         end = text.find(".Lfunc_end", m.start())
         found.append((m.group(1), text[m.start():end]))
     return found
