@@ -57,8 +57,9 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
     unit_off[p] = Hkv * sum_{q<p} S_q;  unit u = unit_off[p] + kvh*S_p + s
     split s covers pages n_lo + [floor(s*n_eff/S), floor((s+1)*n_eff/S)), or in
     row-exact mode the s-th piece of the absolute grid [k*B, (k+1)*B), the last
-    split ending at n_pg and the first starting at n_lo moved down to an even
-    offset from its k*B (the piece's two-page chunks then line up in every call)
+    split ending at n_pg and the first starting at n_lo moved down to a multiple
+    of 2 pages from its k*B, or of 8 pages for e4m3 pools (the pages the sweep
+    groups into one step then line up in every call)
     """
     seq = [int(x) for x in seq_lens]
     assert len(seq) == P
@@ -92,6 +93,9 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
     unit_off = [0]
     for s in splits:
         unit_off.append(unit_off[-1] + Hkv * s)
+    # pages one step of the sweep's arithmetic groups: 128-token PV steps for e4m3
+    # pools, two-page chunks otherwise (the library's written specification)
+    align = 8 if kv_fp8 else 2
     units = []
     for p in range(P):
         S, n, lo, ne = splits[p], n_pg[p], n_lo[p], n_eff[p]
@@ -100,7 +104,7 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
                 if split_pages > 0:
                     k = lo // split_pages + s
                     b0 = k * split_pages
-                    pb = (b0 + ((lo - b0) // 2) * 2) if s == 0 else b0
+                    pb = (b0 + ((lo - b0) // align) * align) if s == 0 else b0
                     pe = n if s + 1 == S else (k + 1) * split_pages
                 else:
                     pb, pe = split_range(ne, S, s)

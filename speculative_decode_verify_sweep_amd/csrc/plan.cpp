@@ -138,7 +138,8 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             pl->unit_off[p + 1] = int32_t(next);
             for (int64_t s = 0; s < S; ++s) {
                 int64_t pb, pe;
-                smallw::split_range(lo, n, S, s, in.split_pages, &pb, &pe);
+                smallw::split_range(lo, n, S, s, in.split_pages, smallw::piece_align(in.kv_dtype), &pb,
+                                    &pe);
                 if (size_t(pe - pb) > pl->max_unit_pages) pl->max_unit_pages = size_t(pe - pb);
             }
         }
@@ -192,7 +193,8 @@ int small_w_attention_plan_export(const smallw_plan* plan, int32_t* buf, size_t 
         for (int kvh = 0; kvh < Hkv; ++kvh)
             for (int64_t s = 0; s < S; ++s) {
                 int64_t pb, pe;
-                smallw::split_range(lo, npg, S, s, plan->prob.split_pages, &pb, &pe);
+                smallw::split_range(lo, npg, S, s, plan->prob.split_pages,
+                                    smallw::piece_align(plan->prob.kv_dtype), &pb, &pe);
                 buf[k++] = p;
                 buf[k++] = kvh;
                 buf[k++] = int32_t(s);

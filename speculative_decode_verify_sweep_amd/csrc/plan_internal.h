@@ -32,16 +32,22 @@ inline int64_t first_page(int64_t L, int32_t W, int32_t causal, int32_t window_l
     return lo > 0 ? lo / SMALLW_PAGE_SIZE : 0;
 }
 
+// Pages the sweep groups together for one step of its arithmetic: two-page
+// chunks for bf16 and MXFP4 pools, eight-page PV steps (128 tokens, the depth
+// of the scaled fp8 MFMA) for e4m3 pools.  A row-exact piece must start on
+// this grid so that every call groups the piece's pages the same way.
+inline int32_t piece_align(int32_t kv_dtype) { return kv_dtype == SMALLW_KV_FP8_E4M3 ? 8 : 2; }
+
 // Page range [*pb, *pe) of split s of a request whose pages [n_lo, n) are
 // streamed in S splits: balanced (split_pages == 0) or on the absolute grid of
 // multiples of split_pages, the last piece ending at n and the first starting
-// at n_lo moved down to the piece's own page-pair grid (so that every call
-// groups the pages of a piece into the same two-page chunks).
+// at n_lo moved down to a multiple of `align` pages from the piece's own grid
+// point (so that every call groups the pages of a piece the same way).
 inline void split_range(int64_t n_lo, int64_t n, int64_t S, int64_t s, int32_t split_pages,
-                        int64_t* pb, int64_t* pe) {
+                        int32_t align, int64_t* pb, int64_t* pe) {
     if (split_pages > 0) {
         const int64_t k = n_lo / split_pages + s;
-        *pb = s == 0 ? k * split_pages + ((n_lo - k * split_pages) & ~int64_t(1))
+        *pb = s == 0 ? k * split_pages + ((n_lo - k * split_pages) & ~int64_t(align - 1))
                      : k * split_pages;
         *pe = (s + 1 == S) ? n : (k + 1) * split_pages;
     } else {

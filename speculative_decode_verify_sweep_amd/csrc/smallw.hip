@@ -70,6 +70,7 @@ struct Params {
     int32_t split_pages;  // > 0: row-exact splits at multiples of this many pages
     int32_t combine;      // 1: every row goes through partials and the combine
     int32_t window_left;  // > 0: sliding window of this many keys per row
+    int32_t piece_align;  // row-exact first pieces start on multiples of this many pages
     float scale_log2;  // softmax scale * log2(e): scores are kept in base 2
     int32_t unit_off[SMALLW_MAX_REQS + 1];
 };
@@ -106,10 +107,10 @@ __device__ __forceinline__ Unit decode_unit(const Params& a, int u) {
         n_lo = k0 > 0 ? k0 / kPage : 0;
     }
     if (a.split_pages > 0) {  // row-exact: absolute grid of pieces; the first one
-        // starts at n_lo moved down to its page-pair grid, the last ends at n
+        // starts at n_lo moved down to its grouping grid, the last ends at n
         const int64_t k = n_lo / a.split_pages + r.s;
         const int64_t b0 = k * a.split_pages;
-        r.pb = int(min(r.s == 0 ? b0 + ((n_lo - b0) & ~int64_t(1)) : b0, n));
+        r.pb = int(min(r.s == 0 ? b0 + ((n_lo - b0) & ~int64_t(a.piece_align - 1)) : b0, n));
         r.pe = r.s + 1 == r.S ? int(n) : int(min((k + 1) * a.split_pages, n));
     } else {
         r.pb = int(n_lo + (int64_t(r.s) * (n - n_lo)) / r.S);
@@ -190,16 +191,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 // ----------------------------------------------------------------------------
-// Split-K sweep kernel.  512 threads = 8 wave64s; wave w owns the 16-row MFMA
-// tile w of the unit's W*G rows (W*G <= 128), and the waves share the DMA work.
+// Split-K sweep kernel for bf16 and MXFP4 pools (e4m3 pools: sweep8_kernel
+// below).  512 threads = 8 wave64s; wave w owns the 16-row MFMA tile w of the
+// unit's W*G rows (W*G <= 128), and the waves share the DMA work.
 //   D    head dim (64/128/256)
 //   NS   LDS ring depth in chunks (2 pages each)
-//   FP8  K/V stored as OCP e4m3fn codes with per-(token, KV-head) fp32 scales,
-//        decoded to bf16 once per chunk into an LDS staging tile (the MFMAs
-//        stay bf16); the scales multiply S and P
-// LDS chunk layout (bytes): [K page0 | K page1 | V^T page0 | V^T page1], each a
-// page-head of 16*D*elt bytes; fp8 chunks add 256 bytes of scales (k page0,
-// k page1, v page0, v page1; 16 floats each) in a separate small array.
+//   KV   storage format (bf16, or MXFP4 with V decoded once per chunk into a
+//        bf16 staging tile)
+// LDS chunk layout of a bf16 ring stage (bytes): [K page0 | K page1 | V^T page0
+// | V^T page1], each a page-head of 16*D*2 bytes (MXFP4: fp4_piece below).
 // K rows are 16-byte-chunk swizzled: token row tau stores global chunk c at
 // slot c ^ h(tau), h(tau) = ((tau>>1)&12)|(tau&3) (masked to the row), so the
 // 16 lanes of one MFMA operand read hit distinct banks.  A bf16 V^T page
@@ -207,7 +207,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // tokens 0..7 of rows 16k..16k+15 at 512k + 16*(d&15), tokens 8..15 256 bytes
 // later.  The two halves of a row then share a bank slot, so a lane's bank
 // depends only on its row, as in a linear read, and each 1 KiB DMA instruction
-// still reads 1 KiB of contiguous HBM.  fp8 V^T rows are a single 16-byte chunk.
+// still reads 1 KiB of contiguous HBM.
 // ----------------------------------------------------------------------------
 constexpr int kSweepWaves = 8;
 constexpr int kSweepThreads = 64 * kSweepWaves;
@@ -232,16 +232,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 #undef SMALLW_WAIT_CASE
         default: wait_vmcnt<24>(); break;
     }
-}
-
-// 8 e4m3fn codes (one per byte, little-endian order) -> 8 bf16, exact
-__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Byte J of w (two E2M1 codes, the low nibble first) -> 2 bf16, each times
@@ -307,29 +297,95 @@ __device__ __forceinline__ void fp4_piece(int q, int& arr, int& pg, int& off) {
     }
 }
 
+// Epilogue of a work unit, on a wave that owns row tile w: normalise the
+// rows, then write the final bf16 output and LSE (an unsplit request) or the
+// fp16 split partial and its {lse, scale} record.  acc holds O^T tiles: lane
+// l = 16g + ln, tile dt, element i is row r = 16w + ln, d = 16dt + 4g + i.
+template <int D>
+__device__ __forceinline__ void finish_unit(const Params& a, const f32x4 (&acc)[D / 16],
+                                            float m_run, float l_run, int u, const Unit& un,
+                                            int w, int l, int g, int r, int qi, int T) {
+    constexpr int DT = D / 16;
+    const int p = un.p, kvh = un.kvh;
+    const float lsum = wave_sum_groups(l_run);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float lse2 = lsum > 0.f ? m_run + __log2f(lsum) : -INFINITY;  // base 2
+    // largest |o| of the row (its four lanes), for the split partial's scale
+    float mabs = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mabs = fmaxf(mabs, fabsf(acc[dt][i]));
+    mabs = wave_max_groups(mabs) * inv;
+    if (r >= a.R) return;
+    const int h = kvh * a.G + (r - qi * a.G);
+    if (un.S == 1 && !a.combine) {
+        uint16_t* orow = a.out + ((int64_t(p) * a.W + qi) * a.Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 o = acc[dt] * inv;
+            uint2 pk;
+            pk.x = uint32_t(f32_to_bf16_bits(o[0])) | (uint32_t(f32_to_bf16_bits(o[1])) << 16);
+            pk.y = uint32_t(f32_to_bf16_bits(o[2])) | (uint32_t(f32_to_bf16_bits(o[3])) << 16);
+            *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pk;
+        }
+        if (g == 0) a.lse[(int64_t(p) * a.W + qi) * a.Hq + h] = lse2 * kLn2;
+    } else {
+        // split partial in fp16, the row divided by 2^e (e the exponent of its
+        // largest |o|, so every value lies in (-1, 1) and keeps 11 significant
+        // bits relative to the row's largest); the combine multiplies 2^e back.
+        // Stored lane-native: block (u, tile w, k) is 64 lanes x 8 halves, lane
+        // l = 16g + ln holding d tiles 2k and 2k+1 of its row, so each store
+        // instruction writes 1 KiB of contiguous memory.
+        int e = 0;
+        (void)frexpf(mabs, &e);
+        e = min(max(e, -100), 127);
+        const float c = ldexpf(inv, -e);
+        uint16_t* ob = a.part_o + ((int64_t(u) * T + w) * (DT / 2)) * 512 + l * 8;
+#pragma unroll
+        for (int k = 0; k < DT / 2; ++k) {
+            const f32x4 x0 = acc[2 * k] * c, x1 = acc[2 * k + 1] * c;
+            uint16_t hb[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hb[i] = __builtin_bit_cast(uint16_t, (_Float16)x0[i]);
+                hb[4 + i] = __builtin_bit_cast(uint16_t, (_Float16)x1[i]);
+            }
+            store_wt(ob + k * 512, u32x4{uint32_t(hb[0]) | (uint32_t(hb[1]) << 16),
+                                         uint32_t(hb[2]) | (uint32_t(hb[3]) << 16),
+                                         uint32_t(hb[4]) | (uint32_t(hb[5]) << 16),
+                                         uint32_t(hb[6]) | (uint32_t(hb[7]) << 16)});
+        }
+        // the S records of one row are contiguous: [unit group][row][split]
+        if (g == 0) {
+            const float2 rec = {lse2, ldexpf(1.f, e)};
+            store_wt(a.part_rec + int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s,
+                     __builtin_bit_cast(uint2, rec));
+        }
+    }
+}
+
 template <int D, int NS, int KV, bool DECH>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
-    constexpr bool FP8 = KV == SMALLW_KV_FP8_E4M3;
+    static_assert(KV == SMALLW_KV_BF16 || KV == SMALLW_KV_MXFP4, "e4m3 pools: sweep8_kernel");
     constexpr bool FP4 = KV == SMALLW_KV_MXFP4;
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
     constexpr int BF_PAGE = 32 * D;                // bf16 page-head of K (or V^T) in LDS
     // page-head codes as streamed from HBM; an MXFP4 stage also holds its scales
-    constexpr int ST_PAGE = FP4 ? 8 * D : (FP8 ? 16 * D : BF_PAGE);
+    constexpr int ST_PAGE = FP4 ? 8 * D : BF_PAGE;
     constexpr int ST_STAGE = FP4 ? 34 * D : 4 * ST_PAGE;
     constexpr int RING = NS * ST_STAGE;            // DMA ring
-    // + V decode staging for the 8- and 4-bit formats: two chunks of V^T, bf16
-    constexpr int LDS_BYTES = RING + (FP8 || FP4 ? 4 * BF_PAGE : 0);
+    // + V decode staging for the 4-bit format: two chunks of V^T, bf16
+    constexpr int LDS_BYTES = RING + (FP4 ? 4 * BF_PAGE : 0);
     constexpr int REG_INST = FP4 ? 1 : ST_PAGE / 1024;  // DMA instructions per region
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
     constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
     constexpr int CPR = D / 8;                     // 16-byte bf16 chunks per K token row
-    // chunks in flight ahead of the one being computed (the 8- and 4-bit
-    // formats decode V one iteration ahead, but read K from the ring slot)
+    // chunks in flight ahead of the one being computed (the 4-bit format
+    // decodes V one iteration ahead, but reads K from the ring slot)
     constexpr int AHEAD = NS - 1;
-    constexpr int NSS = FP8 ? NS + 1 : 1;          // fp8 scale slots: chunks c .. c+NS-1 live
-    constexpr bool LOWP = FP8 || FP4;              // scores on the scaled MFMA, V staged
-    constexpr int SPR8 = D / 16;                   // 16-byte slots per fp8 K row
+    constexpr bool LOWP = FP4;                     // scores on the scaled MFMA, V staged
     // MXFP4: 16-byte pieces per stage, DMA instructions per chunk (instruction
     // i is issued by wave i mod 8) and the most any wave issues
     constexpr int N16 = ST_STAGE / 16;
@@ -339,7 +395,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     static_assert(!FP4 || D == 128 || D == 256, "MXFP4 serves D = 128 and 256");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) float scl[FP8 ? NSS : 1][64];
     __shared__ int32_t ptab[kPtab];
 
     const int tid = threadIdx.x;
@@ -362,7 +417,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- this wave's query rows (tile w)
     const int T = (a.R + 15) >> 4;
     const bool has_tile = w < T;
-    // V decode (8- and 4-bit formats).  Wave w runs on SIMD w mod 4, so five or
+    // V decode (4-bit format).  Wave w runs on SIMD w mod 4, so five or
     // six row tiles put two on SIMDs 0 and 1 and one on SIMDs 2 and 3.  Then
     // (DECH, chosen at launch) only the four waves on SIMDs 2 and 3 decode, as
     // threads dec_id = 0..255 with 4D/256 items each, the row-tile ones after
@@ -374,7 +429,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);  // this row's last key
     const int hi_tok = min(jend - 1, hi_row);
     const int lo_tok = a.window_left > 0 ? hi_row - a.window_left + 1 : INT_MIN;
-    // Q fragments: KS bf16 k-steps, or for the scaled MFMA (8- and 4-bit K)
+    // Q fragments: KS bf16 k-steps, or for the scaled MFMA (4-bit K)
     // qf[4k + 2r + h], the 16-element runs r of 128-deep k-step k (>= 4 entries)
     bf16x8_t qf[LOWP && KS < 4 ? 4 : KS];
 
@@ -388,26 +443,19 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
-    // ---- DMA work of this wave: part (w>>2) of region (w&3) of each chunk, and
-    // for fp8 wave 7 also the chunk's 64 scales
+    // ---- DMA work of this wave: part (w>>2) of region (w&3) of each chunk
     const int region = w & 3;
     const int region_pg = region & 1;
     const bool region_v = region >= 2;
     const bool issues_kv = !FP4 && (SPLIT || w < 4);
-    const bool issues_scale = FP8 && w == kSweepWaves - 1;
     const int nload = FP4 ? (NI4 - w + kSweepWaves - 1) / kSweepWaves   // per chunk
-                          : (issues_kv ? LPW : 0) + (issues_scale ? 1 : 0);
+                          : (issues_kv ? LPW : 0);
     const int ibase = SPLIT ? (w >> 2) * LPW : 0;
     uint32_t goff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int qc = 64 * (ibase + i) + l;  // 16-byte chunk index inside the page-head
-        if (FP8) {
-            // K rows (D bytes) get the bf16 rows' 16-byte-slot swizzle; V^T raw
-            const int tr = qc / SPR8, slot = qc % SPR8;
-            const int hsw = ((((16 * region_pg + tr) >> 1) & 12) | ((16 * region_pg + tr) & 3)) & (SPR8 - 1);
-            goff[i] = region_v ? uint32_t(qc * 16) : uint32_t(tr * D + (slot ^ hsw) * 16);
-        } else if (!region_v) {
+        if (!region_v) {
             const int tr = qc / CPR, slot = qc % CPR;
             const int tau = 16 * region_pg + tr;
             const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
@@ -430,11 +478,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         if (has4[j]) fp4_piece<D>(q, arr4[j], pg4[j], off4[j]);
     }
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
-    const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
     const uint8_t* const pool = region_v ? a.v : a.k;
-    // The scale DMA picks k_scale or v_scale per lane.  Kept opaque in SGPRs so
-    // the compiler cannot turn that select into a per-lane load of the pointer
-    // from the kernel arguments, whose vmcnt(0) wait would drain the ring.
+    // Scale pointers kept opaque in SGPRs, so that the compiler cannot turn a
+    // per-lane select between them into a per-lane load of the pointer from the
+    // kernel arguments, whose vmcnt(0) wait would drain the ring.
     const float* kscale = a.k_scale;
     const float* vscale = a.v_scale;
     asm volatile("" : "+s"(kscale), "+s"(vscale));
@@ -470,61 +517,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i)
                 dma16(base + goff[i], __builtin_amdgcn_readfirstlane(lds + 1024u * i));
-        }
-        if (issues_scale) {
-            // lane l: array l>>4 (k page0, k page1, v page0, v page1), token l&15
-            const int arr = l >> 4;
-            int n = 2 * c + (arr & 1);
-            if (n >= npages) n = 2 * c;
-            const int phys = ptab[n - tbase];
-            const float* src = (arr < 2 ? kscale : vscale) +
-                               (int64_t(phys) * a.Hkv + kvh) * kPage + (l & 15);
-            dma4(src, __builtin_amdgcn_readfirstlane(scl_base + uint32_t((c % NSS) * 256)));
-        }
-    };
-
-    // fp8: decode the V^T codes of ring chunk c once for the whole workgroup
-    // into bf16 staging buffer (c & 1), in the bf16 ring's V^T layout; the V
-    // scales stay out (they multiply P).  Item (page, token half h, row d): 8
-    // codes, one 8-byte read, one 16-byte write.  Straight-line like decode_v4.
-    // Decoders run in two phases, every item's reads and then every item's
-    // converts and staging writes: the compiler cannot tell the staging tile
-    // from the ring slot, so a read placed after a write would wait for it and
-    // the items' LDS round trips would add up.
-    auto decode_v8 = [&](int c) {
-        const uint8_t* src = smem + (c % NS) * ST_STAGE + 2 * ST_PAGE;
-        uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
-        // items it0, it0 + step, ... (N of them, those below 4D real)
-        auto run = [&](int it0, int step, auto n_tag, auto full_tag) {
-            constexpr int N = decltype(n_tag)::value;
-            constexpr bool FULL = decltype(full_tag)::value;  // every item below 4D
-            uint2 w8[N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int it = it0 + step * i;
-                if (FULL || it < 4 * D) {
-                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-                    w8[i] = *reinterpret_cast<const uint2*>(src + pg * ST_PAGE + d * 16 + 8 * h);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int it = it0 + step * i;
-                if (FULL || it < 4 * D) {
-                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-                    *reinterpret_cast<bf16x8_t*>(dst + pg * BF_PAGE + 512 * (d >> 4) +
-                                                 16 * (d & 15) + 256 * h) =
-                        e4m3x8_to_bf16(w8[i].x, w8[i].y);
-                }
-            }
-        };
-        if constexpr (DECH) {
-            if (w & 2)
-                run(dec_id, 256, std::integral_constant<int, 4 * D / 256>{}, std::true_type{});
-        } else {
-            run(tid, kSweepThreads,
-                std::integral_constant<int, (4 * D + kSweepThreads - 1) / kSweepThreads>{},
-                std::integral_constant<bool, (4 * D) % kSweepThreads == 0>{});
         }
     };
 
@@ -597,26 +589,23 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             u32x4 raw = {0u, 0u, 0u, 0u};
             // bf16 k-step ks, lane group g: elements 32ks + 8g ..  Scaled MFMA:
             // qf[4k + 2r + h] holds run r of k-step k, contraction positions
-            // 64r + 16g + 8h .., which are elements 128k + 64r + 16g + 8h .. of
-            // an fp8 K row (zero past D) and ((D/4)(2r + (g>>1)) + 32k + 16(g&1)
-            // + 8h ..) of an MXFP4 one (its K LDS layout gives lane group g the
-            // row's D/4-element slice)
+            // 64r + 16g + 8h .., which are elements ((D/4)(2r + (g>>1)) + 32k +
+            // 16(g&1) + 8h ..) of an MXFP4 K row (its K LDS layout gives lane
+            // group g the row's D/4-element slice)
             const int k4 = ks >> 2, r4 = (ks >> 1) & 1, h4 = ks & 1;
-            const int d0 = FP4   ? (D / 4) * (2 * r4 + (g >> 1)) + 32 * k4 + 16 * (g & 1) + 8 * h4
-                           : FP8 ? 128 * k4 + 64 * r4 + 16 * g + 8 * h4
-                                 : 32 * ks + 8 * g;
+            const int d0 = FP4 ? (D / 4) * (2 * r4 + (g >> 1)) + 32 * k4 + 16 * (g & 1) + 8 * h4
+                               : 32 * ks + 8 * g;
             if (valid && d0 < D) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
             qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-    // ---- 8- and 4-bit scores run on the scaled MFMA (e4m3 or E2M1 K times e4m3
-    // Q, E8M0 scales per 32 elements of the contraction: the MXFP4 block scales
-    // for K, 1 for e4m3 K, whose per-token scale multiplies S instead).  The
-    // MFMA's fp4 and fp8 operands put contraction positions 64r + 16g .. 64r +
-    // 16g + 15 (runs r = 0, 1) or 32g .. 32g + 31 in lane group g.  Q is split
-    // once per unit:
+    // ---- 4-bit scores run on the scaled MFMA (E2M1 K times e4m3 Q, E8M0
+    // scales per 32 elements of the contraction: the MXFP4 block scales for K).
+    // The MFMA's fp4 and fp8 operands put contraction positions 32g .. 32g + 31
+    // and 64r + 16g .. 64r + 16g + 15 (runs r = 0, 1) in lane group g.  Q is
+    // split once per unit:
     // q = hi 2^X + lo 2^(X-4) per 32-element block, hi and lo e4m3 and X =
     // floor(log2 amax) - 7, so |q| / 2^X < 256 and the residual fits lo.  A
     // block's 32 elements are the runs of two lane groups (g, g ^ 1); the scale
@@ -706,25 +695,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             k4sc[t] = uint32_t(32 * D + (tau >> 4) * (D / 2) + (tau & 15) * (D / 32) + g * (KS / 4));
         }
     }
-    // fp8 K: tile t row tau, run r of k-step k = bytes 128k + 64r + 16g .. of
-    // the row, i.e. 16-byte slot 8k + 4r + g, stored at slot ^ h(tau)
-    uint32_t k8addr[2][LOWP ? KS4 : 1][2] = {};
-    if constexpr (FP8) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int tau = 8 * (ln >> 2) + 4 * t + (ln & 3);
-            const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (SPR8 - 1);
-#pragma unroll
-            for (int k = 0; k < KS4; ++k)
-#pragma unroll
-                for (int r4 = 0; r4 < 2; ++r4) {
-                    const int slot = (8 * k + 4 * r4 + g) & (SPR8 - 1);  // D = 64: run 1 unused
-                    k8addr[t][k][r4] = uint32_t((tau >> 4) * ST_PAGE + (tau & 15) * D + 16 * (slot ^ hsw));
-                }
-        }
-    }
     // where this lane's V^T operand rows start: the bf16 ring stage, or the
-    // V staging buffer of the 8- and 4-bit formats (the two V pages only)
+    // V staging buffer of the 4-bit format (the two V pages only)
     const uint32_t va = LOWP ? vaddr - 2 * BF_PAGE : vaddr;
 
     f32x4 acc[DT];
@@ -743,33 +715,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         f32x4 s4[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) s4[t][0] = s4[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-            // per tile row and k-step: the lane's two 16-byte runs of e4m3 codes
-            // (run 1 is zero at D = 64); K block scales 1 (byte 127)
-            i32x8 ka[2][KS4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int k = 0; k < KS4; ++k) {
-                    const u32x4 r0 = *reinterpret_cast<const u32x4*>(st + k8addr[t][k][0]);
-                    u32x4 r1 = {0u, 0u, 0u, 0u};
-                    if constexpr (D >= 128) r1 = *reinterpret_cast<const u32x4*>(st + k8addr[t][k][1]);
-                    ka[t][k] = i32x8{int(r0[0]), int(r0[1]), int(r0[2]), int(r0[3]),
-                                     int(r1[0]), int(r1[1]), int(r1[2]), int(r1[3])};
-                }
-#pragma unroll
-            for (int k = 0; k < KS4; ++k)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    s4[t][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        ka[t][k], qhi[k], s4[t][0], 0, 0, 0, 0x7F7F7F7F, 0, int(shi >> (8 * k)));
-                    s4[t][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        ka[t][k], qlo[k], s4[t][1], 0, 0, 0, 0x7F7F7F7F, 0, int(slo >> (8 * k)));
-                }
-            // this thread's share of the next chunk's V, under the MFMAs (with
-            // DECH the row-tile waves of SIMDs 2 and 3 decode after their PV)
-            if constexpr (!DECH) decode_v8(c + 1);
-        } else if constexpr (FP4) {
+        if constexpr (FP4) {
             // per tile row: the lane's D/8 code bytes (16 per 128-deep k-step:
             // one E2M1 block) and their E8M0 scales (byte k for k-step k); the
             // hi and lo parts of Q accumulate in separate chains
@@ -825,24 +771,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
                 vraw[dt] = *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
             __builtin_amdgcn_sched_barrier(0);
         }
-        float ksc[8], vsc[8];
-        if constexpr (FP8) {
-            // scales of chunk tokens 8g..8g+7: k at [8g], v at [32 + 8g]
-            const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[c % NSS][0]);
-            const f32x4 k0 = sp[2 * g], k1 = sp[2 * g + 1], v0 = sp[8 + 2 * g], v1 = sp[9 + 2 * g];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ksc[e] = k0[e] * a.scale_log2;
-                ksc[e + 4] = k1[e] * a.scale_log2;
-                vsc[e] = v0[e];
-                vsc[e + 4] = v1[e];
-            }
-        }
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = e >> 2, j = e & 3;
-            x[e] = (s4[t][0][j] + s4[t][1][j]) * (FP8 ? ksc[e] : a.scale_log2);
+            x[e] = (s4[t][0][j] + s4[t][1][j]) * a.scale_log2;
             if (TAIL) {
                 const int j = j0 + 8 * g + e;
                 x[e] = (j <= hi_tok && j >= lo_tok) ? x[e] : -INFINITY;
@@ -866,12 +799,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
         l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
         // tokens past the unit's keys may hold anything (even NaN): zero their
-        // V^T elements (and, for fp8, their weights, since the scale may be NaN)
+        // V^T elements
         const int vcnt = TAIL ? min(max(jend - (j0 + 8 * g), 0), 8) : 8;
-        if constexpr (FP8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = (!TAIL || e < vcnt) ? pe[e] * vsc[e] : 0.f;
-        }
         const bf16x8_t pf = bf16x8_t{(__bf16)pe[0], (__bf16)pe[1], (__bf16)pe[2], (__bf16)pe[3],
                                      (__bf16)pe[4], (__bf16)pe[5], (__bf16)pe[6], (__bf16)pe[7]};
         // O^T += V^T . P^T
@@ -893,10 +822,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- ring step for iteration c.
     // bf16: wait for chunk c, then refill the slot freed by chunk c-1 with
     //       chunk c+NS-1.
-    // fp8 and MXFP4: as bf16, but wait for chunk c+1, whose V every thread
-    //       decodes into staging during iteration c (row-tile waves inside
-    //       process, between the score MFMAs and the softmax); chunk c's K is
-    //       read from its ring slot.
+    // MXFP4: as bf16, but wait for chunk c+1, whose V every thread decodes
+    //       into staging during iteration c (row-tile waves inside process,
+    //       between the score MFMAs and the softmax); chunk c's K is read from
+    //       its ring slot.
     auto ring_step = [&](int c) {
         const int need = LOWP ? c + 1 : c;
         // chunks younger than `need` left in flight: all issued up to c+NS-2
@@ -914,8 +843,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
     auto decode_v = [&](int c) {
-        if constexpr (FP8) decode_v8(c);
-        else if constexpr (FP4) decode_v4(c);
+        if constexpr (FP4) decode_v4(c);
     };
     if (LOWP && nchunks > 0) {  // decode chunk 0's V ahead of the loop
         wait_vmcnt_dyn(min(AHEAD - 1, nchunks - 1) * nload);
@@ -949,62 +877,530 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 
     // ---- epilogue: normalise, write the final output or the split partial
     if (!has_tile) return;
-    const float lsum = wave_sum_groups(l_run);
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const float lse2 = lsum > 0.f ? m_run + __log2f(lsum) : -INFINITY;  // base 2
-    // largest |o| of the row (its four lanes), for the split partial's scale
-    float mabs = 0.f;
+    finish_unit<D>(a, acc, m_run, l_run, u, un, w, l, g, r, qi, T);
+}
+
+// ----------------------------------------------------------------------------
+// e4m3 sweep (fp8 KV).  The scores run on the scaled fp8 MFMA as in the other
+// low-precision path, and so does the PV product: the e4m3 V^T codes go from
+// the LDS ring straight into the MFMA's A operand (no decode, no staging), and
+// the weights are split into two e4m3 parts per 32-token block and row,
+//   p = hi 2^X + lo 2^(X-4),  X = floor(log2 max_block p) - 7,
+// which holds every weight to about 2^-8 of itself (the unit roundoff of the
+// bf16 weights of the other paths).  Chunks are 64 tokens (4 pages); two
+// chunks (128 tokens, the MFMA's depth) make one PV step.
+//
+// K streams through a 4-chunk LDS ring (three chunks ahead), V^T through a
+// 2-step one (the next step ahead).
+//
+// Token layout.  Score tile tt (16 tokens) of a chunk puts page g of the
+// chunk in MFMA rows 4g..4g+3 at tokens 4tt..4tt+3, so lane group g ends up
+// holding all 16 scores of page g of the chunk for its row.  That is exactly
+// the PV B operand: k = 16g + e (run 0) is page g, token e of the step's first
+// chunk, k = 64 + 16g + e (run 1) page g, token e of its second.  The A
+// operand (V^T) of lane (g, d-row ln) is then row d of page g of each chunk:
+// two 16-byte LDS reads, the d-major page layout as stored in HBM.
+//
+// The running max only moves to whole numbers, so every rescale is an exact
+// power of two: pending weights shift their block exponent, and the output
+// accumulator is rescaled once per step, before that step's PV MFMAs.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
+    constexpr int KS4 = D < 128 ? 1 : D / 128;  // 128-deep k-steps of the scores
+    constexpr int DT = D / 16;                  // 16-wide d tiles of the output
+    constexpr int PGB = 16 * D;                 // one page-head of codes, K or V^T
+    constexpr int CHB = 4 * PGB;                // one 64-token chunk of K or V^T
+    constexpr int NK = 4, NV = 4;               // ring slots (chunks)
+    constexpr int IPP = PGB / 1024;             // 1 KiB DMA instructions per page
+    constexpr int KI = 4 * IPP;                 // ... per chunk, for K and for V^T
+    constexpr int SPR = D / 16;                 // 16-byte slots per K row
+    constexpr int DH = DT / 2;                  // d tiles per half PV step
+    static_assert(IPP >= 1 && KI <= 16 && DT % 2 == 0, "config");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t kring[NK * CHB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vring[NV * CHB];
+    // per K slot: K scales [page][token] (64), then V scales (64)
+    __shared__ __attribute__((aligned(16))) float scl[NK][128];
+    __shared__ int32_t ptab[kPtab];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int g = l >> 4;
+    const int ln = l & 15;
+
+    const Unit un = decode_unit(a, blockIdx.x);
+    const int u = blockIdx.x;
+    const int p = un.p, kvh = un.kvh, L = un.L;
+    const int npages = un.pe - un.pb;
+    const int nchunks = (npages + 3) >> 2;
+    const int jend = min(L, un.pe * kPage);
+    const int lim_lo = a.causal ? (L - a.W + 1) : L;
+    const int first_masked = min(jend, lim_lo);
+    const int win_hi = a.window_left > 0 ? L - a.window_left : INT_MIN;
+
+    const int T = (a.R + 15) >> 4;
+    const bool has_tile = w < T;
+    const int r = 16 * w + ln;
+    const int qi = r / a.G;
+    const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);
+    const int hi_tok = min(jend - 1, hi_row);
+    const int lo_tok = a.window_left > 0 ? hi_row - a.window_left + 1 : INT_MIN;
+
+    int tbase = 0;
+    auto fill_ptab = [&](int base) {
+        for (int k = tid; k < kPtab; k += kSweepThreads)
+            if (base + k < npages) ptab[k] = phys_page(a, p, un.pb + base + k);
+    };
+    fill_ptab(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    // ---- DMA work of this wave.  K: instructions w and w + 8 of a chunk's KI
+    // (page i / IPP), rows swizzled so that a lane's 16-byte slot sigma of row
+    // (page, token) sits at sigma ^ h, h = (page << 2 | token & 3) masked to the
+    // row: the 8 and 16 lanes of one operand read then hit distinct banks.
+    // Scales: wave 6 the chunk's K scales, wave 7 its V scales (lane l: page
+    // l >> 4, token l & 15).  V^T: instruction i of chunk q of a PV step is
+    // issued by wave (i + q KI) mod 8, a raw 1 KiB copy.
+    uint32_t koff[2];
+    int kpg[2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int j = 0; j < 2; ++j) {
+        const int i = (w + 8 * j) % KI;
+        const int qc = 64 * (i % IPP) + l;
+        const int tr = qc / SPR, ps = qc % SPR;
+        const int pg = i / IPP;
+        const int h = ((pg << 2) | (tr & 3)) & (SPR - 1);
+        koff[j] = uint32_t(tr * D + 16 * (ps ^ h));
+        kpg[j] = pg;
+    }
+    const bool issues_scale = w >= 6;
+    const int nk_w = (w < KI ? 1 : 0) + (w + 8 < KI ? 1 : 0) + (issues_scale ? 1 : 0);
+    int nvq[2] = {0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mabs = fmaxf(mabs, fabsf(acc[dt][i]));
-    mabs = wave_max_groups(mabs) * inv;
-    if (r >= a.R) return;
-    const int h = kvh * a.G + (r - qi * a.G);
-    if (un.S == 1 && !a.combine) {
-        uint16_t* orow = a.out + ((int64_t(p) * a.W + qi) * a.Hq + h) * D;
+    for (int q = 0; q < 2; ++q)
+        for (int i = 0; i < KI; ++i) nvq[q] += ((i + q * KI) & 7) == w ? 1 : 0;
+    const uint32_t kr_base = uint32_t(reinterpret_cast<uintptr_t>(kring));
+    const uint32_t vr_base = uint32_t(reinterpret_cast<uintptr_t>(vring));
+    const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
+    const float* kscale = a.k_scale;
+    const float* vscale = a.v_scale;
+    asm volatile("" : "+s"(kscale), "+s"(vscale));
+
+    // pages past the unit's end are replaced by the chunk's first page (always
+    // present); their tokens are masked
+    auto issue_k = [&](int t) {
+        const int ks = t % NK;
+        const uint32_t slot = uint32_t(ks * CHB);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const f32x4 o = acc[dt] * inv;
-            uint2 pk;
-            pk.x = uint32_t(f32_to_bf16_bits(o[0])) | (uint32_t(f32_to_bf16_bits(o[1])) << 16);
-            pk.y = uint32_t(f32_to_bf16_bits(o[2])) | (uint32_t(f32_to_bf16_bits(o[3])) << 16);
-            *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pk;
-        }
-        if (g == 0) a.lse[(int64_t(p) * a.W + qi) * a.Hq + h] = lse2 * kLn2;
-    } else {
-        // split partial in fp16, the row divided by 2^e (e the exponent of its
-        // largest |o|, so every value lies in (-1, 1) and keeps 11 significant
-        // bits relative to the row's largest); the combine multiplies 2^e back.
-        // Stored lane-native: block (u, tile w, k) is 64 lanes x 8 halves, lane
-        // l = 16g + ln holding d tiles 2k and 2k+1 of its row, so each store
-        // instruction writes 1 KiB of contiguous memory.
-        int e = 0;
-        (void)frexpf(mabs, &e);
-        e = min(max(e, -100), 127);
-        const float c = ldexpf(inv, -e);
-        uint16_t* ob = a.part_o + ((int64_t(u) * T + w) * (DT / 2)) * 512 + l * 8;
-#pragma unroll
-        for (int k = 0; k < DT / 2; ++k) {
-            const f32x4 x0 = acc[2 * k] * c, x1 = acc[2 * k + 1] * c;
-            uint16_t hb[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hb[i] = __builtin_bit_cast(uint16_t, (_Float16)x0[i]);
-                hb[4 + i] = __builtin_bit_cast(uint16_t, (_Float16)x1[i]);
+        for (int j = 0; j < 2; ++j) {
+            const int i = w + 8 * j;
+            if (i < KI) {
+                int n = 4 * t + kpg[j];
+                if (n >= npages) n = 4 * t;
+                const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
+                dma16(a.k + (int64_t(phys) * a.Hkv + kvh) * PGB + koff[j],
+                      __builtin_amdgcn_readfirstlane(kr_base + slot + 1024u * uint32_t(i)));
             }
-            store_wt(ob + k * 512, u32x4{uint32_t(hb[0]) | (uint32_t(hb[1]) << 16),
-                                         uint32_t(hb[2]) | (uint32_t(hb[3]) << 16),
-                                         uint32_t(hb[4]) | (uint32_t(hb[5]) << 16),
-                                         uint32_t(hb[6]) | (uint32_t(hb[7]) << 16)});
         }
-        // the S records of one row are contiguous: [unit group][row][split]
-        if (g == 0) {
-            const float2 rec = {lse2, ldexpf(1.f, e)};
-            store_wt(a.part_rec + int64_t(u - un.s) * a.R + int64_t(r) * un.S + un.s,
-                     __builtin_bit_cast(uint2, rec));
+        if (issues_scale) {
+            int n = 4 * t + (l >> 4);
+            if (n >= npages) n = 4 * t;
+            const int phys = ptab[n - tbase];
+            const float* src = (w == 6 ? kscale : vscale) +
+                               (int64_t(phys) * a.Hkv + kvh) * kPage + (l & 15);
+            dma4(src, __builtin_amdgcn_readfirstlane(
+                          scl_base + uint32_t((ks * 128 + (w - 6) * 64) * 4)));
+        }
+    };
+    auto issue_v = [&](int gi) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int t = 2 * gi + q;
+            if (t >= nchunks) break;
+            const uint32_t slot = uint32_t((t % NV) * CHB);
+#pragma unroll
+            for (int m = 0; m < (KI + 7) / 8; ++m) {
+                const int i = ((w - q * KI) & 7) + 8 * m;
+                if (i < KI) {
+                    int n = 4 * t + i / IPP;
+                    if (n >= npages) n = 4 * t;
+                    const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
+                    dma16(a.v + (int64_t(phys) * a.Hkv + kvh) * PGB + 16 * (64 * (i % IPP) + l),
+                          __builtin_amdgcn_readfirstlane(vr_base + slot + 1024u * uint32_t(i)));
+                }
+            }
+        }
+    };
+
+    // ---- prologue: issue order K0 K1 V0 K2; then Q (one round trip for all of
+    // it).  Each wave's issue order continues K3 V1 | K4 | K5 V2 | K6 | ...:
+    // ring step t issues K(t + 3) and, for even t, the V^T of step t/2 + 1, so
+    // step g's V^T always follows K(2g + 1)
+    for (int t = 0; t < min(2, nchunks); ++t) issue_k(t);
+    if (nchunks > 0) issue_v(0);
+    if (nchunks > 2) issue_k(2);
+    bf16x8_t qf[4 * KS4];
+    {
+        const bool valid = has_tile && r < a.R;
+        const int gq = r - qi * a.G;
+        const uint16_t* qrow =
+            a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < 4 * KS4; ++ks) {
+            // qf[4k + 2r + h]: contraction positions 128k + 64r + 16g + 8h .. (zero past D)
+            const int d0 = 128 * (ks >> 2) + 64 * ((ks >> 1) & 1) + 16 * g + 8 * (ks & 1);
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (valid && d0 < D) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // ---- Q split per 32-element block into two e4m3 parts q = hi 2^X + lo
+    // 2^(X-4), X = floor(log2 amax) - 7, which hold a bf16 q exactly (4 + 4
+    // significant bits).  Block b of a 128-deep k-step is run b >> 1 of lane
+    // groups 2(b & 1), 2(b & 1) + 1; lane group g supplies the scale of block g.
+    i32x8 qhi[KS4], qlo[KS4];
+    uint32_t shi = 0, slo = 0;
+#pragma unroll
+    for (int k = 0; k < KS4; ++k) {
+        int X[2];
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+            float m = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    m = fmaxf(m, fabsf(float(qf[4 * k + 2 * r4 + hh][e])));
+            m = pair16(m, true);
+            int ex = 0;
+            (void)frexpf(m, &ex);
+            X[r4] = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; e += 4) {
+                    float x4[4], y4[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        x4[i] = ldexpf(float(qf[4 * k + 2 * r4 + hh][e + i]), -X[r4]);
+                    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[0], x4[1], 0, false);
+                    hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[2], x4[3], hw, true);
+                    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+                    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+                    y4[0] = (x4[0] - h01[0]) * 16.f;
+                    y4[1] = (x4[1] - h01[1]) * 16.f;
+                    y4[2] = (x4[2] - h23[0]) * 16.f;
+                    y4[3] = (x4[3] - h23[1]) * 16.f;
+                    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[0], y4[1], 0, false);
+                    lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[2], y4[3], lw, true);
+                    const int wi = 4 * r4 + 2 * hh + e / 4;  // byte 16 r4 + 8 hh + e
+                    qhi[k][wi] = hw;
+                    qlo[k][wi] = lw;
+                }
+        const int src = 16 * 2 * (g & 1) + ln;
+        const int x0 = __shfl(X[0], src), x1 = __shfl(X[1], src);
+        const int xs = (g >> 1) ? x1 : x0;
+        shi |= uint32_t(xs + 127) << (8 * k);
+        slo |= uint32_t(xs - 4 + 127) << (8 * k);
+    }
+
+    // K operand reads: lane row (page ln >> 2, token 4 tt + (ln & 3)), run r of
+    // k-step k = 16-byte slot 8k + 4r + g of the row, stored at slot ^ (ln & (SPR-1))
+    uint32_t k8a[KS4][2];
+#pragma unroll
+    for (int k = 0; k < KS4; ++k)
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+            const int slot = (8 * k + 4 * r4 + g) & (SPR - 1);
+            k8a[k][r4] = uint32_t((ln >> 2) * PGB + (ln & 3) * D + 16 * (slot ^ (ln & (SPR - 1))));
+        }
+    // V^T operand reads: page g of a chunk, row d = 16 dt + ln
+    const uint32_t v8a = uint32_t(g * PGB + 16 * ln);
+
+    f32x4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    float m_acc = -INFINITY;  // the running max acc is expressed against
+
+    // ---- scores of chunk t on the scaled MFMA: s4[tt][i] = page g, token 4tt + i
+    auto qk = [&](int t, f32x4 (&s4)[4]) {
+        const uint8_t* ks = kring + (t % NK) * CHB;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) s4[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // two tiles and one k-step at a time: their K operands, then the hi and
+        // lo MFMAs of both tiles
+#pragma unroll
+        for (int t2 = 0; t2 < 4; t2 += 2)
+#pragma unroll
+            for (int k = 0; k < KS4; ++k) {
+                i32x8 ka[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int off = 4 * (t2 + tt) * D;
+                    const u32x4 r0 = *reinterpret_cast<const u32x4*>(ks + k8a[k][0] + off);
+                    u32x4 r1 = {0u, 0u, 0u, 0u};
+                    if constexpr (D >= 128)
+                        r1 = *reinterpret_cast<const u32x4*>(ks + k8a[k][1] + off);
+                    ka[tt] = i32x8{int(r0[0]), int(r0[1]), int(r0[2]), int(r0[3]),
+                                   int(r1[0]), int(r1[1]), int(r1[2]), int(r1[3])};
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    s4[t2 + tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka[tt], qhi[k], s4[t2 + tt], 0, 0, 0, 0x7F7F7F7F, 0, int(shi >> (8 * k)));
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    s4[t2 + tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka[tt], qlo[k], s4[t2 + tt], 0, 0, 0, 0x7F7F7F7F, 0, int(slo >> (8 * k)));
+            }
+    };
+
+    // ---- softmax of chunk t (branch-free), then its weights (row ln, page g,
+    // tokens 0..15, times the V scales) split into e4m3 parts; a pending first
+    // chunk of the same step (PEND) shifts its exponent Xp when the max moves
+    auto softmax_split = [&](int t, const f32x4 (&s4)[4], i32x8& hi, i32x8& lo, int& X, int& Xp,
+                             auto tail_tag, auto pend_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        constexpr bool PEND = decltype(pend_tag)::value;  // second chunk: dwords 4..7
+        constexpr int HO = PEND ? 4 : 0;
+        const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[t % NK][0]);
+        const int j0 = (un.pb + 4 * t + g) * kPage;  // absolute position of token 0 of page g
+        float x[16];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 kq = sp[4 * g + tt] * a.scale_log2;  // scores in base-2 units
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * tt + i;
+                x[e] = s4[tt][i] * kq[i];
+                if (TAIL) x[e] = (j0 + e <= hi_tok && j0 + e >= lo_tok) ? x[e] : -INFINITY;
+            }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+        mx = wave_max_groups(mx);
+        const bool grow = mx > m_run + kRescaleSlack;
+        const float m_new = grow ? ceilf(mx) : m_run;
+        if constexpr (PEND) {
+            if (grow && m_run != -INFINITY) Xp = max(Xp + int(m_run - m_new), -123);
+        }
+        l_run *= grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // a power of two, or 0
+        m_run = m_new;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float pw[16];
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            pw[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+            ls += pw[e];
+        }
+        l_run += ls;
+        const int vcnt = TAIL ? min(max(jend - j0, 0), 16) : 16;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 vq = sp[16 + 4 * g + tt];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * tt + i;
+                // stale tokens (past the unit's keys) may carry NaN scales
+                pw[e] = (!TAIL || e < vcnt) ? pw[e] * vq[i] : 0.f;
+            }
+        }
+        // block max over lanes l and l ^ 16 (one 32-token block)
+        float m = pw[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) m = fmaxf(m, pw[e]);
+        m = pair16(m, true);
+        int ex = 0;
+        (void)frexpf(m, &ex);
+        X = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+            float x4[4], y4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x4[i] = ldexpf(pw[e + i], -X);
+            int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[0], x4[1], 0, false);
+            hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[2], x4[3], hw, true);
+            const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+            const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+            y4[0] = (x4[0] - h01[0]) * 16.f;
+            y4[1] = (x4[1] - h01[1]) * 16.f;
+            y4[2] = (x4[2] - h23[0]) * 16.f;
+            y4[3] = (x4[3] - h23[1]) * 16.f;
+            int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[0], y4[1], 0, false);
+            lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[2], y4[3], lw, true);
+            hi[HO + e / 4] = hw;
+            lo[HO + e / 4] = lw;
+        }
+    };
+
+    // ---- the previous PV step, carried through the pipeline: its split
+    // weights (the MFMA's B operands: dwords 0..3 the first chunk, 4..7 the
+    // second), exponents, first chunk and valid-token counts per run
+    struct Step {
+        i32x8 bhi, blo;
+        int XA, XB, tA, c0, c1;
+    };
+    // half H (d tiles H*DH ..) of the PV MFMAs of step s
+    auto pv_half = [&](const Step& s, auto half_tag, auto tail_tag) {
+        constexpr int H = decltype(half_tag)::value;
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        // run 0 of lane group g lies in 32-token block g >> 1, run 1 in block
+        // 2 + (g >> 1); lane group g supplies block g's scale: its own run 0
+        // (g = 0) or run 1 (g = 3); lane group 1 takes lane group 3's run 0 and
+        // lane group 2 lane group 0's run 1, across the 32-lane halves
+        const int send = g == 0 ? s.XB : s.XA;
+        const auto sw = __builtin_amdgcn_permlane32_swap(uint32_t(send), uint32_t(send), false, false);
+        const int other = int(sw[0]) == send ? int(sw[1]) : int(sw[0]);
+        const int xs = g == 0 ? s.XA : g == 3 ? s.XB : other;
+        const int sc_hi = xs + 127, sc_lo = xs - 4 + 127;
+        const uint8_t* va = vring + (s.tA % NV) * CHB + v8a;
+        const uint8_t* vb = vring + ((s.tA + 1) % NV) * CHB + v8a;
+        uint32_t mask0[4], mask1[4];
+        if constexpr (TAIL) {
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const int n0 = min(max(s.c0 - 4 * k2, 0), 4), n1 = min(max(s.c1 - 4 * k2, 0), 4);
+                mask0[k2] = n0 == 4 ? ~0u : (1u << (8 * n0)) - 1u;
+                mask1[k2] = n1 == 4 ? ~0u : (1u << (8 * n1)) - 1u;
+            }
+        }
+        constexpr int DG = 1;  // d tiles per MFMA group
+#pragma unroll
+        for (int d0 = H * DH; d0 < (H + 1) * DH; d0 += DG) {
+            i32x8 vop[DG];
+#pragma unroll
+            for (int j = 0; j < DG; ++j) {
+                u32x4 x0 = *reinterpret_cast<const u32x4*>(va + 256 * (d0 + j));
+                // an absent second chunk reads a stale slot, masked to zero
+                u32x4 x1 = *reinterpret_cast<const u32x4*>(vb + 256 * (d0 + j));
+                if constexpr (TAIL) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        x0[k2] &= mask0[k2];
+                        x1[k2] &= mask1[k2];
+                    }
+                }
+                vop[j] = i32x8{int(x0[0]), int(x0[1]), int(x0[2]), int(x0[3]),
+                               int(x1[0]), int(x1[1]), int(x1[2]), int(x1[3])};
+            }
+#pragma unroll
+            for (int j = 0; j < DG; ++j)
+                acc[d0 + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    vop[j], s.bhi, acc[d0 + j], 0, 0, 0, 0x7F7F7F7F, 0, sc_hi);
+#pragma unroll
+            for (int j = 0; j < DG; ++j)
+                acc[d0 + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    vop[j], s.blo, acc[d0 + j], 0, 0, 0, 0x7F7F7F7F, 0, sc_lo);
+        }
+    };
+    // the accumulator follows the running max before a step's PV MFMAs
+    auto rescale_acc = [&]() {
+        if (__any(m_acc != m_run)) {
+            // a power of two, or 0 from -inf; rows whose max did not move keep 1
+            const float alpha = m_acc == m_run ? 1.f : __builtin_amdgcn_exp2f(m_acc - m_run);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            m_acc = m_run;
+        }
+    };
+
+    // ---- ring step of chunk t: wait for K(t) (odd t: and for the step's
+    // V^T, which follows K(t)), barrier, then issue K(t + 3) into the slot
+    // chunk t - 1 freed and, for even t, the V^T of step t/2 + 1 into the slots
+    // step t/2 - 1 freed (its PV ran at that step's end)
+    auto kcnt = [&](int x) { return x < nchunks ? nk_w : 0; };
+    auto vcnt_of = [&](int gi) {
+        return gi >= 0 && 2 * gi < nchunks ? nvq[0] + (2 * gi + 1 < nchunks ? nvq[1] : 0) : 0;
+    };
+    auto ring_step = [&](int t) {
+        if (t > 0) {
+            // this wave's loads issued after the ones needed now
+            const int younger = (t & 1)
+                ? kcnt(t + 1) + kcnt(t + 2) + vcnt_of((t + 1) >> 1)
+                : kcnt(t + 1) + vcnt_of(t >> 1) + kcnt(t + 2);
+            wait_vmcnt_dyn(younger);
+        }
+        __syncthreads();
+        const bool v_next = !(t & 1) && t + 2 < nchunks;
+        if (t + 3 < nchunks || v_next) {
+            const int lo_need = v_next ? 4 * t + 8 : 4 * t + 12;
+            const int hi_need = min(4 * t + 15, npages - 1);
+            if (hi_need - tbase >= kPtab) {  // slide the page-table window (long units only)
+                tbase = lo_need;
+                fill_ptab(tbase);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __syncthreads();
+            }
+            if (t + 3 < nchunks) issue_k(t + 3);
+            if (v_next) issue_v((t >> 1) + 1);
+        }
+    };
+
+    // ---- step j: scores and softmax of chunks 2j and 2j + 1 (the second may
+    // be absent in a masked step), then the step's PV MFMAs
+    auto step = [&](int j, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int tA = 2 * j;
+        const bool hasB = tA + 1 < nchunks;
+        Step cur;
+        cur.tA = tA;
+        cur.bhi = cur.blo = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        cur.XA = cur.XB = 0;
+        cur.c0 = min(max(jend - (un.pb + tA * 4 + g) * kPage, 0), 16);
+        cur.c1 = hasB ? min(max(jend - (un.pb + tA * 4 + 4 + g) * kPage, 0), 16) : 0;
+        ring_step(tA);
+        if (has_tile) {
+            f32x4 s4[4];
+            qk(tA, s4);
+            softmax_split(tA, s4, cur.bhi, cur.blo, cur.XA, cur.XB, tail_tag, std::false_type{});
+        }
+        if (!TAIL || hasB) {
+            ring_step(tA + 1);  // its wait also covers this step's V^T
+            if (has_tile) {
+                f32x4 s4[4];
+                qk(tA + 1, s4);
+                softmax_split(tA + 1, s4, cur.bhi, cur.blo, cur.XB, cur.XA, tail_tag,
+                              std::true_type{});
+            }
+        } else {
+            wait_vmcnt<0>();  // the last chunk: this step's V^T may be the newest load
+            __syncthreads();
+        }
+        if (has_tile) {
+            rescale_acc();
+            pv_half(cur, std::integral_constant<int, 0>{}, tail_tag);
+            pv_half(cur, std::integral_constant<int, 1>{}, tail_tag);
+        }
+    };
+
+    // Chunks that need a mask (keys past the unit's end or some row's causal
+    // limit) are a suffix, those below some row's sliding window a prefix; a
+    // step with any of them, or with one chunk only, runs the masked code.
+    // Three loops, so that no loop body carries both variants.
+    int c_tail = nchunks;
+    while (c_tail > 0 && (un.pb + 4 * (c_tail - 1)) * kPage + 64 > first_masked) --c_tail;
+    int c_head = 0;
+    while (c_head < c_tail && (un.pb + 4 * c_head) * kPage < win_hi) ++c_head;
+    const int ngroups = (nchunks + 1) >> 1;
+    const int g_head = (c_head + 1) >> 1, g_tail = c_tail >> 1;  // unmasked steps [g_head, g_tail)
+    int j = 0;
+    for (; j < g_head; ++j) step(j, std::true_type{});
+    for (; j < g_tail; ++j) step(j, std::false_type{});
+    for (; j < ngroups; ++j) step(j, std::true_type{});
+
+    if (!has_tile) return;
+    finish_unit<D>(a, acc, m_run, l_run, u, un, w, l, g, r, qi, T);
 }
 
 // ----------------------------------------------------------------------------
@@ -1282,6 +1678,7 @@ void fill_params(Params& a, const smallw_plan* pl) {
     a.split_pages = pr.split_pages;
     a.combine = pl->combine ? 1 : 0;
     a.window_left = pr.window_left;
+    a.piece_align = smallw::piece_align(pr.kv_dtype);
     for (int p = 0; p <= pr.num_reqs; ++p) a.unit_off[p] = pl->unit_off[p];
 }
 
@@ -1308,10 +1705,8 @@ int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* e
     const int T = (pl->R + 15) / 16;
     const bool dech = T == 5 || T == 6;
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
-        return dech ? launch(sweep_kernel<D, 7, SMALLW_KV_FP8_E4M3, true>, pl->U, kSweepThreads, a,
-                             st, ev0, ev1, "sweep kernel launch")
-                    : launch(sweep_kernel<D, 7, SMALLW_KV_FP8_E4M3, false>, pl->U, kSweepThreads, a,
-                             st, ev0, ev1, "sweep kernel launch");
+        return launch(sweep8_kernel<D>, pl->U, kSweepThreads, a, st, ev0, ev1,
+                      "sweep kernel launch");
     if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
         if constexpr (D == 64) return SMALLW_EUNSUPPORTED;  // the planner rejects it first
         else

@@ -65,9 +65,10 @@ def test_every_kernel_is_present(asm):
     names = [n for n, _ in kernels(asm["smallw.hip"])]
     for k in ("sweep_kernel", "combine_kernel", "trace_kernel"):
         assert any(k in n for n in names), (k, names)
-    # bf16, fp8 and MXFP4 sweeps at D = 64 / 128 / 256 (no MXFP4 at D = 64); the
-    # 8- and 4-bit ones in both V-decode placements
-    assert sum("sweep_kernel" in n for n in names) == 3 + 2 * 3 + 2 * 2
+    # bf16 and MXFP4 sweeps at D = 64 / 128 / 256 (no MXFP4 at D = 64), MXFP4 in
+    # both V-decode placements; the e4m3 sweep at the three head dims
+    assert sum("sweep_kernel" in n for n in names) == 3 + 2 * 2
+    assert sum("sweep8_kernel" in n for n in names) == 3
     # the combine with clamped and with skipped loads, at D = 64 / 128 / 256
     assert sum("combine_kernel" in n for n in names) == 2 * 3
     assert any("append_kernel" in n for n, _ in kernels(asm["append.hip"]))
@@ -106,7 +107,7 @@ def test_m0_written_only_by_the_dma_statements(asm):
 
 def test_group_reductions_use_lane_swaps(asm):
     for name, body in kernels(asm["smallw.hip"]):
-        if "sweep_kernel" not in name:
+        if "sweep_kernel" not in name and "sweep8_kernel" not in name:
             continue
         ins = [i.split()[0] for i in instructions(body)]
         assert any(i.startswith("v_permlane16_swap_b32") for i in ins), name

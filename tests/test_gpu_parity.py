@@ -390,9 +390,10 @@ def test_mxfp4_edge_shapes(case, force):
     check(w, o, l, *oracle.attention(w))
 
 
-# Five or six row tiles (W*G in 65..96): the 8- and 4-bit V decode runs only on
-# the four waves of SIMDs 2 and 3; the row-tile waves among them decode after
-# their chunk's PV.  T = ceil(W*G / 16) noted per case.
+# Five or six row tiles (W*G in 65..96): two row-tile waves share SIMDs 0 and 1;
+# the MXFP4 V decode then runs only on the four waves of SIMDs 2 and 3 (the
+# row-tile waves among them after their chunk's PV).  The e4m3 cases check the
+# same shapes on the e4m3 sweep.  T = ceil(W*G / 16) noted per case.
 DECH_CASES = [
     ("fp8", dict(P=2, Hq=5, Hkv=1, D=64, ctx=(37, 300), W=16, causal=True)),        # T = 5
     ("fp8", dict(P=1, Hq=12, Hkv=2, D=128, ctx=(1000,), W=16, causal=False)),      # T = 6
@@ -672,11 +673,15 @@ def test_sliding_window_trace_pages_skip_the_early_pages():
     check(w, o, l, *oracle.attention(w))
 
 
-def test_row_exact_with_window_rows_do_not_depend_on_the_window_rows():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_row_exact_with_window_rows_do_not_depend_on_the_window_rows(kv):
+    """With a sliding window the first row-exact piece starts below row 0's
+    window, aligned to the pages one arithmetic step groups (2 for bf16, 8 for
+    e4m3), so every row's pieces group their pages alike in every call."""
     w = make_workload(None, P=1, Hq=24, Hkv=4, D=256, ctx=(2000,), W=16, causal=True,
-                      kv="bf16", placement="permuted", pool_pages=140, seed=97, poison=False,
+                      kv=kv, placement="permuted", pool_pages=140, seed=97, poison=False,
                       window_left=500)
-    announce("row-exact + window independence")
+    announce(f"row-exact + window independence {kv}")
     o, l = gpu_run(w, split_pages=10)
     for i in (0, 9, 15):
         w1 = dataclasses.replace(w, W=1, q=np.ascontiguousarray(w.q[:, i:i + 1]),

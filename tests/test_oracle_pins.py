@@ -562,6 +562,15 @@ def test_row_exact_plan_splits_at_fixed_page_multiples():
     ua = [u[3:] for u in a["units"] if u[0] == 0 and u[1] == 0]
     ub = [u[3:] for u in b["units"] if u[1] == 0]
     assert ua[:-1] == ub[:-1] and ua[-1] == (60, 63) and ub[-1] == (60, 62)
+    # with a sliding window the first piece starts below the window's first page,
+    # on the grid of the pages one arithmetic step groups: L = 1000, W = 4, causal,
+    # window 700 -> row 0's first key 996 - 700 + 1 = 297, page 18; B = 20 -> k = 0.
+    # bf16 groups page pairs: piece 0 starts at 18; e4m3 groups 8 pages: at 16
+    for fp8, start in ((False, 18), (True, 16)):
+        pl = oracle.plan(P=1, Hkv=1, D=128, kv_fp8=fp8, seq_lens=[1000], num_cus=256,
+                         split_pages=20, W=4, causal=True, window_left=700)
+        assert pl["splits"] == [4] and pl["units"][0][3:] == (start, 20)
+        assert [u[3:] for u in pl["units"][1:]] == [(20, 40), (40, 60), (60, 63)]
 
 
 def test_row_exact_split_partials_combine_to_the_full_result():
