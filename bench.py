@@ -276,10 +276,14 @@ def main():
                  ("verify64k W=16 row-exact, 65-page splits",
                   dict(name="verify64k", W=16, split_pages=65)),
                  ("verify64k W=16 sliding window 4096",
-                  dict(name="verify64k", W=16, window_left=4096))]
+                  dict(name="verify64k", W=16, window_left=4096)),
+                 ("verify64k W=16 token-major V", dict(name="verify64k", W=16, v_layout=1)),
+                 ("verify64k W=1 token-major V", dict(name="verify64k", W=1, v_layout=1)),
+                 ("draft token-major V", dict(name="draft", v_layout=1))]
         for label, spec in specs:
             wl = make_workload(spec["name"], W=spec.get("W"),
-                               window_left=spec.get("window_left", 0))
+                               window_left=spec.get("window_left", 0),
+                               v_layout=spec.get("v_layout", 0))
             dd = dv.upload(wl)
             pl = dv.plan_for(wl, split_pages=spec.get("split_pages", 0))
             wsb = dv.workspace_for(pl)

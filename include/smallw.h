@@ -42,6 +42,7 @@
  *   v_pool       [num_pages][Hkv][D][16]     bf16, or e4m3fn bytes; each
  *                                            16-token page-head is stored
  *                                            transposed (d-major)
+ *                [num_pages][Hkv][16][D]     bf16 with v_layout token-major
  *   k_scale      fp32 [num_pages][Hkv][16]   fp8 only: value = code * scale
  *   v_scale      fp32 [num_pages][Hkv][16]   fp8 only
  * MXFP4 pools (kv_dtype SMALLW_KV_MXFP4, head_dim 128 or 256) hold two E2M1
@@ -107,6 +108,11 @@ extern "C" {
 
 typedef enum { SMALLW_KV_BF16 = 0, SMALLW_KV_FP8_E4M3 = 1, SMALLW_KV_MXFP4 = 2 } smallw_kv_dtype;
 
+/* How each 16-token page-head of the value pool is laid out.  D-major is the
+ * default; token-major stores V like K (a 16 x D block, token rows of D
+ * values), the layout a pool written token by token has. */
+typedef enum { SMALLW_V_DMAJOR = 0, SMALLW_V_TOKEN_MAJOR = 1 } smallw_v_layout;
+
 typedef struct smallw_problem {
     int32_t num_reqs;          /* P, 1..SMALLW_MAX_REQS                              */
     int32_t window;            /* W, 1..SMALLW_MAX_WINDOW                            */
@@ -133,6 +139,8 @@ typedef struct smallw_problem {
                                   visible key is at position h sees only the keys
                                   h-N+1 .. h (pages before the lowest row's window
                                   are not read at all)                               */
+    int32_t v_layout;          /* smallw_v_layout; token-major needs kv_dtype bf16
+                                  (SMALLW_EUNSUPPORTED otherwise)                   */
 } smallw_problem;
 
 typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
@@ -263,7 +271,8 @@ size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan);
  *   k_pool, v_pool, k_scale, v_scale, block_table, seq_lens: as for
  *                 small_w_attention_run (scales required for e4m3 and MXFP4)
  * The K row goes to slot pos % 16 of page block_table[p][pos / 16], the V row
- * to the same slot of the transposed value page.  bf16 pools get the bits as
+ * to the same slot of the transposed value page (row pos % 16 of the value
+ * page when the plan's v_layout is token-major).  bf16 pools get the bits as
  * given.  e4m3 pools get, per (token, KV head) row, scale = amax|x| / 448 (1.0
  * for an all-zero row) and codes = round-to-nearest-even of x / scale on the
  * OCP e4m3fn grid, computed in fp32 with IEEE division.  MXFP4 pools get, per

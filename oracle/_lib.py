@@ -72,6 +72,10 @@ def attention(w, rows=None, key_lo: int = 0, key_hi: int = 2**31 - 1):
         lse = np.zeros((n,), dtype=np.float64)
     fmt = KV_FORMATS[w.kv]
     scaled = fmt != 0
+    if getattr(w, "v_layout", 0) == 1:     # token-major value pages (bf16 only)
+        if w.kv != "bf16":
+            raise ValueError("token-major value pages are a bf16 layout")
+        fmt = 3
     arrs = [np.ascontiguousarray(a) if a is not None else None
             for a in (w.q, w.k_pool, w.v_pool, w.k_scale if scaled else None,
                       w.v_scale if scaled else None, w.block_table, w.seq_lens)]

@@ -108,15 +108,17 @@ def mxfp4_row_quantize(x) -> tuple[np.ndarray, np.ndarray]:
 
 
 def kv_append(*, P, W, Hkv, D, k_new_bits, v_new_bits, k_pool, v_pool, k_scale,
-              v_scale, block_table, seq_lens, num_pages, kv="bf16"):
+              v_scale, block_table, seq_lens, num_pages, kv="bf16", v_layout=0):
     """Return updated copies of the pools after appending the window tokens.
 
     k_new_bits / v_new_bits: uint16 bf16 bits [P][W][Hkv][D].  Pools and scales
     in the library's layouts for kv = "bf16" | "fp8" | "mxfp4" (uint8 bytes
     for the last two; the MXFP4 value pool packs tokens 2i, 2i+1 of a row d
     into byte i, the even token in the low nibble, and its scales are
-    block-major [page][head][D/32][16])."""
+    block-major [page][head][D/32][16]).  v_layout=1: a bf16 value pool laid
+    out token-major [page][head][16][D], written like K."""
     assert kv in ("bf16", "fp8", "mxfp4")
+    assert v_layout in (0, 1) and (v_layout == 0 or kv == "bf16")
     kp, vp = k_pool.copy(), v_pool.copy()
     ks = None if k_scale is None else k_scale.copy()
     vs = None if v_scale is None else v_scale.copy()
@@ -135,7 +137,10 @@ def kv_append(*, P, W, Hkv, D, k_new_bits, v_new_bits, k_pool, v_pool, k_scale,
                 vb = v_new_bits[p, i, h]
                 if kv == "bf16":
                     kp[page, h, slot, :] = kb
-                    vp[page, h, :, slot] = vb
+                    if v_layout:
+                        vp[page, h, slot, :] = vb
+                    else:
+                        vp[page, h, :, slot] = vb
                 elif kv == "mxfp4":
                     kx = (kb.astype(np.uint32) << 16).view(np.float32)
                     vx = (vb.astype(np.uint32) << 16).view(np.float32)

@@ -36,7 +36,8 @@
  * Storage it reads (the library's documented layout):
  *   q        uint16 bf16 bits  [P][W][Hq][D]
  *   k_pool   [num_pages][Hkv][16][D]   bf16 bits or e4m3fn bytes
- *   v_pool   [num_pages][Hkv][D][16]   (each page-head stored transposed)
+ *   v_pool   [num_pages][Hkv][D][16]   (each page-head stored transposed), or
+ *            [num_pages][Hkv][16][D] like K for bf16 with token-major values
  *   k_scale, v_scale  fp32 [num_pages][Hkv][16]  (fp8 only)
  *   MXFP4 (two E2M1 codes per byte, the even element in the low nibble):
  *   k_pool   [num_pages][Hkv][16][D/2]  byte (t, i): elements 2i, 2i+1 of token t
@@ -100,7 +101,8 @@ double oracle_e8m0_to_double(uint8_t e)
     return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127);
 }
 
-enum { ORACLE_KV_BF16 = 0, ORACLE_KV_E4M3 = 1, ORACLE_KV_MXFP4 = 2 };
+/* ORACLE_KV_BF16_VTOK: bf16 pools whose value pages are token-major like K */
+enum { ORACLE_KV_BF16 = 0, ORACLE_KV_E4M3 = 1, ORACLE_KV_MXFP4 = 2, ORACLE_KV_BF16_VTOK = 3 };
 
 typedef struct {
     int P, W, Hq, Hkv, D, num_pages, bt_stride, causal, kv_fmt;
@@ -150,6 +152,9 @@ static double v_elem(const oracle_in *in, int64_t page, int kvh, int slot, int d
         uint8_t code = nibble(((const uint8_t *)in->v_pool)[byte], slot & 1);
         return oracle_e2m1_to_double(code) * mx_scale(in->v_scale, in, page, kvh, slot, d, 1);
     }
+    if (in->kv_fmt == ORACLE_KV_BF16_VTOK)
+        return oracle_bf16_to_double(
+            ((const uint16_t *)in->v_pool)[((page * in->Hkv + kvh) * ORACLE_PAGE + slot) * in->D + d]);
     int64_t idx = ((page * in->Hkv + kvh) * in->D + d) * ORACLE_PAGE + slot;
     if (in->kv_fmt == ORACLE_KV_E4M3) {
         double sc = (double)((const float *)in->v_scale)[(page * in->Hkv + kvh) * ORACLE_PAGE + slot];
@@ -221,9 +226,9 @@ int oracle_attention(int P, int W, int Hq, int Hkv, int D, int num_pages, int bt
 {
     if (P < 1 || W < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || bt_stride < 1)
         return -1;
-    if (kv_fmt < ORACLE_KV_BF16 || kv_fmt > ORACLE_KV_MXFP4)
+    if (kv_fmt < ORACLE_KV_BF16 || kv_fmt > ORACLE_KV_BF16_VTOK)
         return -1;
-    if (kv_fmt != ORACLE_KV_BF16 && (!k_scale || !v_scale))
+    if ((kv_fmt == ORACLE_KV_E4M3 || kv_fmt == ORACLE_KV_MXFP4) && (!k_scale || !v_scale))
         return -1;
     if (kv_fmt == ORACLE_KV_MXFP4 && D % 32)
         return -1;

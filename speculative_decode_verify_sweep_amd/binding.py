@@ -23,6 +23,8 @@ SMALLW_ENOMEM = -5
 SMALLW_KV_BF16 = 0
 SMALLW_KV_FP8_E4M3 = 1
 SMALLW_KV_MXFP4 = 2
+SMALLW_V_DMAJOR = 0
+SMALLW_V_TOKEN_MAJOR = 1
 
 
 class SmallwError(RuntimeError):
@@ -40,7 +42,8 @@ class smallw_problem(ctypes.Structure):
                 ("scale", ctypes.c_float), ("num_cus", ctypes.c_int32),
                 ("force_splits", ctypes.c_int32),
                 ("split_pages", ctypes.c_int32),
-                ("window_left", ctypes.c_int32)]
+                ("window_left", ctypes.c_int32),
+                ("v_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -99,10 +102,12 @@ class Plan:
 
 def make_problem(*, num_reqs, window, num_q_heads, num_kv_heads, head_dim, num_pages,
                  max_pages_per_req, causal, kv_dtype=SMALLW_KV_BF16, scale=0.0, num_cus=0,
-                 force_splits=0, split_pages=0, window_left=0, page_size=16) -> smallw_problem:
+                 force_splits=0, split_pages=0, window_left=0, page_size=16,
+                 v_layout=0) -> smallw_problem:
     return smallw_problem(num_reqs, window, num_q_heads, num_kv_heads, head_dim, page_size,
                           num_pages, max_pages_per_req, int(causal), int(kv_dtype),
-                          float(scale), num_cus, force_splits, split_pages, window_left)
+                          float(scale), num_cus, force_splits, split_pages, window_left,
+                          int(v_layout))
 
 
 def small_w_attention_plan(problem: smallw_problem, seq_lens_host) -> Plan:

@@ -8,7 +8,8 @@
 // one shared pool addressed by a batched block table and per-request lengths.
 // Token i of request p sits at position L_p - W + i; its K row goes to slot
 // pos % 16 of pool page block_table[p][pos / 16] and its V row to the same
-// slot of the transposed (d-major) value page.  For e4m3 pools each (token,
+// slot of the transposed (d-major) value page, or, for a bf16 pool laid out
+// token-major, to row pos % 16 of the value page like K.  For e4m3 pools each (token,
 // KV head) row gets scale = amax|x| / 448 (1 when the row is all zero) and
 // codes = round-to-nearest-even of x / scale on the OCP e4m3fn grid, all in
 // fp32 (IEEE division), so the codes are exactly reproducible.  For MXFP4
@@ -38,6 +39,7 @@ struct AppendParams {
     const int32_t* bt;
     const int32_t* seq;
     int32_t P, W, Hkv, bt_stride, num_pages;
+    int32_t v_tok;  // bf16 pools only: V pages token-major [16][D] like K
 };
 
 constexpr float kE4m3Max = 448.0f;
@@ -174,11 +176,20 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams a) {
         }
     } else if constexpr (!FP8) {
         uint16_t* kp = reinterpret_cast<uint16_t*>(a.k_pool) + (ph * 16 + slot) * D + E * l;
-        uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool) + ph * D * 16 + slot;
+        if (a.v_tok) {
+            uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool) + (ph * 16 + slot) * D + E * l;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            kp[e] = kb[e];
-            vp[int64_t(E * l + e) * 16] = vb[e];
+            for (int e = 0; e < E; ++e) {
+                kp[e] = kb[e];
+                vp[e] = vb[e];
+            }
+        } else {
+            uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool) + ph * D * 16 + slot;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                kp[e] = kb[e];
+                vp[int64_t(E * l + e) * 16] = vb[e];
+            }
         }
     } else {
         float km = 0.f, vm = 0.f;
@@ -247,6 +258,7 @@ extern "C" int small_w_kv_append(const smallw_plan* pl, const void* k_new, const
     a.Hkv = pl->prob.num_kv_heads;
     a.bt_stride = pl->prob.max_pages_per_req;
     a.num_pages = pl->prob.num_pages;
+    a.v_tok = pl->prob.v_layout == SMALLW_V_TOKEN_MAJOR;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     switch (pl->prob.head_dim) {

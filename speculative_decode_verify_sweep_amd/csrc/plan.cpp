@@ -71,6 +71,7 @@ int validate(const smallw_problem& pr, const int32_t* seq) {
         pr.head_dim < 1 || pr.page_size < 1 || pr.num_pages < 1 || pr.max_pages_per_req < 1 ||
         pr.num_cus < 0 || pr.force_splits < 0 || pr.split_pages < 0 || pr.window_left < 0)
         return SMALLW_EINVAL;
+    if (pr.v_layout != SMALLW_V_DMAJOR && pr.v_layout != SMALLW_V_TOKEN_MAJOR) return SMALLW_EINVAL;
     if (pr.force_splits > 0 && pr.split_pages > 0) return SMALLW_EINVAL;
     if (pr.causal != 0 && pr.causal != 1) return SMALLW_EINVAL;
     if (pr.kv_dtype != SMALLW_KV_BF16 && pr.kv_dtype != SMALLW_KV_FP8_E4M3 &&
@@ -83,6 +84,8 @@ int validate(const smallw_problem& pr, const int32_t* seq) {
     if (pr.page_size != SMALLW_PAGE_SIZE) return SMALLW_EUNSUPPORTED;
     if (pr.head_dim != 64 && pr.head_dim != 128 && pr.head_dim != 256) return SMALLW_EUNSUPPORTED;
     if (pr.kv_dtype == SMALLW_KV_MXFP4 && pr.head_dim == 64) return SMALLW_EUNSUPPORTED;
+    if (pr.v_layout == SMALLW_V_TOKEN_MAJOR && pr.kv_dtype != SMALLW_KV_BF16)
+        return SMALLW_EUNSUPPORTED;
     const int64_t rows = int64_t(pr.window) * (pr.num_q_heads / pr.num_kv_heads);
     if (rows > SMALLW_MAX_ROWS) return SMALLW_EUNSUPPORTED;
     if (!seq) return SMALLW_EINVAL;

@@ -208,6 +208,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // later.  The two halves of a row then share a bank slot, so a lane's bank
 // depends only on its row, as in a linear read, and each 1 KiB DMA instruction
 // still reads 1 KiB of contiguous HBM.
+// VT (bf16 pools laid out token-major, V pages [16][D] like K): V rows are
+// swizzled like K, with hv(tau) = 2*((tau&3)|(((tau>>3)&1)<<2)) (masked to the
+// row), and the PV operand comes from ds_read_b64_tr_b16 transpose reads: in
+// each 16-lane group, lane 4q+e gets element e of the 8-byte piece lane 4j+q
+// addresses (j = 0..3), so lanes 4j..4j+3 address tokens 8g+4*a2+j of four
+// d-quads and one read returns four tokens of one d column per lane.
 // ----------------------------------------------------------------------------
 constexpr int kSweepWaves = 8;
 constexpr int kSweepThreads = 64 * kSweepWaves;
@@ -365,9 +371,10 @@ __device__ __forceinline__ void finish_unit(const Params& a, const f32x4 (&acc)[
     }
 }
 
-template <int D, int NS, int KV, bool DECH>
+template <int D, int NS, int KV, bool DECH, bool VT = false>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     static_assert(KV == SMALLW_KV_BF16 || KV == SMALLW_KV_MXFP4, "e4m3 pools: sweep8_kernel");
+    static_assert(!VT || KV == SMALLW_KV_BF16, "token-major V is a bf16 layout");
     constexpr bool FP4 = KV == SMALLW_KV_MXFP4;
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
@@ -460,6 +467,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             const int tau = 16 * region_pg + tr;
             const int hsw = (((tau >> 1) & 12) | (tau & 3)) & (CPR - 1);
             goff[i] = uint32_t(tr * (2 * D) + (slot ^ hsw) * 16);
+        } else if constexpr (VT) {
+            const int tr = qc / CPR, slot = qc % CPR;
+            const int tau = 16 * region_pg + tr;
+            const int hv = (2 * ((tau & 3) | (((tau >> 3) & 1) << 2))) & (CPR - 1);
+            goff[i] = uint32_t(tr * (2 * D) + (slot ^ hv) * 16);
         } else {
             // LDS slot qc = 32*a + 16*h + r of its 1 KiB block holds half h of
             // row 16*(2*block + a) + r
@@ -698,6 +710,33 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // where this lane's V^T operand rows start: the bf16 ring stage, or the
     // V staging buffer of the 4-bit format (the two V pages only)
     const uint32_t va = LOWP ? vaddr - 2 * BF_PAGE : vaddr;
+    // VT: the two transpose-read addresses of d tile 0 (tile dt: xor 32 dt);
+    // read a2 covers tokens 8g + 4a2 .. 8g + 4a2 + 3 of the chunk
+    uint32_t vtA[2] = {};
+    if constexpr (VT) {
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+            const int tau = 8 * g + 4 * a2 + (ln >> 2);
+            const int q = ln & 3;
+            const int y = (tau & 3) | (((tau >> 3) & 1) << 2);
+            vtA[a2] = uint32_t(2 * BF_PAGE + (tau >> 4) * BF_PAGE + (tau & 15) * (2 * D)) |
+                      uint32_t((32 * y + 16 * (q >> 1) + 8 * (q & 1)) & (2 * D - 1));
+        }
+    }
+    // one d tile of the PV operand (8 tokens x this lane's d column)
+    typedef short v4s_t __attribute__((ext_vector_type(4)));
+    auto vread = [&](const uint8_t* vst, int dt) -> u32x4 {
+        if constexpr (VT) {
+            const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t*)(vst + (vtA[0] ^ uint32_t(32 * dt))));
+            const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t*)(vst + (vtA[1] ^ uint32_t(32 * dt))));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            return u32x4{l2.x, l2.y, h2.x, h2.y};
+        } else {
+            return *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
+        }
+    };
 
     f32x4 acc[DT];
 #pragma unroll
@@ -768,7 +807,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         if constexpr (VPRE) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                vraw[dt] = *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
+                vraw[dt] = vread(vst, dt);
             __builtin_amdgcn_sched_barrier(0);
         }
         float x[8];
@@ -808,7 +847,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         for (int dt = 0; dt < DT; ++dt) {
             u32x4 raw;
             if constexpr (VPRE) raw = vraw[dt];
-            else raw = *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
+            else raw = vread(vst, dt);
             if constexpr (TAIL) {
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2)
@@ -1715,6 +1754,9 @@ int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* e
                         : launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4, false>, pl->U, kSweepThreads,
                                  a, st, ev0, ev1, "sweep kernel launch");
     }
+    if (pl->prob.v_layout == SMALLW_V_TOKEN_MAJOR)
+        return launch(sweep_kernel<D, 4, SMALLW_KV_BF16, false, true>, pl->U, kSweepThreads, a, st,
+                      ev0, ev1, "sweep kernel launch");
     return launch(sweep_kernel<D, 4, SMALLW_KV_BF16, false>, pl->U, kSweepThreads, a, st, ev0, ev1,
                   "sweep kernel launch");
 }

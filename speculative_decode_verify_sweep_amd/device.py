@@ -46,7 +46,8 @@ def plan_for(w, *, num_cus: int = 0, force_splits: int = 0, split_pages: int = 0
                         max_pages_per_req=w.block_table.shape[1], causal=w.causal,
                         kv_dtype=KV_DTYPES[w.kv],
                         scale=w.scale, num_cus=num_cus, force_splits=force_splits,
-                        split_pages=split_pages, window_left=getattr(w, "window_left", 0))
+                        split_pages=split_pages, window_left=getattr(w, "window_left", 0),
+                        v_layout=getattr(w, "v_layout", 0))
     return B.small_w_attention_plan(pr, w.seq_lens)
 
 

@@ -52,6 +52,7 @@ int main(int argc, char** argv) {
         pr.force_splits = pick<int32_t>({0, 0, 0, 1, 2, 3, 17, 200});
         pr.split_pages = pr.force_splits ? 0 : pick<int32_t>({0, 0, 0, 1, 5, 9, 65});
         pr.window_left = pick<int32_t>({0, 0, 1, 7, 4096, 1 << 30});
+        pr.v_layout = pr.kv_dtype == 0 ? pick<int32_t>({0, 1}) : 0;
         const int64_t cap = int64_t(pr.max_pages_per_req) * 16;
         std::vector<int32_t> seq(SMALLW_MAX_REQS + 1);
         for (auto& L : seq) {
@@ -60,7 +61,7 @@ int main(int argc, char** argv) {
             if (L > cap) L = int32_t(cap);
         }
         if (std::uniform_int_distribution<int>(0, 9)(rng) < 3) {
-            switch (std::uniform_int_distribution<int>(0, 14)(rng)) {
+            switch (std::uniform_int_distribution<int>(0, 15)(rng)) {
                 case 0: pr.num_reqs = pick<int32_t>({0, -1, 257}); break;
                 case 1: pr.window = pick<int32_t>({0, 17}); break;
                 case 2: pr.num_kv_heads = pick<int32_t>({0, 3}); break;
@@ -76,6 +77,7 @@ int main(int argc, char** argv) {
                 case 11: pr.split_pages = -2; break;
                 case 12: pr.window_left = -1; break;
                 case 13: seq[0] = pick<int32_t>({-1, int32_t(cap + 1)}); break;
+                case 14: pr.v_layout = pick<int32_t>({-1, 2}); break;
                 default: if (pr.window > 1) { pr.causal = 1; seq[0] = pr.window - 1; } break;
             }
         }

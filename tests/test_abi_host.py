@@ -65,6 +65,7 @@ def base_problem(**kw):
     ("force_splits", -2, B.SMALLW_EINVAL),
     ("split_pages", -1, B.SMALLW_EINVAL),
     ("window_left", -5, B.SMALLW_EINVAL),
+    ("v_layout", 2, B.SMALLW_EINVAL),
 ])
 def test_plan_rejects_bad_problems(field, value, code):
     kw = {field: value}
@@ -209,6 +210,14 @@ def test_scaled_formats_require_scales(kv):
     rc = B.lib().small_w_attention_run(plan.handle, fake, fake, fake, None, None, fake, fake,
                                        fake, fake, None, 0, None)
     assert rc == B.SMALLW_EINVAL
+
+
+def test_token_major_values_are_a_bf16_layout():
+    for kv in (B.SMALLW_KV_FP8_E4M3, B.SMALLW_KV_MXFP4):
+        with pytest.raises(B.SmallwError) as e:
+            sw.small_w_attention_plan(base_problem(kv_dtype=kv, head_dim=128, v_layout=1), [260])
+        assert e.value.code == B.SMALLW_EUNSUPPORTED
+    sw.small_w_attention_plan(base_problem(v_layout=1), [260])
 
 
 def test_mxfp4_needs_head_dim_128_or_256():

@@ -53,7 +53,10 @@ def dense_kv(w):
             V[p, :, :L] = vd.transpose(1, 0, 2)
             continue
         kc = w.k_pool[phys, :, slot, :]                  # [L][Hkv][D]
-        vc = w.v_pool[phys, :, :, slot]                  # [L][Hkv][D]
+        if getattr(w, "v_layout", 0) == 1:               # token-major value pages
+            vc = w.v_pool[phys, :, slot, :]
+        else:
+            vc = w.v_pool[phys, :, :, slot]              # [L][Hkv][D]
         if w.kv == "fp8":
             kd = torch.from_numpy(np.ascontiguousarray(kc)).view(torch.float8_e4m3fn).double()
             vd = torch.from_numpy(np.ascontiguousarray(vc)).view(torch.float8_e4m3fn).double()
@@ -151,6 +154,57 @@ def test_oracle_matches_dense_brute_force(case):
     assert np.isfinite(o).all()
     np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l, lb, rtol=1e-13, atol=1e-12)
+
+
+VTOK_CASES = [c for c in CASES if c.get("kv", "bf16") == "bf16"]
+
+
+@pytest.mark.parametrize("case", range(len(VTOK_CASES)))
+def test_oracle_reads_token_major_value_pages(case):
+    """bf16 value pages stored token-major ([page][head][16][D], like K): the
+    generator lays the same values out as the transpose of the d-major pool,
+    the oracle matches the brute force (which gathers V by its own indexing)
+    and is bitwise its own d-major result on those values."""
+    spec = VTOK_CASES[case]
+    wt = tiny(seed=40 + case, v_layout=1, **spec)
+    wd = tiny(seed=40 + case, v_layout=0, **spec)
+    np.testing.assert_array_equal(wt.v_pool.transpose(0, 1, 3, 2), wd.v_pool)
+    o, l = oracle.attention(wt)
+    ob, lb = brute(wt)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=1e-13, atol=1e-12)
+    od, ld = oracle.attention(wd)
+    np.testing.assert_array_equal(o, od)
+    np.testing.assert_array_equal(l, ld)
+    if spec["D"] != 16:   # reading a d-major pool as token-major changes the output
+        wrong = dataclasses.replace(wt, v_pool=np.ascontiguousarray(
+            wd.v_pool.reshape(wt.v_pool.shape)))
+        assert not np.array_equal(oracle.attention(wrong)[0], o)
+
+
+def test_oracle_rejects_token_major_low_precision_pools():
+    w = tiny(kv="fp8", D=16)
+    with pytest.raises(ValueError):
+        oracle.attention(dataclasses.replace(w, v_layout=1))
+
+
+def test_oracle_append_token_major_is_the_transposed_append():
+    wt = tiny(P=2, Hq=4, Hkv=2, D=32, ctx=(40, 5), W=4, seed=72, v_layout=1)
+    wd = tiny(P=2, Hq=4, Hkv=2, D=32, ctx=(40, 5), W=4, seed=72, v_layout=0)
+    rng = np.random.default_rng(5)
+    kn = to_bf16_bits(rng.standard_normal((2, 4, 2, 32), dtype=np.float32))
+    vn = to_bf16_bits(rng.standard_normal((2, 4, 2, 32), dtype=np.float32))
+    out = {}
+    for lay, w in ((1, wt), (0, wd)):
+        out[lay] = oracle.kv_append(P=2, W=4, Hkv=2, D=32, kv="bf16", k_new_bits=kn,
+                                    v_new_bits=vn, k_pool=w.k_pool, v_pool=w.v_pool,
+                                    k_scale=None, v_scale=None, block_table=w.block_table,
+                                    seq_lens=w.seq_lens, num_pages=w.num_pages, v_layout=lay)
+    np.testing.assert_array_equal(out[1][0], out[0][0])
+    np.testing.assert_array_equal(out[1][1].transpose(0, 1, 3, 2), out[0][1])
+    pos = int(wt.seq_lens[0]) - 4 + 2                 # token 2 of request 0
+    pg = int(wt.block_table[0, pos // 16])
+    np.testing.assert_array_equal(out[1][1][pg, 1, pos % 16, :], vn[0, 2, 1])
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))

@@ -3,7 +3,8 @@
 Storage layout (the library's documented layout):
   q         bf16 bits, uint16 [P][W][Hq][D]
   k_pool    [num_pages][Hkv][16][D]     uint16 bf16 bits, or uint8 e4m3fn codes
-  v_pool    [num_pages][Hkv][D][16]     each page-head stored transposed
+  v_pool    [num_pages][Hkv][D][16]     each page-head stored transposed, or
+            [num_pages][Hkv][16][D]     like K (bf16, v_layout = 1: token-major)
   k_scale   fp32 [num_pages][Hkv][16]   fp8 only (dequantised value = code * scale)
   v_scale   fp32 [num_pages][Hkv][16]
   MXFP4 (kv = "mxfp4"): uint8, two E2M1 codes per byte, the even element in the
@@ -106,6 +107,7 @@ class Workload:
     seq_lens: np.ndarray         # int32 [P]
     seed: int
     window_left: int = 0         # sliding window (keys per row); 0 = none
+    v_layout: int = 0            # 0: value pages d-major; 1: token-major (bf16)
 
     @property
     def G(self) -> int:
@@ -150,6 +152,8 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
     pool_pages = max(pool_pages, need)
     fp8 = spec["kv"] == "fp8"
     fp4 = spec["kv"] == "mxfp4"
+    vtok = int(spec.get("v_layout", 0)) == 1
+    assert not vtok or spec["kv"] == "bf16", "token-major value pages are a bf16 layout"
 
     q = to_bf16_bits(rng.standard_normal((P, Wn, Hq, D), dtype=np.float32))
 
@@ -176,7 +180,8 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
         v_scale = np.full((pool_pages, Hkv, PAGE), np.nan, dtype=np.float32)
     else:
         k_pool = np.full((pool_pages, Hkv, PAGE, D), 0x7FC0, dtype=np.uint16)
-        v_pool = np.full((pool_pages, Hkv, D, PAGE), 0x7FC0, dtype=np.uint16)
+        v_pool = np.full((pool_pages, Hkv, PAGE, D) if vtok else (pool_pages, Hkv, D, PAGE),
+                         0x7FC0, dtype=np.uint16)
         k_scale = v_scale = None
     if not poison:
         k_pool[...] = 0
@@ -225,6 +230,8 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
                     k_pool[phys, :, :t1 - t0, :] = blk
                     if fp8:
                         k_scale[phys, :, :t1 - t0] = sc[:, t0:t1]
+                elif vtok:
+                    v_pool[phys, :, :t1 - t0, :] = blk
                 else:
                     v_pool[phys, :, :, :t1 - t0] = blk.transpose(0, 2, 1)
                     if fp8:
@@ -235,4 +242,4 @@ def make_workload(name: str | None = None, *, W: int | None = None, seed: int | 
                     num_pages=pool_pages, max_pages=max_pages, q=q, k_pool=k_pool,
                     v_pool=v_pool, k_scale=k_scale, v_scale=v_scale, block_table=bt,
                     seq_lens=np.asarray(seq, dtype=np.int32), seed=seed,
-                    window_left=int(spec.get("window_left", 0)))
+                    window_left=int(spec.get("window_left", 0)), v_layout=int(vtok))
