@@ -49,7 +49,7 @@ int main(int argc, char **argv)
     int bad = 0;
     for (int it = 0; it < iters; ++it) {
         int P = 1 + rnd() % 3, W = 1 + rnd() % 4, Hkv = 1 + rnd() % 2, G = 1 + rnd() % 3;
-        int Hq = Hkv * G, fmt = rnd() % 3;
+        int Hq = Hkv * G, fmt = rnd() % 4;   /* 3: bf16, token-major V pages */
         int D = fmt == 2 ? 32 * (1 + rnd() % 2) : (rnd() % 2 ? 8 : 64);
         int bt_stride = 1 + rnd() % 4, num_pages = P * bt_stride + rnd() % 3;
         int causal = rnd() % 2, cap = 16 * bt_stride;
@@ -63,9 +63,9 @@ int main(int argc, char **argv)
         for (int i = 0; i < P * bt_stride; ++i)
             bt[i] = rnd() % num_pages;
         size_t elems = (size_t)num_pages * Hkv * 16 * D;
-        size_t pool_bytes = fmt == 0 ? 2 * elems : fmt == 1 ? elems : elems / 2;
+        size_t pool_bytes = fmt == 0 || fmt == 3 ? 2 * elems : fmt == 1 ? elems : elems / 2;
         void *kp = fill(pool_bytes), *vp = fill(pool_bytes), *ks = NULL, *vs = NULL;
-        if (fmt == 0) {   /* finite bf16 values */
+        if (fmt == 0 || fmt == 3) {   /* finite bf16 values */
             uint16_t *k16 = kp, *v16 = vp;
             for (size_t i = 0; i < elems; ++i) {
                 k16[i] = bf16_of((float)((int)(rnd() % 2001) - 1000) / 400.f);
