@@ -37,7 +37,7 @@ CTX = 65536
 WINDOWS = (1, 8, 12, 16)
 COUNTERS = os.path.join(ROOT, "profiles", "sweep_verify64k_w16_counters.json")
 SWEEP_SRC = os.path.join(ROOT, "speculative_decode_verify_sweep_amd", "csrc", "smallw.hip")
-SWEEP_KERNEL = "sweep_kernel<256, 4, 0, false>"   # bf16 KV (format code 0), head_dim 256, 4-chunk ring
+SWEEP_KERNEL = "sweep_kernel<256, 4, 0, false, false>"  # bf16 KV (format 0), head_dim 256, 4-chunk ring, d-major V
 COMBINE_KERNEL = "combine_kernel<256, false>"
 
 
@@ -279,11 +279,15 @@ def main():
                   dict(name="verify64k", W=16, window_left=4096)),
                  ("verify64k W=16 token-major V", dict(name="verify64k", W=16, v_layout=1)),
                  ("verify64k W=1 token-major V", dict(name="verify64k", W=1, v_layout=1)),
-                 ("draft token-major V", dict(name="draft", v_layout=1))]
+                 ("draft token-major V", dict(name="draft", v_layout=1)),
+                 # the same pages in pool order: what the random placement costs
+                 ("verify64k W=16 pages in pool order",
+                  dict(name="verify64k", W=16, placement="in_order"))]
         for label, spec in specs:
+            extra = {"placement": spec["placement"]} if "placement" in spec else {}
             wl = make_workload(spec["name"], W=spec.get("W"),
                                window_left=spec.get("window_left", 0),
-                               v_layout=spec.get("v_layout", 0))
+                               v_layout=spec.get("v_layout", 0), **extra)
             dd = dv.upload(wl)
             pl = dv.plan_for(wl, split_pages=spec.get("split_pages", 0))
             wsb = dv.workspace_for(pl)
