@@ -37,6 +37,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s2_t __attribute__((ext_vector_type(2)));  // packed fp8 pair results
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPage = SMALLW_PAGE_SIZE;
@@ -1216,7 +1217,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         float x[16];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const f32x4 kq = sp[4 * g + tt] * a.scale_log2;  // scores in base-2 units
+            const f32x4 kq = sp[4 * g + tt];  // K scales; the softmax scale goes in the exponent
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * tt + i;
@@ -1227,7 +1228,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         float mx = x[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-        mx = wave_max_groups(mx);
+        mx = wave_max_groups(mx) * a.scale_log2;  // base 2 (the scale is positive)
         const bool grow = mx > m_run + kRescaleSlack;
         const float m_new = grow ? ceilf(mx) : m_run;
         if constexpr (PEND) {
@@ -1240,7 +1241,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            pw[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+            pw[e] = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
             ls += pw[e];
         }
         l_run += ls;
@@ -1262,24 +1263,28 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         m = pair16(m, true);
         int ex = 0;
         (void)frexpf(m, &ex);
-        X = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
+        // X >= -119 keeps both conversion scales below normal floats
+        X = m > 0.f ? min(max(ex - 8, -119), 127) : 0;
+        // hi = RNE(p / 2^X), lo = RNE((p - hi 2^X) / 2^(X-4)): the scaled converts
+        // divide by (and the reverse one multiplies by) an exact power of two,
+        // and p - hi 2^X is exact, so this is the plain split without the
+        // separate scalings
+        const float s_hi = __uint_as_float(uint32_t(X + 127) << 23);
+        const float s_lo = __uint_as_float(uint32_t(X + 123) << 23);
 #pragma unroll
         for (int e = 0; e < 16; e += 4) {
-            float x4[4], y4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x4[i] = ldexpf(pw[e + i], -X);
-            int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[0], x4[1], 0, false);
-            hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[2], x4[3], hw, true);
-            const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-            const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-            y4[0] = (x4[0] - h01[0]) * 16.f;
-            y4[1] = (x4[1] - h01[1]) * 16.f;
-            y4[2] = (x4[2] - h23[0]) * 16.f;
-            y4[3] = (x4[3] - h23[1]) * 16.f;
-            int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[0], y4[1], 0, false);
-            lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[2], y4[3], lw, true);
+            s2_t h2 = {0, 0}, l2 = {0, 0};
+            h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, pw[e], pw[e + 1], s_hi, false);
+            h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, pw[e + 2], pw[e + 3], s_hi, true);
+            const int hw = __builtin_bit_cast(int, h2);
+            const auto h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, s_hi, false);
+            const auto h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, s_hi, true);
+            l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, pw[e] - h01[0], pw[e + 1] - h01[1],
+                                                          s_lo, false);
+            l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, pw[e + 2] - h23[0],
+                                                          pw[e + 3] - h23[1], s_lo, true);
             hi[HO + e / 4] = hw;
-            lo[HO + e / 4] = lw;
+            lo[HO + e / 4] = __builtin_bit_cast(int, l2);
         }
     };
 
