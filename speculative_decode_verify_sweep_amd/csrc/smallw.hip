@@ -815,7 +815,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = e >> 2, j = e & 3;
-            x[e] = (s4[t][0][j] + s4[t][1][j]) * a.scale_log2;
+            x[e] = s4[t][0][j] + s4[t][1][j];  // the softmax scale goes in the exponent
             if (TAIL) {
                 const int j = j0 + 8 * g + e;
                 x[e] = (j <= hi_tok && j >= lo_tok) ? x[e] : -INFINITY;
@@ -823,7 +823,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = wave_max_groups(mx);
+        mx = wave_max_groups(mx) * a.scale_log2;  // base 2 (the scale is positive)
         // row-uniform: the four lanes of a row hold the same mx and m_run
         const bool grow = mx > m_run + kRescaleSlack;
         if (__any(grow)) {
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float pe[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
         l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
         // tokens past the unit's keys may hold anything (even NaN): zero their
         // V^T elements
