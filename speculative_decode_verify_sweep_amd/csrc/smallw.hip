@@ -1017,11 +1017,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         kpg[j] = pg;
     }
     const bool issues_scale = w >= 6;
-    const int nk_w = (w < KI ? 1 : 0) + (w + 8 < KI ? 1 : 0) + (issues_scale ? 1 : 0);
-    int nvq[2] = {0, 0};
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-        for (int i = 0; i < KI; ++i) nvq[q] += ((i + q * KI) & 7) == w ? 1 : 0;
     const uint32_t kr_base = uint32_t(reinterpret_cast<uintptr_t>(kring));
     const uint32_t vr_base = uint32_t(reinterpret_cast<uintptr_t>(vring));
     const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
@@ -1075,13 +1070,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         }
     };
 
-    // ---- prologue: issue order K0 K1 V0 K2; then Q (one round trip for all of
-    // it).  Each wave's issue order continues K3 V1 | K4 | K5 V2 | K6 | ...:
-    // ring step t issues K(t + 3) and, for even t, the V^T of step t/2 + 1, so
-    // step g's V^T always follows K(2g + 1)
+    // ---- prologue: step 0's K and V^T, then Q (one round trip for all of it).
+    // Each step then issues the next step's loads right after its barrier, so
+    // one step is in flight while the current one computes.
     for (int t = 0; t < min(2, nchunks); ++t) issue_k(t);
     if (nchunks > 0) issue_v(0);
-    if (nchunks > 2) issue_k(2);
     bf16x8_t qf[4 * KS4];
     {
         const bool valid = has_tile && r < a.R;
@@ -1204,87 +1197,109 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
             }
     };
 
-    // ---- softmax of chunk t (branch-free), then its weights (row ln, page g,
-    // tokens 0..15, times the V scales) split into e4m3 parts; a pending first
-    // chunk of the same step (PEND) shifts its exponent Xp when the max moves
-    auto softmax_split = [&](int t, const f32x4 (&s4)[4], i32x8& hi, i32x8& lo, int& X, int& Xp,
-                             auto tail_tag, auto pend_tag) {
+    // ---- softmax of one PV step (branch-free): the scores of its two chunks
+    // share one running max; then each chunk's weights (row ln, page g, tokens
+    // 0..15, times the V scales) are split into e4m3 parts of their 32-token
+    // block, p = hi 2^X + lo 2^(X-4): chunk A's into dwords 0..3 of the MFMA's
+    // B operands with exponent XA, chunk B's into dwords 4..7 with XB.  A
+    // masked step may lack chunk B (hasB false): its scores are masked out.
+    auto softmax_step = [&](int tA, const f32x4 (&sa)[4], const f32x4 (&sb)[4], bool hasB,
+                            i32x8& hi, i32x8& lo, int& XA, int& XB, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        constexpr bool PEND = decltype(pend_tag)::value;  // second chunk: dwords 4..7
-        constexpr int HO = PEND ? 4 : 0;
-        const f32x4* sp = reinterpret_cast<const f32x4*>(&scl[t % NK][0]);
-        const int j0 = (un.pb + 4 * t + g) * kPage;  // absolute position of token 0 of page g
-        float x[16];
+        const f32x4* spa = reinterpret_cast<const f32x4*>(&scl[tA % NK][0]);
+        const f32x4* spb = reinterpret_cast<const f32x4*>(&scl[(tA + 1) % NK][0]);
+        const int j0 = (un.pb + 4 * tA + g) * kPage;  // absolute position of token 0 of page g
+        // x[e]: chunk A, page g, token e; x[16 + e]: chunk B (64 tokens later).
+        // K scales only: the softmax scale goes in the exponent's FMA
+        float x[32];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const f32x4 kq = sp[4 * g + tt];  // K scales; the softmax scale goes in the exponent
+            const f32x4 ka = spa[4 * g + tt], kb = spb[4 * g + tt];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * tt + i;
-                x[e] = s4[tt][i] * kq[i];
-                if (TAIL) x[e] = (j0 + e <= hi_tok && j0 + e >= lo_tok) ? x[e] : -INFINITY;
+                x[e] = sa[tt][i] * ka[i];
+                x[16 + e] = sb[tt][i] * kb[i];
+                if (TAIL) {
+                    x[e] = (j0 + e <= hi_tok && j0 + e >= lo_tok) ? x[e] : -INFINITY;
+                    x[16 + e] = (hasB && j0 + 64 + e <= hi_tok && j0 + 64 + e >= lo_tok)
+                                    ? x[16 + e] : -INFINITY;
+                }
             }
         }
-        float mx = x[0];
+        float mx = fmaxf(x[0], x[16]);
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(x[e], x[16 + e]));
         mx = wave_max_groups(mx) * a.scale_log2;  // base 2 (the scale is positive)
         const bool grow = mx > m_run + kRescaleSlack;
         const float m_new = grow ? ceilf(mx) : m_run;
-        if constexpr (PEND) {
-            if (grow && m_run != -INFINITY) Xp = max(Xp + int(m_run - m_new), -123);
-        }
         l_run *= grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // a power of two, or 0
         m_run = m_new;
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float pw[16];
-        float ls = 0.f;
+        float la = 0.f, lb = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            pw[e] = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
-            ls += pw[e];
+            x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
+            x[16 + e] = __builtin_amdgcn_exp2f(fmaf(x[16 + e], a.scale_log2, -m_use));
+            la += x[e];
+            lb += x[16 + e];
         }
-        l_run += ls;
-        const int vcnt = TAIL ? min(max(jend - j0, 0), 16) : 16;
+        l_run += la + lb;
+        const int ca = TAIL ? min(max(jend - j0, 0), 16) : 16;
+        const int cb = TAIL ? (hasB ? min(max(jend - j0 - 64, 0), 16) : 0) : 16;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const f32x4 vq = sp[16 + 4 * g + tt];
+            const f32x4 va = spa[16 + 4 * g + tt], vb = spb[16 + 4 * g + tt];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * tt + i;
                 // stale tokens (past the unit's keys) may carry NaN scales
-                pw[e] = (!TAIL || e < vcnt) ? pw[e] * vq[i] : 0.f;
+                x[e] = (!TAIL || e < ca) ? x[e] * va[i] : 0.f;
+                x[16 + e] = (!TAIL || e < cb) ? x[16 + e] * vb[i] : 0.f;
             }
         }
-        // block max over lanes l and l ^ 16 (one 32-token block)
-        float m = pw[0];
+        // block maxima over lanes l and l ^ 16 (one 32-token block each)
+        float ma = x[0], mb = x[16];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) m = fmaxf(m, pw[e]);
-        m = pair16(m, true);
-        int ex = 0;
-        (void)frexpf(m, &ex);
-        // X >= -119 keeps both conversion scales below normal floats
-        X = m > 0.f ? min(max(ex - 8, -119), 127) : 0;
+        for (int e = 1; e < 16; ++e) {
+            ma = fmaxf(ma, x[e]);
+            mb = fmaxf(mb, x[16 + e]);
+        }
+        ma = pair16(ma, true);
+        mb = pair16(mb, true);
+        auto expo = [](float m) {
+            int ex = 0;
+            (void)frexpf(m, &ex);
+            // >= -119 keeps both conversion scales below normal floats
+            return m > 0.f ? min(max(ex - 8, -119), 127) : 0;
+        };
+        XA = expo(ma);
+        XB = expo(mb);
         // hi = RNE(p / 2^X), lo = RNE((p - hi 2^X) / 2^(X-4)): the scaled converts
         // divide by (and the reverse one multiplies by) an exact power of two,
-        // and p - hi 2^X is exact, so this is the plain split without the
-        // separate scalings
-        const float s_hi = __uint_as_float(uint32_t(X + 127) << 23);
-        const float s_lo = __uint_as_float(uint32_t(X + 123) << 23);
+        // and p - hi 2^X is exact, so this is the plain split without separate
+        // scalings
 #pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-            s2_t h2 = {0, 0}, l2 = {0, 0};
-            h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, pw[e], pw[e + 1], s_hi, false);
-            h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, pw[e + 2], pw[e + 3], s_hi, true);
-            const int hw = __builtin_bit_cast(int, h2);
-            const auto h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, s_hi, false);
-            const auto h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, s_hi, true);
-            l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, pw[e] - h01[0], pw[e + 1] - h01[1],
-                                                          s_lo, false);
-            l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, pw[e + 2] - h23[0],
-                                                          pw[e + 3] - h23[1], s_lo, true);
-            hi[HO + e / 4] = hw;
-            lo[HO + e / 4] = __builtin_bit_cast(int, l2);
+        for (int c = 0; c < 2; ++c) {
+            const int X = c ? XB : XA;
+            const float s_hi = __uint_as_float(uint32_t(X + 127) << 23);
+            const float s_lo = __uint_as_float(uint32_t(X + 123) << 23);
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const float* pw = x + 16 * c + e;
+                s2_t h2 = {0, 0}, l2 = {0, 0};
+                h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, pw[0], pw[1], s_hi, false);
+                h2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h2, pw[2], pw[3], s_hi, true);
+                const int hw = __builtin_bit_cast(int, h2);
+                const auto h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, s_hi, false);
+                const auto h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, s_hi, true);
+                l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, pw[0] - h01[0], pw[1] - h01[1],
+                                                              s_lo, false);
+                l2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l2, pw[2] - h23[0], pw[3] - h23[1],
+                                                              s_lo, true);
+                hi[4 * c + e / 4] = hw;
+                lo[4 * c + e / 4] = __builtin_bit_cast(int, l2);
+            }
         }
     };
 
@@ -1359,69 +1374,47 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         }
     };
 
-    // ---- ring step of chunk t: wait for K(t) (odd t: and for the step's
-    // V^T, which follows K(t)), barrier, then issue K(t + 3) into the slot
-    // chunk t - 1 freed and, for even t, the V^T of step t/2 + 1 into the slots
-    // step t/2 - 1 freed (its PV ran at that step's end)
-    auto kcnt = [&](int x) { return x < nchunks ? nk_w : 0; };
-    auto vcnt_of = [&](int gi) {
-        return gi >= 0 && 2 * gi < nchunks ? nvq[0] + (2 * gi + 1 < nchunks ? nvq[1] : 0) : 0;
-    };
-    auto ring_step = [&](int t) {
-        if (t > 0) {
-            // this wave's loads issued after the ones needed now
-            const int younger = (t & 1)
-                ? kcnt(t + 1) + kcnt(t + 2) + vcnt_of((t + 1) >> 1)
-                : kcnt(t + 1) + vcnt_of(t >> 1) + kcnt(t + 2);
-            wait_vmcnt_dyn(younger);
-        }
+    // ---- ring step of PV step j: every load this wave has in flight is step
+    // j's (issued right after the previous step's barrier), so wait for all of
+    // them; the barrier then also frees the slots step j - 1 used, and the
+    // next step's K (chunks 2j + 2, 2j + 3) and V^T go into them
+    auto ring_step = [&](int j) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        const bool v_next = !(t & 1) && t + 2 < nchunks;
-        if (t + 3 < nchunks || v_next) {
-            const int lo_need = v_next ? 4 * t + 8 : 4 * t + 12;
-            const int hi_need = min(4 * t + 15, npages - 1);
+        const int tn = 2 * j + 2;
+        if (tn < nchunks) {
+            const int lo_need = 4 * tn, hi_need = min(4 * tn + 7, npages - 1);
             if (hi_need - tbase >= kPtab) {  // slide the page-table window (long units only)
                 tbase = lo_need;
                 fill_ptab(tbase);
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 __syncthreads();
             }
-            if (t + 3 < nchunks) issue_k(t + 3);
-            if (v_next) issue_v((t >> 1) + 1);
+            issue_k(tn);
+            if (tn + 1 < nchunks) issue_k(tn + 1);
+            issue_v(j + 1);
         }
     };
 
-    // ---- step j: scores and softmax of chunks 2j and 2j + 1 (the second may
-    // be absent in a masked step), then the step's PV MFMAs
+    // ---- step j: scores of chunks 2j and 2j + 1 (the second may be absent in
+    // a masked step), their softmax, then the step's PV MFMAs
     auto step = [&](int j, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int tA = 2 * j;
         const bool hasB = tA + 1 < nchunks;
         Step cur;
         cur.tA = tA;
-        cur.bhi = cur.blo = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        cur.XA = cur.XB = 0;
         cur.c0 = min(max(jend - (un.pb + tA * 4 + g) * kPage, 0), 16);
         cur.c1 = hasB ? min(max(jend - (un.pb + tA * 4 + 4 + g) * kPage, 0), 16) : 0;
-        ring_step(tA);
+        ring_step(j);
         if (has_tile) {
-            f32x4 s4[4];
-            qk(tA, s4);
-            softmax_split(tA, s4, cur.bhi, cur.blo, cur.XA, cur.XB, tail_tag, std::false_type{});
-        }
-        if (!TAIL || hasB) {
-            ring_step(tA + 1);  // its wait also covers this step's V^T
-            if (has_tile) {
-                f32x4 s4[4];
-                qk(tA + 1, s4);
-                softmax_split(tA + 1, s4, cur.bhi, cur.blo, cur.XB, cur.XA, tail_tag,
-                              std::true_type{});
-            }
-        } else {
-            wait_vmcnt<0>();  // the last chunk: this step's V^T may be the newest load
-            __syncthreads();
-        }
-        if (has_tile) {
+            f32x4 sa[4], sb[4];
+            qk(tA, sa);
+            if (!TAIL || hasB) qk(tA + 1, sb);
+            else
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) sb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            softmax_step(tA, sa, sb, hasB, cur.bhi, cur.blo, cur.XA, cur.XB, tail_tag);
             rescale_acc();
             pv_half(cur, std::integral_constant<int, 0>{}, tail_tag);
             pv_half(cur, std::integral_constant<int, 1>{}, tail_tag);
