@@ -1334,7 +1334,9 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
                 mask1[k2] = n1 == 4 ? ~0u : (1u << (8 * n1)) - 1u;
             }
         }
-        constexpr int DG = 1;  // d tiles per MFMA group
+        // d tiles per MFMA group (their V^T reads first)
+        constexpr int DG = DH < 4 ? DH : 4;
+        static_assert(DH % DG == 0, "whole groups per half");
 #pragma unroll
         for (int d0 = H * DH; d0 < (H + 1) * DH; d0 += DG) {
             i32x8 vop[DG];
@@ -1410,10 +1412,12 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
         if (has_tile) {
             f32x4 sa[4], sb[4];
             qk(tA, sa);
-            if (!TAIL || hasB) qk(tA + 1, sb);
-            else
+            if (!TAIL || hasB) {
+                qk(tA + 1, sb);
+            } else {
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) sb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
             softmax_step(tA, sa, sb, hasB, cur.bhi, cur.blo, cur.XA, cur.XB, tail_tag);
             rescale_acc();
             pv_half(cur, std::integral_constant<int, 0>{}, tail_tag);
