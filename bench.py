@@ -37,7 +37,7 @@ CTX = 65536
 WINDOWS = (1, 8, 12, 16)
 COUNTERS = os.path.join(ROOT, "profiles", "sweep_verify64k_w16_counters.json")
 SWEEP_SRC = os.path.join(ROOT, "speculative_decode_verify_sweep_amd", "csrc", "smallw.hip")
-SWEEP_KERNEL = "sweep_kernel<256, 4, 0, false, false>"  # bf16 KV (format 0), head_dim 256, 4-chunk ring, d-major V
+SWEEP_KERNEL = "sweep_kernel<256, 4, false>"  # bf16 KV, head_dim 256, 4-chunk ring, d-major V
 COMBINE_KERNEL = "combine_kernel<256, false>"
 
 

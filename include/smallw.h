@@ -152,8 +152,9 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  *                  for causal calls L_p == 0 or L_p >= W.
  *   out            receives a new plan; release it with ..._plan_destroy.
  * Splits: n_p = ceil(L_p/16) pages, n_eff of them streamed (fewer with a
- * sliding window); slots = num_cus * (1 if D == 256 else 2) (work units
- * resident per compute unit); a round holds max(1, floor(slots / Hkv)) splits.
+ * sliding window); slots = num_cus * (2 for a bf16 pool with D < 256, else 1)
+ * (work units resident per compute unit); a round holds max(1, floor(slots /
+ * Hkv)) splits.
  * S_p = 1 for an empty request, min(force_splits, n_eff) when forced, else
  * apportioned: every request starts at one split, and one more at a time goes
  * to the request with the most pages per split (n_eff / S_p; the lower index on
@@ -168,7 +169,8 @@ typedef struct smallw_plan smallw_plan; /* opaque, host-only, immutable */
  * N + 1) / 16), h0 = L - W (causal) or L - 1, are skipped: the formulas above
  * apply to the n_p - n_lo pages from n_lo on (row-exact pieces stay on the
  * absolute grid of multiples of B; the first one starts at n_lo moved down to
- * an even offset from its grid point, so two-page chunks line up in every call).
+ * a multiple of 2 pages (bf16) or 8 pages (e4m3, MXFP4) from its grid point, so
+ * the pages one step of the sweep groups line up in every call).
  * Returns SMALLW_EINVAL / SMALLW_EUNSUPPORTED on bad input (nothing allocated),
  * SMALLW_EDEVICE if num_cus == 0 and the device query fails, SMALLW_ENOMEM.
  */

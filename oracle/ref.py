@@ -38,12 +38,12 @@ def first_page(L: int, W: int, causal: bool, window_left: int) -> int:
 
 
 def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0, W=1,
-         causal=True, window_left=0):
+         causal=True, window_left=0, kv=None):
     """Split plan for one call.
 
     n_pg(p)     = ceil(L_p / 16);  n_lo(p) = first page any row needs (0 without a
                   sliding window);  n_eff(p) = n_pg - n_lo  pages streamed
-    slots       = num_cus * (1 if D == 256 else 2)          units resident per CU
+    slots       = num_cus * (2 if bf16 and D < 256 else 1)  units resident per CU
     round       = max(1, floor(slots / Hkv))     splits that one round of units holds
     S_p         = 1                          if n_pg(p) == 0
                 = ceil(n_pg/B) - floor(n_lo/B) if split_pages = B > 0 (row-exact mode)
@@ -58,15 +58,17 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
     split s covers pages n_lo + [floor(s*n_eff/S), floor((s+1)*n_eff/S)), or in
     row-exact mode the s-th piece of the absolute grid [k*B, (k+1)*B), the last
     split ending at n_pg and the first starting at n_lo moved down to a multiple
-    of 2 pages from its k*B, or of 8 pages for e4m3 pools (the pages the sweep
-    groups into one step then line up in every call)
+    of 2 pages from its k*B, or of 8 pages for e4m3 and MXFP4 pools (the pages
+    the sweep groups into one step then line up in every call); kv names the
+    storage format ("bf16", "fp8", "mxfp4"), by default fp8 if kv_fp8 else bf16
     """
     seq = [int(x) for x in seq_lens]
     assert len(seq) == P
     n_pg = [_ceil_div(L, PAGE) for L in seq]
     n_lo = [first_page(L, W, causal, window_left) for L in seq]
     n_eff = [n - lo for n, lo in zip(n_pg, n_lo)]
-    slots = num_cus * (1 if D == 256 else 2)
+    fmt = kv or ("fp8" if kv_fp8 else "bf16")
+    slots = num_cus * (2 if fmt == "bf16" and D < 256 else 1)
     splits = []
     for n, lo, ne in zip(n_pg, n_lo, n_eff):
         if n == 0:
@@ -93,9 +95,9 @@ def plan(*, P, Hkv, D, kv_fp8, seq_lens, num_cus, force_splits=0, split_pages=0,
     unit_off = [0]
     for s in splits:
         unit_off.append(unit_off[-1] + Hkv * s)
-    # pages one step of the sweep's arithmetic groups: 128-token PV steps for e4m3
-    # pools, two-page chunks otherwise (the library's written specification)
-    align = 8 if kv_fp8 else 2
+    # pages one step of the sweep's arithmetic groups: 128-token steps for e4m3
+    # and MXFP4 pools, two-page chunks for bf16 (the library's written specification)
+    align = 2 if fmt == "bf16" else 8
     units = []
     for p in range(P):
         S, n, lo, ne = splits[p], n_pg[p], n_lo[p], n_eff[p]

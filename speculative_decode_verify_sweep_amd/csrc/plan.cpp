@@ -9,8 +9,9 @@
 // the per-split pipeline start and the partial traffic stay small against the
 // KV stream:
 //   n_p   = ceil(L_p / 16), n_eff = pages streamed (n_p less a window's skip)
-//   slots = num_cus * (1 if D == 256 else 2)   (units resident per CU: a D=256
-//           unit needs one CU's VGPRs and LDS; smaller heads fit two)
+//   slots = num_cus * (2 if bf16 pool and D < 256 else 1)   (units resident
+//           per CU: a D=256 unit, and every e4m3 or MXFP4 unit, needs one CU's
+//           VGPRs; bf16 units of smaller heads fit two)
 //   round = max(1, floor(slots / Hkv))         (splits one round of units holds)
 //   S_p   = 1 (empty request) | min(force_splits, n_eff) | apportioned:
 //           every request starts at 1; while sum S < budget, the request with
@@ -126,7 +127,8 @@ int build_plan(const smallw_problem& in, const int32_t* seq, smallw_plan** out) 
             else if (in.force_splits > 0) Sv[p] = std::min<int64_t>(in.force_splits, ne[p]);
         }
         if (in.split_pages == 0 && in.force_splits == 0) {
-            const int64_t slots = int64_t(in.num_cus) * (D == 256 ? 1 : 2);
+            const int64_t slots =
+                int64_t(in.num_cus) * (D < 256 && in.kv_dtype == SMALLW_KV_BF16 ? 2 : 1);
             const int64_t round = std::max<int64_t>(1, slots / Hkv);
             apportion(ne, P <= round ? round : P + round, Sv);
         }

@@ -33,10 +33,10 @@ inline int64_t first_page(int64_t L, int32_t W, int32_t causal, int32_t window_l
 }
 
 // Pages the sweep groups together for one step of its arithmetic: two-page
-// chunks for bf16 and MXFP4 pools, eight-page PV steps (128 tokens, the depth
-// of the scaled fp8 MFMA) for e4m3 pools.  A row-exact piece must start on
-// this grid so that every call groups the piece's pages the same way.
-inline int32_t piece_align(int32_t kv_dtype) { return kv_dtype == SMALLW_KV_FP8_E4M3 ? 8 : 2; }
+// chunks for bf16 pools, eight-page steps (128 tokens, one softmax each) for
+// e4m3 and MXFP4 pools.  A row-exact piece must start on this grid so that
+// every call groups the piece's pages the same way.
+inline int32_t piece_align(int32_t kv_dtype) { return kv_dtype == SMALLW_KV_BF16 ? 2 : 8; }
 
 // Page range [*pb, *pe) of split s of a request whose pages [n_lo, n) are
 // streamed in S splits: balanced (split_pages == 0) or on the absolute grid of

@@ -192,15 +192,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 // ----------------------------------------------------------------------------
-// Split-K sweep kernel for bf16 and MXFP4 pools (e4m3 pools: sweep8_kernel
-// below).  512 threads = 8 wave64s; wave w owns the 16-row MFMA tile w of the
-// unit's W*G rows (W*G <= 128), and the waves share the DMA work.
+// Split-K sweep kernel for bf16 pools (e4m3 pools: sweep8_kernel, MXFP4
+// pools: sweep4_kernel, below).  512 threads = 8 wave64s; wave w owns the
+// 16-row MFMA tile w of the unit's W*G rows (W*G <= 128), and the waves share
+// the DMA work.
 //   D    head dim (64/128/256)
 //   NS   LDS ring depth in chunks (2 pages each)
-//   KV   storage format (bf16, or MXFP4 with V decoded once per chunk into a
-//        bf16 staging tile)
+//   VT   V pages token-major ([16][D], like K) instead of d-major
 // LDS chunk layout of a bf16 ring stage (bytes): [K page0 | K page1 | V^T page0
-// | V^T page1], each a page-head of 16*D*2 bytes (MXFP4: fp4_piece below).
+// | V^T page1], each a page-head of 16*D*2 bytes.
 // K rows are 16-byte-chunk swizzled: token row tau stores global chunk c at
 // slot c ^ h(tau), h(tau) = ((tau>>1)&12)|(tau&3) (masked to the row), so the
 // 16 lanes of one MFMA operand read hit distinct banks.  A bf16 V^T page
@@ -256,52 +256,6 @@ __device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t w, uint32_t e8) {
 template <int J>
 __device__ __forceinline__ uint32_t e2m1x2_two_scales(uint32_t w, uint32_t e_lo, uint32_t e_hi) {
     return (e2m1x2_to_bf16<J>(w, e_lo) & 0xFFFFu) | (e2m1x2_to_bf16<J>(w, e_hi) & 0xFFFF0000u);
-}
-
-// Where 16-byte piece q of an MXFP4 ring stage comes from: array (0 K codes,
-// 1 V codes, 2 K scales, 3 V scales), page of the chunk (0/1) and byte offset
-// inside that page-head.  Stage layout (bytes):
-//   [0, 16D)    K codes of both pages in blocks (rg, g) of D bytes: row group
-//               rg = 8-token group (rg >> 1 = page), g = MFMA lane group, each
-//               block holding bytes [g D/8, (g+1) D/8) of the group's 8 rows.
-//               Row x of a group sits at position x ^ 4 (odd rg); at D = 256
-//               its two 16-byte halves swap for rg >= 2; at D = 128 block g of
-//               rg >= 2 holds lane group g ^ 1.  A lane's bank then depends
-//               only on its row (D = 256), and every 1 KiB of the stage is
-//               1 KiB of contiguous HBM.
-//   [16D, 32D)  V^T codes, page 0 then page 1 (8D each: row d of 8 bytes =
-//               tokens 0..15)
-//   [32D, 34D)  E8M0 scales, K page 0, K page 1 ([16 tokens][D/32 blocks]),
-//               V page 0, V page 1 ([D/32 blocks][16 tokens]), D/2 each
-template <int D>
-__device__ __forceinline__ void fp4_piece(int q, int& arr, int& pg, int& off) {
-    const int o = 16 * q;
-    if (o < 16 * D) {
-        const int b = o / D, rg = b >> 2, within = o % D;
-        pg = rg >> 1;
-        int x, byte;
-        if constexpr (D == 256) {
-            const int g = b & 3;
-            x = (within >> 5) ^ (4 * (rg & 1));
-            byte = 32 * g + 16 * (((within >> 4) & 1) ^ (rg >> 1));
-        } else {
-            const int g = (b & 3) ^ (rg >> 1);
-            x = (within >> 4) ^ (4 * (rg & 1));
-            byte = 16 * g;
-        }
-        arr = 0;
-        off = (8 * (rg & 1) + x) * (D / 2) + byte;
-    } else if (o < 32 * D) {
-        const int o2 = o - 16 * D;
-        pg = o2 / (8 * D);
-        arr = 1;
-        off = o2 % (8 * D);
-    } else {
-        const int o3 = o - 32 * D, blk = o3 / (D / 2);
-        arr = 2 + (blk >> 1);
-        pg = blk & 1;
-        off = o3 % (D / 2);
-    }
 }
 
 // Epilogue of a work unit, on a wave that owns row tile w: normalise the
@@ -372,37 +326,22 @@ __device__ __forceinline__ void finish_unit(const Params& a, const f32x4 (&acc)[
     }
 }
 
-template <int D, int NS, int KV, bool DECH, bool VT = false>
+template <int D, int NS, bool VT = false>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
-    static_assert(KV == SMALLW_KV_BF16 || KV == SMALLW_KV_MXFP4, "e4m3 pools: sweep8_kernel");
-    static_assert(!VT || KV == SMALLW_KV_BF16, "token-major V is a bf16 layout");
-    constexpr bool FP4 = KV == SMALLW_KV_MXFP4;
     constexpr int KS = D / 32;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
     constexpr int BF_PAGE = 32 * D;                // bf16 page-head of K (or V^T) in LDS
-    // page-head codes as streamed from HBM; an MXFP4 stage also holds its scales
-    constexpr int ST_PAGE = FP4 ? 8 * D : BF_PAGE;
-    constexpr int ST_STAGE = FP4 ? 34 * D : 4 * ST_PAGE;
+    constexpr int ST_PAGE = BF_PAGE;               // one ring region (a page-head)
+    constexpr int ST_STAGE = 4 * ST_PAGE;
     constexpr int RING = NS * ST_STAGE;            // DMA ring
-    // + V decode staging for the 4-bit format: two chunks of V^T, bf16
-    constexpr int LDS_BYTES = RING + (FP4 ? 4 * BF_PAGE : 0);
-    constexpr int REG_INST = FP4 ? 1 : ST_PAGE / 1024;  // DMA instructions per region
+    constexpr int REG_INST = ST_PAGE / 1024;       // DMA instructions per region
     constexpr bool SPLIT = REG_INST >= 2;          // region shared by waves w, w+4
     constexpr int LPW = SPLIT ? REG_INST / 2 : 1;  // DMA instructions per issuing wave
     constexpr int CPR = D / 8;                     // 16-byte bf16 chunks per K token row
-    // chunks in flight ahead of the one being computed (the 4-bit format
-    // decodes V one iteration ahead, but reads K from the ring slot)
-    constexpr int AHEAD = NS - 1;
-    constexpr bool LOWP = FP4;                     // scores on the scaled MFMA, V staged
-    // MXFP4: 16-byte pieces per stage, DMA instructions per chunk (instruction
-    // i is issued by wave i mod 8) and the most any wave issues
-    constexpr int N16 = ST_STAGE / 16;
-    constexpr int NI4 = (N16 + 63) / 64;
-    constexpr int MI4 = (NI4 + kSweepWaves - 1) / kSweepWaves;
-    static_assert(REG_INST >= 1 && NS >= (LOWP ? 3 : 2), "config");
-    static_assert(!FP4 || D == 128 || D == 256, "MXFP4 serves D = 128 and 256");
+    constexpr int AHEAD = NS - 1;                  // chunks in flight ahead of the one computed
+    static_assert(REG_INST >= 1 && NS >= 2, "config");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[RING];
     __shared__ int32_t ptab[kPtab];
 
     const int tid = threadIdx.x;
@@ -425,21 +364,13 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- this wave's query rows (tile w)
     const int T = (a.R + 15) >> 4;
     const bool has_tile = w < T;
-    // V decode (4-bit format).  Wave w runs on SIMD w mod 4, so five or
-    // six row tiles put two on SIMDs 0 and 1 and one on SIMDs 2 and 3.  Then
-    // (DECH, chosen at launch) only the four waves on SIMDs 2 and 3 decode, as
-    // threads dec_id = 0..255 with 4D/256 items each, the row-tile ones after
-    // their chunk's PV; otherwise every thread decodes its 4D/512 items, a
-    // row-tile wave under its score MFMAs.
-    const int dec_id = (w >> 2) * 128 + (w & 1) * 64 + l;
     const int r = 16 * w + ln;
     const int qi = r / a.G;
     const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);  // this row's last key
     const int hi_tok = min(jend - 1, hi_row);
     const int lo_tok = a.window_left > 0 ? hi_row - a.window_left + 1 : INT_MIN;
-    // Q fragments: KS bf16 k-steps, or for the scaled MFMA (4-bit K)
-    // qf[4k + 2r + h], the 16-element runs r of 128-deep k-step k (>= 4 entries)
-    bf16x8_t qf[LOWP && KS < 4 ? 4 : KS];
+    // Q fragments: KS bf16 k-steps
+    bf16x8_t qf[KS];
 
     // ---- pool page ids of this unit, staged in LDS (window of kPtab pages)
     int tbase = 0;  // unit-relative page index of ptab[0]
@@ -455,9 +386,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     const int region = w & 3;
     const int region_pg = region & 1;
     const bool region_v = region >= 2;
-    const bool issues_kv = !FP4 && (SPLIT || w < 4);
-    const int nload = FP4 ? (NI4 - w + kSweepWaves - 1) / kSweepWaves   // per chunk
-                          : (issues_kv ? LPW : 0);
+    const bool issues_kv = SPLIT || w < 4;
+    const int nload = issues_kv ? LPW : 0;  // DMA instructions per chunk
     const int ibase = SPLIT ? (w >> 2) * LPW : 0;
     uint32_t goff[LPW];
 #pragma unroll
@@ -480,46 +410,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             goff[i] = uint32_t(d * 32 + h * 16);
         }
     }
-    // MXFP4: this wave's pieces (lane l of its j-th instruction i = w + 8j)
-    int arr4[MI4], pg4[MI4], off4[MI4];
-    bool has4[MI4];
-#pragma unroll
-    for (int j = 0; j < MI4; ++j) {
-        const int q = 64 * (w + kSweepWaves * j) + l;
-        has4[j] = FP4 && q < N16;
-        arr4[j] = pg4[j] = off4[j] = 0;
-        if (has4[j]) fp4_piece<D>(q, arr4[j], pg4[j], off4[j]);
-    }
     const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
     const uint8_t* const pool = region_v ? a.v : a.k;
-    // Scale pointers kept opaque in SGPRs, so that the compiler cannot turn a
-    // per-lane select between them into a per-lane load of the pointer from the
-    // kernel arguments, whose vmcnt(0) wait would drain the ring.
-    const float* kscale = a.k_scale;
-    const float* vscale = a.v_scale;
-    asm volatile("" : "+s"(kscale), "+s"(vscale));
 
     auto issue_chunk = [&](int c) {
-        if constexpr (FP4) {
-            int n1 = 2 * c + 1;
-            if (n1 >= npages) n1 = 2 * c;  // absent second page: reload the first, masked later
-            const int phys0 = __builtin_amdgcn_readfirstlane(ptab[2 * c - tbase]);
-            const int phys1 = __builtin_amdgcn_readfirstlane(ptab[n1 - tbase]);
-            const uint8_t* ks8 = reinterpret_cast<const uint8_t*>(kscale);
-            const uint8_t* vs8 = reinterpret_cast<const uint8_t*>(vscale);
-#pragma unroll
-            for (int j = 0; j < MI4; ++j) {
-                const int i = w + kSweepWaves * j;
-                if (i >= NI4) break;  // wave-uniform
-                const int64_t ph = (int64_t(pg4[j] ? phys1 : phys0) * a.Hkv + kvh);
-                const uint8_t* src = arr4[j] == 0 ? a.k + ph * ST_PAGE
-                                   : arr4[j] == 1 ? a.v + ph * ST_PAGE
-                                   : arr4[j] == 2 ? ks8 + ph * (D / 2) : vs8 + ph * (D / 2);
-                const uint32_t lds = smem_base + uint32_t((c % NS) * ST_STAGE + 1024 * i);
-                if (has4[j]) dma16(src + off4[j], __builtin_amdgcn_readfirstlane(lds));
-            }
-            return;
-        }
         if (issues_kv) {
             int n = 2 * c + region_pg;
             if (n >= npages) n = 2 * c;  // absent second page: reload the first, masked later
@@ -533,59 +427,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
 
-    // MXFP4: decode the V^T codes of ring chunk c once for the whole workgroup
-    // into bf16 staging buffer (c & 1), in the bf16 ring's V^T layout (16-row
-    // groups, tokens 8..15 of a row 256 bytes after tokens 0..7).  Item (page,
-    // token half h, row d): 8 codes (one word) and the 8 tokens' scales of the
-    // row's block (one 8-byte read, V scales being block-major).  The two
-    // tokens of a byte have their own scales, so each byte is converted twice
-    // and the halves are kept: the V scale is exact in the staged values.
-    // Straight-line (4D / 512 items per thread, or 4D / 256 on the waves of
-    // SIMDs 2 and 3 with DECH), so that a row-tile wave can run it between its
-    // score MFMAs and the softmax and the two overlap.
-    auto decode_v4 = [&](int c) {
-        const uint8_t* src = smem + (c % NS) * ST_STAGE;
-        uint8_t* dst = smem + RING + (c & 1) * (2 * BF_PAGE);
-        auto run = [&](int it0, int step, auto n_tag, auto full_tag) {
-            constexpr int N = decltype(n_tag)::value;
-            constexpr bool FULL = decltype(full_tag)::value;  // every item below 4D
-            uint32_t w4[N];
-            uint2 sb[N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int it = it0 + step * i;
-                if (FULL || it < 4 * D) {
-                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-                    w4[i] = *reinterpret_cast<const uint32_t*>(src + 16 * D + pg * 8 * D + d * 8 + 4 * h);
-                    sb[i] = *reinterpret_cast<const uint2*>(src + 33 * D + pg * (D / 2) +
-                                                            (d >> 5) * 16 + 8 * h);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int it = it0 + step * i;
-                if (FULL || it < 4 * D) {
-                    const int d = it % D, h = (it / D) & 1, pg = it / (2 * D);
-                    const uint2 b = sb[i];
-                    const u32x4 o = {e2m1x2_two_scales<0>(w4[i], b.x & 0xFFu, (b.x >> 8) & 0xFFu),
-                                     e2m1x2_two_scales<1>(w4[i], (b.x >> 16) & 0xFFu, b.x >> 24),
-                                     e2m1x2_two_scales<2>(w4[i], b.y & 0xFFu, (b.y >> 8) & 0xFFu),
-                                     e2m1x2_two_scales<3>(w4[i], (b.y >> 16) & 0xFFu, b.y >> 24)};
-                    *reinterpret_cast<u32x4*>(dst + pg * BF_PAGE + 512 * (d >> 4) + 16 * (d & 15) +
-                                              256 * h) = o;
-                }
-            }
-        };
-        if constexpr (DECH) {
-            if (w & 2)
-                run(dec_id, 256, std::integral_constant<int, 4 * D / 256>{}, std::true_type{});
-        } else {
-            run(tid, kSweepThreads,
-                std::integral_constant<int, (4 * D + kSweepThreads - 1) / kSweepThreads>{},
-                std::integral_constant<bool, (4 * D) % kSweepThreads == 0>{});
-        }
-    };
-
     // ---- prologue: start the ring, then load Q while the first chunks are in
     // flight (one memory round trip for both), and wait for all of it here so
     // that no compiler-visible vector load is pending inside the loop
@@ -596,81 +437,15 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         const int gq = r - qi * a.G;
         const uint16_t* qrow =
             a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
-        constexpr int NQ = LOWP && KS < 4 ? 4 : KS;
 #pragma unroll
-        for (int ks = 0; ks < NQ; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            // bf16 k-step ks, lane group g: elements 32ks + 8g ..  Scaled MFMA:
-            // qf[4k + 2r + h] holds run r of k-step k, contraction positions
-            // 64r + 16g + 8h .., which are elements ((D/4)(2r + (g>>1)) + 32k +
-            // 16(g&1) + 8h ..) of an MXFP4 K row (its K LDS layout gives lane
-            // group g the row's D/4-element slice)
-            const int k4 = ks >> 2, r4 = (ks >> 1) & 1, h4 = ks & 1;
-            const int d0 = FP4 ? (D / 4) * (2 * r4 + (g >> 1)) + 32 * k4 + 16 * (g & 1) + 8 * h4
-                               : 32 * ks + 8 * g;
-            if (valid && d0 < D) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+            // k-step ks, lane group g: elements 32ks + 8g ..
+            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
             qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-    // ---- 4-bit scores run on the scaled MFMA (E2M1 K times e4m3 Q, E8M0
-    // scales per 32 elements of the contraction: the MXFP4 block scales for K).
-    // The MFMA's fp4 and fp8 operands put contraction positions 32g .. 32g + 31
-    // and 64r + 16g .. 64r + 16g + 15 (runs r = 0, 1) in lane group g.  Q is
-    // split once per unit:
-    // q = hi 2^X + lo 2^(X-4) per 32-element block, hi and lo e4m3 and X =
-    // floor(log2 amax) - 7, so |q| / 2^X < 256 and the residual fits lo.  A
-    // block's 32 elements are the runs of two lane groups (g, g ^ 1); the scale
-    // that lane group g hands the MFMA is that of contraction block g, whose
-    // elements are run g >> 1 of lane groups 2(g & 1) and 2(g & 1) + 1.
-    constexpr int KS4 = D < 128 ? 1 : D / 128;  // 128-deep k-steps of the scaled MFMA
-    i32x8 qhi[LOWP ? KS4 : 1], qlo[LOWP ? KS4 : 1];
-    uint32_t shi = 0, slo = 0;    // byte k: E8M0 scale this lane supplies for k-step k
-    if constexpr (LOWP) {
-#pragma unroll
-        for (int k = 0; k < KS4; ++k) {
-            int X[2];
-#pragma unroll
-            for (int r4 = 0; r4 < 2; ++r4) {
-                float m = 0.f;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(float(qf[4 * k + 2 * r4 + h][e])));
-                m = fmaxf(m, __shfl_xor(m, 16));
-                int ex = 0;
-                (void)frexpf(m, &ex);
-                X[r4] = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
-            }
-#pragma unroll
-            for (int r4 = 0; r4 < 2; ++r4)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 8; e += 4) {
-                        float x[4], y[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) x[i] = float(qf[4 * k + 2 * r4 + h][e + i]);
-                        int hw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[0], -X[r4]), ldexpf(x[1], -X[r4]), 0, false);
-                        hw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[2], -X[r4]), ldexpf(x[3], -X[r4]), hw, true);
-                        y[0] = x[0] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 0), X[r4]);
-                        y[1] = x[1] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 1), X[r4]);
-                        y[2] = x[2] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 2), X[r4]);
-                        y[3] = x[3] - ldexpf(__builtin_amdgcn_cvt_f32_fp8(hw, 3), X[r4]);
-                        int lw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(y[0], 4 - X[r4]), ldexpf(y[1], 4 - X[r4]), 0, false);
-                        lw = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(y[2], 4 - X[r4]), ldexpf(y[3], 4 - X[r4]), lw, true);
-                        const int wi = 4 * r4 + 2 * h + (e >> 2);  // byte 16 r4 + 8 h + e of the operand
-                        qhi[k][wi] = hw;
-                        qlo[k][wi] = lw;
-                    }
-            const int src = 16 * 2 * (g & 1) + ln;
-            const int x0 = __shfl(X[0], src), x1 = __shfl(X[1], src);
-            const int xs = (g >> 1) ? x1 : x0;
-            shi |= uint32_t(xs + 127) << (8 * k);
-            slo |= uint32_t(xs - 4 + 127) << (8 * k);
-        }
-    }
 
     // ---- LDS read addressing (per lane, constant over chunks), bf16 layout
     // K operand for QK tile t: M-row ln holds chunk token tau = 8*(ln>>2) + 4t + (ln&3),
@@ -690,27 +465,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     }
     const uint32_t vaddr = uint32_t(2 * BF_PAGE + (g >> 1) * BF_PAGE + (g & 1) * 256 + ln * 16);
-    // MXFP4 K addressing (stage layout at fp4_piece): tile t row tau = 8 rg +
-    // 4t + (ln & 3) with rg = ln >> 2; logical 16-byte half h of the lane's
-    // D/8 bytes.  K scales: the lane's first block of that row.
-    uint32_t k4addr[2][2] = {}, k4sc[2] = {};
-    if constexpr (FP4) {
-        const int rg = ln >> 2;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int pos = (4 * t + (ln & 3)) ^ (4 * (rg & 1));
-            const int tau = 8 * rg + 4 * t + (ln & 3);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                k4addr[t][h] = D == 256
-                    ? uint32_t((rg * 4 + g) * D + pos * 32 + 16 * (h ^ (rg >> 1)))
-                    : uint32_t((rg * 4 + (g ^ (rg >> 1))) * D + pos * 16);
-            k4sc[t] = uint32_t(32 * D + (tau >> 4) * (D / 2) + (tau & 15) * (D / 32) + g * (KS / 4));
-        }
-    }
-    // where this lane's V^T operand rows start: the bf16 ring stage, or the
-    // V staging buffer of the 4-bit format (the two V pages only)
-    const uint32_t va = LOWP ? vaddr - 2 * BF_PAGE : vaddr;
     // VT: the two transpose-read addresses of d tile 0 (tile dt: xor 32 dt);
     // read a2 covers tokens 8g + 4a2 .. 8g + 4a2 + 3 of the chunk
     uint32_t vtA[2] = {};
@@ -735,7 +489,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
             return u32x4{l2.x, l2.y, h2.x, h2.y};
         } else {
-            return *reinterpret_cast<const u32x4*>(vst + va + 512 * dt);
+            return *reinterpret_cast<const u32x4*>(vst + vaddr + 512 * dt);
         }
     };
 
@@ -747,7 +501,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     auto process = [&](int c, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const uint8_t* st = smem + (c % NS) * ST_STAGE;
-        const uint8_t* vst = LOWP ? smem + RING + (c & 1) * (2 * BF_PAGE) : st;  // V^T operand rows
+        const uint8_t* vst = st;  // V^T operand rows
         const int j0 = (un.pb + 2 * c) * kPage;  // absolute position of chunk token 0
         // S^T = K . Q^T over the chunk's 32 tokens (two 16-token tiles), four
         // independent accumulation chains for MFMA pipelining.  All K operand
@@ -755,37 +509,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         f32x4 s4[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) s4[t][0] = s4[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP4) {
-            // per tile row: the lane's D/8 code bytes (16 per 128-deep k-step:
-            // one E2M1 block) and their E8M0 scales (byte k for k-step k); the
-            // hi and lo parts of Q accumulate in separate chains
-            u32x4 kw[2][2];
-            uint32_t ksb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                kw[t][0] = *reinterpret_cast<const u32x4*>(st + k4addr[t][0]);
-                if constexpr (D == 256) kw[t][1] = *reinterpret_cast<const u32x4*>(st + k4addr[t][1]);
-                ksb[t] = D == 256 ? uint32_t(*reinterpret_cast<const uint16_t*>(st + k4sc[t]))
-                                  : uint32_t(st[k4sc[t]]);
-            }
-            auto kstep = [&](auto kc) {
-                constexpr int k = decltype(kc)::value;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const u32x4 w = kw[t][k];
-                    const i32x8 ka = {int(w[0]), int(w[1]), int(w[2]), int(w[3]), 0, 0, 0, 0};
-                    s4[t][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        ka, qhi[k], s4[t][0], 4, 0, k, int(ksb[t]), k, int(shi));
-                    s4[t][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        ka, qlo[k], s4[t][1], 4, 0, k, int(ksb[t]), k, int(slo));
-                }
-            };
-            kstep(std::integral_constant<int, 0>{});
-            if constexpr (KS4 > 1) kstep(std::integral_constant<int, 1>{});
-            // this thread's share of the next chunk's V decode, under the MFMAs
-            // (past the last chunk it decodes a stale slot that nobody reads)
-            if constexpr (!DECH) decode_v4(c + 1);
-        } else {
+        {
             bf16x8_t kop[KS][2];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -859,17 +583,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
         }
     };
 
-    // ---- ring step for iteration c.
-    // bf16: wait for chunk c, then refill the slot freed by chunk c-1 with
-    //       chunk c+NS-1.
-    // MXFP4: as bf16, but wait for chunk c+1, whose V every thread decodes
-    //       into staging during iteration c (row-tile waves inside process,
-    //       between the score MFMAs and the softmax); chunk c's K is read from
-    //       its ring slot.
+    // ---- ring step for iteration c: wait for chunk c, then refill the slot
+    // freed by chunk c-1 with chunk c+NS-1
     auto ring_step = [&](int c) {
-        const int need = LOWP ? c + 1 : c;
-        // chunks younger than `need` left in flight: all issued up to c+NS-2
-        if (need < nchunks) wait_vmcnt_dyn(min(LOWP ? NS - 3 : NS - 2, nchunks - 1 - need) * nload);
+        // chunks younger than c left in flight: all issued up to c+NS-2
+        wait_vmcnt_dyn(min(NS - 2, nchunks - 1 - c) * nload);
         __syncthreads();
         const int cn = c + AHEAD;
         if (cn < nchunks) {
@@ -882,14 +600,6 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
             issue_chunk(cn);
         }
     };
-    auto decode_v = [&](int c) {
-        if constexpr (FP4) decode_v4(c);
-    };
-    if (LOWP && nchunks > 0) {  // decode chunk 0's V ahead of the loop
-        wait_vmcnt_dyn(min(AHEAD - 1, nchunks - 1) * nload);
-        __syncthreads();
-        decode_v(0);
-    }
     // Chunks that need no mask come first: the masked ones (keys past the
     // unit's end, or past some row's causal limit) are always a suffix.
     int c_tail = nchunks;
@@ -900,15 +610,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     while (c_head < c_tail && (un.pb + 2 * c_head) * kPage < win_hi) ++c_head;
 
     // one iteration: the ring step, then the row-tile waves' scores, softmax
-    // and PV of chunk c and everyone's share of the V decode of chunk c+1
+    // and PV of chunk c
     auto step = [&](int c, auto tail_tag) {
         ring_step(c);
-        if (has_tile) {
-            process(c, tail_tag);
-            if constexpr (DECH) decode_v(c + 1);
-        } else if constexpr (LOWP) {
-            decode_v(c + 1);
-        }
+        if (has_tile) process(c, tail_tag);
     };
     int c = 0;
     for (; c < c_head; ++c) step(c, std::true_type{});
@@ -918,6 +623,84 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep_kernel(Params a) {
     // ---- epilogue: normalise, write the final output or the split partial
     if (!has_tile) return;
     finish_unit<D>(a, acc, m_run, l_run, u, un, w, l, g, r, qi, T);
+}
+
+// Q rows of a work unit as the B operand of the scaled fp8 MFMA: loaded in the
+// operand's contraction order, then split per 32-element block into two e4m3
+// parts q = hi 2^X + lo 2^(X-4), X = floor(log2 amax) - 7, which hold a bf16 q
+// exactly (4 + 4 significant bits).  Block b of a 128-deep k-step is run b >> 1
+// of lane groups 2(b & 1), 2(b & 1) + 1; lane group g supplies the scale of
+// block g (byte k of shi / slo for k-step k).  Shared by the e4m3 and MXFP4
+// sweeps; it waits for all of this wave's loads.
+template <int D>
+__device__ __forceinline__ void load_split_q(const Params& a, int p, int kvh, bool valid, int qi,
+                                             int gq, int g, int ln,
+                                             i32x8 (&qhi)[D < 128 ? 1 : D / 128],
+                                             i32x8 (&qlo)[D < 128 ? 1 : D / 128], uint32_t& shi,
+                                             uint32_t& slo) {
+    constexpr int KS4 = D < 128 ? 1 : D / 128;
+    bf16x8_t qf[4 * KS4];
+    {
+        const uint16_t* qrow =
+            a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < 4 * KS4; ++ks) {
+            // qf[4k + 2r + h]: contraction positions 128k + 64r + 16g + 8h .. (zero past D)
+            const int d0 = 128 * (ks >> 2) + 64 * ((ks >> 1) & 1) + 16 * g + 8 * (ks & 1);
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (valid && d0 < D) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+#pragma unroll
+    for (int k = 0; k < KS4; ++k) {
+        int X[2];
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+            float m = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    m = fmaxf(m, fabsf(float(qf[4 * k + 2 * r4 + hh][e])));
+            m = pair16(m, true);
+            int ex = 0;
+            (void)frexpf(m, &ex);
+            X[r4] = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; e += 4) {
+                    float x4[4], y4[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        x4[i] = ldexpf(float(qf[4 * k + 2 * r4 + hh][e + i]), -X[r4]);
+                    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[0], x4[1], 0, false);
+                    hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[2], x4[3], hw, true);
+                    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+                    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+                    y4[0] = (x4[0] - h01[0]) * 16.f;
+                    y4[1] = (x4[1] - h01[1]) * 16.f;
+                    y4[2] = (x4[2] - h23[0]) * 16.f;
+                    y4[3] = (x4[3] - h23[1]) * 16.f;
+                    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[0], y4[1], 0, false);
+                    lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[2], y4[3], lw, true);
+                    const int wi = 4 * r4 + 2 * hh + e / 4;  // byte 16 r4 + 8 hh + e
+                    qhi[k][wi] = hw;
+                    qlo[k][wi] = lw;
+                }
+        const int src = 16 * 2 * (g & 1) + ln;
+        const int x0 = __shfl(X[0], src), x1 = __shfl(X[1], src);
+        const int xs = (g >> 1) ? x1 : x0;
+        shi |= uint32_t(xs + 127) << (8 * k);
+        slo |= uint32_t(xs - 4 + 127) << (8 * k);
+    }
+
 }
 
 // ----------------------------------------------------------------------------
@@ -1075,75 +858,10 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
     // one step is in flight while the current one computes.
     for (int t = 0; t < min(2, nchunks); ++t) issue_k(t);
     if (nchunks > 0) issue_v(0);
-    bf16x8_t qf[4 * KS4];
-    {
-        const bool valid = has_tile && r < a.R;
-        const int gq = r - qi * a.G;
-        const uint16_t* qrow =
-            a.q + ((int64_t(p) * a.W + (valid ? qi : 0)) * a.Hq + kvh * a.G + (valid ? gq : 0)) * D;
-#pragma unroll
-        for (int ks = 0; ks < 4 * KS4; ++ks) {
-            // qf[4k + 2r + h]: contraction positions 128k + 64r + 16g + 8h .. (zero past D)
-            const int d0 = 128 * (ks >> 2) + 64 * ((ks >> 1) & 1) + 16 * g + 8 * (ks & 1);
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (valid && d0 < D) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
-            qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-    // ---- Q split per 32-element block into two e4m3 parts q = hi 2^X + lo
-    // 2^(X-4), X = floor(log2 amax) - 7, which hold a bf16 q exactly (4 + 4
-    // significant bits).  Block b of a 128-deep k-step is run b >> 1 of lane
-    // groups 2(b & 1), 2(b & 1) + 1; lane group g supplies the scale of block g.
+    // Q as two e4m3 parts (its loads overlap the DMA issued above)
     i32x8 qhi[KS4], qlo[KS4];
     uint32_t shi = 0, slo = 0;
-#pragma unroll
-    for (int k = 0; k < KS4; ++k) {
-        int X[2];
-#pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-            float m = 0.f;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    m = fmaxf(m, fabsf(float(qf[4 * k + 2 * r4 + hh][e])));
-            m = pair16(m, true);
-            int ex = 0;
-            (void)frexpf(m, &ex);
-            X[r4] = m > 0.f ? min(max(ex - 8, -123), 127) : 0;
-        }
-#pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int e = 0; e < 8; e += 4) {
-                    float x4[4], y4[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        x4[i] = ldexpf(float(qf[4 * k + 2 * r4 + hh][e + i]), -X[r4]);
-                    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[0], x4[1], 0, false);
-                    hw = __builtin_amdgcn_cvt_pk_fp8_f32(x4[2], x4[3], hw, true);
-                    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-                    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-                    y4[0] = (x4[0] - h01[0]) * 16.f;
-                    y4[1] = (x4[1] - h01[1]) * 16.f;
-                    y4[2] = (x4[2] - h23[0]) * 16.f;
-                    y4[3] = (x4[3] - h23[1]) * 16.f;
-                    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[0], y4[1], 0, false);
-                    lw = __builtin_amdgcn_cvt_pk_fp8_f32(y4[2], y4[3], lw, true);
-                    const int wi = 4 * r4 + 2 * hh + e / 4;  // byte 16 r4 + 8 hh + e
-                    qhi[k][wi] = hw;
-                    qlo[k][wi] = lw;
-                }
-        const int src = 16 * 2 * (g & 1) + ln;
-        const int x0 = __shfl(X[0], src), x1 = __shfl(X[1], src);
-        const int xs = (g >> 1) ? x1 : x0;
-        shi |= uint32_t(xs + 127) << (8 * k);
-        slo |= uint32_t(xs - 4 + 127) << (8 * k);
-    }
+    load_split_q<D>(a, p, kvh, has_tile && r < a.R, qi, r - qi * a.G, g, ln, qhi, qlo, shi, slo);
 
     // K operand reads: lane row (page ln >> 2, token 4 tt + (ln & 3)), run r of
     // k-step k = 16-byte slot 8k + 4r + g of the row, stored at slot ^ (ln & (SPR-1))
@@ -1439,6 +1157,411 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
     for (; j < g_head; ++j) step(j, std::true_type{});
     for (; j < g_tail; ++j) step(j, std::false_type{});
     for (; j < ngroups; ++j) step(j, std::true_type{});
+
+    if (!has_tile) return;
+    finish_unit<D>(a, acc, m_run, l_run, u, un, w, l, g, r, qi, T);
+}
+
+// ----------------------------------------------------------------------------
+// MXFP4 sweep.  Steps of 128 tokens (two 64-token chunks of 4 pages each) with
+// one softmax per step, as in the e4m3 sweep.  Scores run on the scaled MFMA:
+// the E2M1 K codes are its A operand and their E8M0 bytes its A scales, Q
+// split into two e4m3 parts (load_split_q) its B operand.  The V^T codes of a
+// step are decoded by all eight waves into a bf16 staging tile, the V scales
+// exact in it, and the PV product runs on the bf16 MFMA over four 32-token
+// blocks.
+//
+// One step: barrier (the step's loads have landed and every read of the
+// previous step is done) -> loads of the next step into the slots the previous
+// step used -> decode of this step's V -> scores and softmax -> barrier (the
+// staging tile is complete) -> PV.
+//
+// Token map: MFMA row m of score tile tt (0..3) of a chunk is chunk token
+// 32 (tt >> 1) + 8 (m >> 2) + 4 (tt & 1) + (m & 3), so the S^T accumulators of
+// tiles 2b and 2b + 1 give lane group g the chunk tokens 32b + 8g .. 32b + 8g
+// + 7: the B operand of the bf16 PV MFMA over 32-token block b of the chunk.
+//
+// LDS layouts are operand-major: every 16-byte operand piece a lane reads
+// sits at 16 l of a 1 KiB block, so the 16 lanes of a group read 256
+// contiguous bytes (measured on gfx950: ds_read_b128 with each lane in its
+// own row reaches about 60% of the rate of such contiguous reads, whatever
+// the bank swizzle).  The DMA places every piece there from its own source.
+// LDS ring slot of a chunk (bytes):
+//   [0, 32D)    K codes: block (tt, k) of 1 KiB = the A operand of score tile
+//               tt, k-step k: piece 16g + m = bytes 64k + 16g .. of the K row
+//               of MFMA row m (chunk token 32 (tt >> 1) + 8 (m >> 2) +
+//               4 (tt & 1) + (m & 3))
+//   [32D, 64D)  V^T codes of the chunk's 4 page-heads as stored ([D][8] each)
+//   [64D, 66D)  K scales of the 4 page-heads ([16][D/32] each: [token][D/32])
+//   [66D, 68D)  V scales of the 4 page-heads ([D/32][16] each)
+// Staging (bf16 V^T of a step): block (32-token block b, d tile dt) of 1 KiB
+// = the A operand of the PV MFMA: piece 16c + m = tokens 8c .. 8c + 7 of
+// block b, row d = 16 dt + m.
+// ----------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
+    static_assert(D == 128 || D == 256, "MXFP4 serves D = 128 and 256");
+    constexpr int KS4 = D / 128;               // 128-deep k-steps of the scores
+    constexpr int DT = D / 16;                 // 16-wide d tiles of the output
+    constexpr int PGB = 8 * D;                 // codes of one page-head, K or V^T
+    constexpr int SPB = D / 2;                 // E8M0 scales of one page-head
+    constexpr int OFF_V = 4 * PGB;             // ring slot: V^T codes
+    constexpr int OFF_KS = 8 * PGB;            // ring slot: K scales
+    constexpr int OFF_VS = OFF_KS + 4 * SPB;   // ring slot: V scales
+    constexpr int CHB = OFF_VS + 4 * SPB;      // one chunk's ring slot
+    constexpr int NR = 4;                      // ring slots: two steps
+    constexpr int N16 = CHB / 16;              // 16-byte pieces of a chunk
+    constexpr int NI = (N16 + 63) / 64;        // DMA instructions per chunk
+    constexpr int MI = (2 * NI + kSweepWaves - 1) / kSweepWaves;  // per wave and step, at most
+    constexpr int BLK = 64 * D;                // staging bytes of one 32-token block
+    constexpr int NDEC = 8 * D / kSweepThreads;  // decode items per thread and step
+    // score tiles whose K operands are read together, (block, d tile) PV
+    // products per operand-read group (measured: 4 and 4 are faster at D = 128)
+    constexpr int QB = D == 256 ? 8 : 4;
+    constexpr int PG = D == 256 ? 8 : 4;
+    static_assert(CHB % 256 == 0 && NDEC * kSweepThreads == 8 * D, "config");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NR * CHB];
+    __shared__ __attribute__((aligned(1024))) uint8_t stg[4 * BLK];
+    __shared__ int32_t ptab[kPtab];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int g = l >> 4;
+    const int ln = l & 15;
+
+    const Unit un = decode_unit(a, blockIdx.x);
+    const int u = blockIdx.x;
+    const int p = un.p, kvh = un.kvh, L = un.L;
+    const int npages = un.pe - un.pb;
+    const int nchunks = (npages + 3) >> 2;
+    const int jend = min(L, un.pe * kPage);
+    const int lim_lo = a.causal ? (L - a.W + 1) : L;
+    const int first_masked = min(jend, lim_lo);
+    const int win_hi = a.window_left > 0 ? L - a.window_left : INT_MIN;
+
+    const int T = (a.R + 15) >> 4;
+    const bool has_tile = w < T;
+    const int r = 16 * w + ln;
+    const int qi = r / a.G;
+    const int hi_row = a.causal ? (L - a.W + qi) : (L - 1);
+    const int hi_tok = min(jend - 1, hi_row);
+    const int lo_tok = a.window_left > 0 ? hi_row - a.window_left + 1 : INT_MIN;
+
+    int tbase = 0;
+    auto fill_ptab = [&](int base) {
+        for (int k = tid; k < kPtab; k += kSweepThreads)
+            if (base + k < npages) ptab[k] = phys_page(a, p, un.pb + base + k);
+    };
+    fill_ptab(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    // ---- DMA work of this wave: instructions I = w + 8m of a step's 2 NI,
+    // I = NI c + i being instruction i of the step's chunk c.  Lane l of
+    // instruction i moves piece q = 64 i + l of the chunk; its source array
+    // (0 K codes, 1 V^T codes, 2 K scales, 3 V scales), page of the chunk and
+    // byte offset in that page-head are packed as off | pg << 12 | arr << 14,
+    // bit 16 set for a piece inside the chunk.
+    uint32_t dsc[MI];
+#pragma unroll
+    for (int m = 0; m < MI; ++m) {
+        const int q = 64 * ((w + kSweepWaves * m) % NI) + l;
+        int arr = 0, pg = 0, off = 0;
+        if (q < 2 * D) {  // block (tt, k) = q >> 6, piece 16g + m = q & 63
+            const int tt = (q >> 6) / KS4, k = (q >> 6) % KS4, gg = (q >> 4) & 3, m = q & 15;
+            const int row = 32 * (tt >> 1) + 8 * (m >> 2) + 4 * (tt & 1) + (m & 3);
+            pg = row >> 4;
+            off = (row & 15) * (D / 2) + 16 * (4 * k + gg);
+        } else if (q < 4 * D) {
+            const int o = 16 * (q - 2 * D);
+            arr = 1;
+            pg = o / PGB;
+            off = o % PGB;
+        } else {
+            const int o = 16 * (q - 4 * D);
+            arr = o >= 4 * SPB ? 3 : 2;
+            pg = (o % (4 * SPB)) / SPB;
+            off = o % SPB;
+        }
+        dsc[m] = uint32_t(off) | uint32_t(pg) << 12 | uint32_t(arr) << 14 |
+                 (q < N16 ? 1u << 16 : 0u);
+    }
+    const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>(ring));
+    // Source addresses as integers: the array is a base plus a uniform
+    // (code instructions) or per-lane (the scale instruction) difference.  A
+    // select among the four pointers would be compiled as a per-lane lookup
+    // in a private table, a memory load in front of every DMA.
+    const uint64_t kcb = reinterpret_cast<uint64_t>(a.k);
+    const uint64_t vcd = reinterpret_cast<uint64_t>(a.v) - kcb;
+    const uint64_t ksb = reinterpret_cast<uint64_t>(a.k_scale);
+    const uint64_t vsd = reinterpret_cast<uint64_t>(a.v_scale) - ksb;
+
+    // loads of step j: chunks 2j and 2j + 1, those that exist; pages past the
+    // unit's end are replaced by the chunk's first page and masked later.
+    // Every page id is read first: a DMA statement carries a memory clobber,
+    // so an LDS read placed between two of them would make the second wait
+    // for the first's page id to arrive.
+    auto issue_step = [&](int j) {
+        int phys[MI];
+#pragma unroll
+        for (int m = 0; m < MI; ++m) {
+            const int t = 2 * j + (w + kSweepWaves * m) / NI;
+            int n = 4 * t + (int(dsc[m] >> 12) & 3);
+            if (n >= npages) n = 4 * t;
+            phys[m] = ptab[min(max(n - tbase, 0), kPtab - 1)];
+        }
+#pragma unroll
+        for (int m = 0; m < MI; ++m) {
+            const int I = w + kSweepWaves * m;
+            if (I >= 2 * NI) break;  // wave-uniform
+            const int c = I / NI, i = I % NI;
+            const int t = 2 * j + c;
+            if (t < nchunks) {
+                const uint32_t ds = dsc[m];
+                const int64_t ph = int64_t(phys[m]) * a.Hkv + kvh;
+                // one array per code instruction (i is uniform); the scale
+                // instruction holds K scales, then V scales (bit 14)
+                const uint64_t src =
+                    i < 4 * D / 64
+                        ? kcb + (i >= 2 * D / 64 ? vcd : 0) + uint64_t(ph) * PGB
+                        : ksb + ((ds >> 14) & 1 ? vsd : 0) + uint64_t(ph) * SPB;
+                const uint32_t lds = ring_base + uint32_t((t % NR) * CHB + 1024 * i);
+                if (ds & (1u << 16))
+                    dma16(reinterpret_cast<const void*>(src + (ds & 0xFFFu)),
+                          __builtin_amdgcn_readfirstlane(lds));
+            }
+        }
+    };
+
+    // ---- prologue: step 0's loads, then Q (one round trip for both)
+    if (nchunks > 0) issue_step(0);
+    i32x8 qhi[KS4], qlo[KS4];
+    uint32_t shi = 0, slo = 0;
+    load_split_q<D>(a, p, kvh, has_tile && r < a.R, qi, r - qi * a.G, g, ln, qhi, qlo, shi, slo);
+
+    // K scales: the E8M0 byte of the lane's K row r = 32 (tt >> 1) + 4 (tt & 1)
+    // + rl, rl = 8 (ln >> 2) + (ln & 3), for its k-block g of k-step k: byte
+    // 4k + g of the row's scales
+    const int rl = 8 * (ln >> 2) + (ln & 3);
+    const uint32_t ksof = uint32_t(OFF_KS + rl * (D / 32) + g);
+
+    f32x4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto ring_step = [&](int j) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        const int tn = 2 * j + 2;
+        if (tn < nchunks) {
+            const int lo_need = 4 * tn, hi_need = min(4 * tn + 7, npages - 1);
+            if (hi_need - tbase >= kPtab) {  // slide the page-table window (long units only)
+                tbase = lo_need;
+                fill_ptab(tbase);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __syncthreads();
+            }
+            issue_step(j + 1);
+        }
+    };
+
+    // ---- decode of step j's V^T codes: item (chunk c, page pg, row d) is the
+    // row's 16 codes (8 bytes, the even token in the low nibble) and the 16
+    // tokens' E8M0 bytes of its 32-row block; each code byte is converted with
+    // each of its two tokens' scales and one half of each kept.  Tokens past
+    // the unit's keys (stale slots, pages past the end) are written as zeros.
+    auto decode = [&](int j, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        constexpr int NB = NDEC < 4 ? NDEC : 4;  // items whose reads are issued together
+#pragma unroll
+        for (int n0 = 0; n0 < NDEC; n0 += NB) {
+            uint2 cw[NB];
+            u32x4 sv[NB];
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const int it = tid + kSweepThreads * (n0 + n);
+                const int d = it % D, pg = (it / D) & 3, c = it / (4 * D);
+                const uint8_t* src = ring + ((2 * j + c) % NR) * CHB;
+                cw[n] = *reinterpret_cast<const uint2*>(src + OFF_V + pg * PGB + d * 8);
+                sv[n] = *reinterpret_cast<const u32x4*>(src + OFF_VS + pg * SPB + (d >> 5) * 16);
+            }
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const int it = tid + kSweepThreads * (n0 + n);
+                const int d = it % D, pg = (it / D) & 3, c = it / (4 * D);
+                const u32x4 s = sv[n];
+                u32x4 o0 = {e2m1x2_two_scales<0>(cw[n].x, s[0] & 0xFFu, (s[0] >> 8) & 0xFFu),
+                            e2m1x2_two_scales<1>(cw[n].x, (s[0] >> 16) & 0xFFu, s[0] >> 24),
+                            e2m1x2_two_scales<2>(cw[n].x, s[1] & 0xFFu, (s[1] >> 8) & 0xFFu),
+                            e2m1x2_two_scales<3>(cw[n].x, (s[1] >> 16) & 0xFFu, s[1] >> 24)};
+                u32x4 o1 = {e2m1x2_two_scales<0>(cw[n].y, s[2] & 0xFFu, (s[2] >> 8) & 0xFFu),
+                            e2m1x2_two_scales<1>(cw[n].y, (s[2] >> 16) & 0xFFu, s[2] >> 24),
+                            e2m1x2_two_scales<2>(cw[n].y, s[3] & 0xFFu, (s[3] >> 8) & 0xFFu),
+                            e2m1x2_two_scales<3>(cw[n].y, (s[3] >> 16) & 0xFFu, s[3] >> 24)};
+                if constexpr (TAIL) {
+                    const int vc = min(max(jend - (un.pb + 4 * (2 * j + c) + pg) * kPage, 0), 16);
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        o0[k2] &= (2 * k2 + 1 < vc) ? 0xffffffffu : (2 * k2 < vc ? 0x0000ffffu : 0u);
+                        o1[k2] &= (2 * k2 + 9 < vc) ? 0xffffffffu : (2 * k2 + 8 < vc ? 0x0000ffffu : 0u);
+                    }
+                }
+                // pieces 2 (pg & 1) and 2 (pg & 1) + 1 of row d of block 2c + (pg >> 1)
+                uint8_t* dst = stg + (2 * c + (pg >> 1)) * BLK + (d >> 4) * 1024 + (pg & 1) * 512 +
+                               (d & 15) * 16;
+                *reinterpret_cast<u32x4*>(dst) = o0;
+                *reinterpret_cast<u32x4*>(dst + 256) = o1;
+            }
+        }
+    };
+
+    // ---- scores of step j: s[4c + tt] = tile tt of chunk 2j + c (chunk B
+    // only if present); per k-step all tiles' K operands, then the hi MFMAs,
+    // then the lo MFMAs
+    auto qk = [&](int j, bool hasB, f32x4 (&s)[8]) {
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) s[t8] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // tiles t0 .. t0 + QB - 1, k-step k
+        auto kstep = [&](int t0, auto k_tag) {
+            constexpr int k = decltype(k_tag)::value;
+            u32x4 kw[QB];
+            uint32_t sa[QB];
+#pragma unroll
+            for (int e = 0; e < QB; ++e) {
+                const int t8 = t0 + e;
+                const uint8_t* sl = ring + ((2 * j + (t8 >> 2)) % NR) * CHB;
+                const int tt = t8 & 3, r0 = 32 * (tt >> 1) + 4 * (tt & 1);
+                kw[e] = *reinterpret_cast<const u32x4*>(sl + (tt * KS4 + k) * 1024 + 16 * l);
+                sa[e] = sl[ksof + r0 * (D / 32) + 4 * k];
+            }
+#pragma unroll
+            for (int e = 0; e < QB; ++e) {
+                if (t0 + e >= 4 && !hasB) break;
+                const i32x8 ka = {int(kw[e][0]), int(kw[e][1]), int(kw[e][2]), int(kw[e][3]),
+                                  0, 0, 0, 0};
+                s[t0 + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    ka, qhi[k], s[t0 + e], 4, 0, 0, int(sa[e]), k, int(shi));
+            }
+#pragma unroll
+            for (int e = 0; e < QB; ++e) {
+                if (t0 + e >= 4 && !hasB) break;
+                const i32x8 ka = {int(kw[e][0]), int(kw[e][1]), int(kw[e][2]), int(kw[e][3]),
+                                  0, 0, 0, 0};
+                s[t0 + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    ka, qlo[k], s[t0 + e], 4, 0, 0, int(sa[e]), k, int(slo));
+            }
+        };
+#pragma unroll
+        for (int t0 = 0; t0 < 8; t0 += QB) {
+            kstep(t0, std::integral_constant<int, 0>{});
+            if constexpr (KS4 > 1) kstep(t0, std::integral_constant<int, 1>{});
+        }
+    };
+
+    // ---- softmax of step j: one running max over the step's 32 scores per
+    // lane (the softmax scale goes in the exponent), lazy rescale as in the
+    // bf16 sweep, then the weights of 32-token block b as bf16 PV operands
+    auto softmax = [&](int j, const f32x4 (&s)[8], bf16x8_t (&pf)[4], auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int j0 = (un.pb + 8 * j) * kPage + 8 * g;  // tile 0, element 0 of lane group g
+        float x[32];
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = s[t8][i];
+                if (TAIL) {
+                    const int tt = t8 & 3;
+                    const int jj = j0 + 64 * (t8 >> 2) + 32 * (tt >> 1) + 4 * (tt & 1) + i;
+                    v = (jj <= hi_tok && jj >= lo_tok) ? v : -INFINITY;
+                }
+                x[4 * t8 + i] = v;
+            }
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
+        mx = wave_max_groups(mx) * a.scale_log2;
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__any(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+            m_run = grow ? mx : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -m_use));
+            ls += x[e];
+        }
+        l_run += ls;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            pf[b] = bf16x8_t{(__bf16)x[8 * b], (__bf16)x[8 * b + 1], (__bf16)x[8 * b + 2],
+                             (__bf16)x[8 * b + 3], (__bf16)x[8 * b + 4], (__bf16)x[8 * b + 5],
+                             (__bf16)x[8 * b + 6], (__bf16)x[8 * b + 7]};
+    };
+
+    // ---- O^T += V^T . P^T over the step's four 32-token blocks, in groups
+    // of PG (block, d tile) products: the operand reads of group n + 1 are
+    // issued before the MFMAs of group n, so LDS latency hides behind them
+    auto pv = [&](const bf16x8_t (&pf)[4]) {
+        constexpr int NG = 4 * DT / PG;
+        u32x4 vb[2][PG];
+        auto rd = [&](int n, u32x4 (&dst)[PG]) {
+#pragma unroll
+            for (int e = 0; e < PG; ++e) {
+                const int x = PG * n + e, b = x / DT, dt = x % DT;
+                dst[e] = *reinterpret_cast<const u32x4*>(stg + b * BLK + dt * 1024 + 16 * l);
+            }
+        };
+        rd(0, vb[0]);
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+            if (n + 1 < NG) rd(n + 1, vb[(n + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < PG; ++e) {
+                const int x = PG * n + e, b = x / DT, dt = x % DT;
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, vb[n & 1][e]), pf[b], acc[dt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    auto step = [&](int j, auto tail_tag) {
+        const bool hasB = 2 * j + 1 < nchunks;
+        ring_step(j);
+        decode(j, tail_tag);
+        f32x4 s[8];
+        bf16x8_t pf[4];
+        if (has_tile) {
+            qk(j, hasB, s);
+            softmax(j, s, pf, tail_tag);
+        }
+        __syncthreads();
+        if (has_tile) pv(pf);
+    };
+
+    // masked steps as in the e4m3 sweep: a suffix (keys past the unit's end or
+    // some row's causal limit), a prefix (below some row's sliding window)
+    int c_tail = nchunks;
+    while (c_tail > 0 && (un.pb + 4 * (c_tail - 1)) * kPage + 64 > first_masked) --c_tail;
+    int c_head = 0;
+    while (c_head < c_tail && (un.pb + 4 * c_head) * kPage < win_hi) ++c_head;
+    const int nsteps = (nchunks + 1) >> 1;
+    const int g_head = (c_head + 1) >> 1, g_tail = c_tail >> 1;
+    int j = 0;
+    for (; j < g_head; ++j) step(j, std::true_type{});
+    for (; j < g_tail; ++j) step(j, std::false_type{});
+    for (; j < nsteps; ++j) step(j, std::true_type{});
 
     if (!has_tile) return;
     finish_unit<D>(a, acc, m_run, l_run, u, un, w, l, g, r, qi, T);
@@ -1742,24 +1865,19 @@ int launch(K kernel, int64_t blocks, int threads, const Params& a, hipStream_t s
 
 template <int D>
 int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* ev0, void* ev1) {
-    // five or six row tiles: the V decode moves to the waves on SIMDs 2 and 3
-    const int T = (pl->R + 15) / 16;
-    const bool dech = T == 5 || T == 6;
     if (pl->prob.kv_dtype == SMALLW_KV_FP8_E4M3)
         return launch(sweep8_kernel<D>, pl->U, kSweepThreads, a, st, ev0, ev1,
                       "sweep kernel launch");
     if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
         if constexpr (D == 64) return SMALLW_EUNSUPPORTED;  // the planner rejects it first
         else
-            return dech ? launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4, true>, pl->U, kSweepThreads,
-                                 a, st, ev0, ev1, "sweep kernel launch")
-                        : launch(sweep_kernel<D, 10, SMALLW_KV_MXFP4, false>, pl->U, kSweepThreads,
-                                 a, st, ev0, ev1, "sweep kernel launch");
+            return launch(sweep4_kernel<D>, pl->U, kSweepThreads, a, st, ev0, ev1,
+                          "sweep kernel launch");
     }
     if (pl->prob.v_layout == SMALLW_V_TOKEN_MAJOR)
-        return launch(sweep_kernel<D, 4, SMALLW_KV_BF16, false, true>, pl->U, kSweepThreads, a, st,
+        return launch(sweep_kernel<D, 4, true>, pl->U, kSweepThreads, a, st,
                       ev0, ev1, "sweep kernel launch");
-    return launch(sweep_kernel<D, 4, SMALLW_KV_BF16, false>, pl->U, kSweepThreads, a, st, ev0, ev1,
+    return launch(sweep_kernel<D, 4>, pl->U, kSweepThreads, a, st, ev0, ev1,
                   "sweep kernel launch");
 }
 

@@ -130,6 +130,7 @@ def test_plan_export_matches_oracle_plan_bit_exactly():
         plan = sw.small_w_attention_plan(pr, seq)
         mine = sw.small_w_attention_plan_export(plan)
         pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=fp8 == 1, seq_lens=seq, num_cus=cus,
+                         kv=("bf16", "fp8", "mxfp4")[fp8],
                          force_splits=force, split_pages=spg, W=W, causal=bool(causal),
                          window_left=win)
         np.testing.assert_array_equal(mine, oracle.plan_export(pl, R=W * G))

@@ -66,10 +66,10 @@ def test_every_kernel_is_present(asm):
     for k in ("sweep_kernel", "combine_kernel", "trace_kernel"):
         assert any(k in n for n in names), (k, names)
     # bf16 sweeps at D = 64 / 128 / 256 for d-major and token-major value pages,
-    # MXFP4 sweeps at D = 128 / 256 in both V-decode placements; the e4m3 sweep
-    # at the three head dims
-    assert sum("sweep_kernel" in n for n in names) == 2 * 3 + 2 * 2
+    # the e4m3 sweep at the three head dims, the MXFP4 sweep at D = 128 / 256
+    assert sum("sweep_kernel" in n for n in names) == 2 * 3
     assert sum("sweep8_kernel" in n for n in names) == 3
+    assert sum("sweep4_kernel" in n for n in names) == 2
     # the combine with clamped and with skipped loads, at D = 64 / 128 / 256
     assert sum("combine_kernel" in n for n in names) == 2 * 3
     assert any("append_kernel" in n for n, _ in kernels(asm["append.hip"]))
@@ -108,17 +108,17 @@ def test_m0_written_only_by_the_dma_statements(asm):
 
 def test_group_reductions_use_lane_swaps(asm):
     for name, body in kernels(asm["smallw.hip"]):
-        if "sweep_kernel" not in name and "sweep8_kernel" not in name:
+        if not any(k in name for k in ("sweep_kernel", "sweep8_kernel", "sweep4_kernel")):
             continue
         ins = [i.split()[0] for i in instructions(body)]
         assert any(i.startswith("v_permlane16_swap_b32") for i in ins), name
         assert any(i.startswith("v_permlane32_swap_b32") for i in ins), name
-        if "ELi4ELi0E" in name:     # bf16 sweeps: <D, 4, 0, false, VT>
+        if "sweep_kernel" in name:     # bf16 sweeps: <D, 4, VT>
             assert not any(i.startswith("ds_bpermute") for i in ins), name
             # token-major value pages (VT = true): the PV operand comes from
             # transpose reads, and only there
             vt = any(i.startswith("ds_read_b64_tr_b16") for i in ins)
-            assert vt == ("ELb0ELb1EEE" in name), name
+            assert vt == ("ELi4ELb1EEE" in name), name
 
 
 def test_combine_merges_rows_with_dpp(asm):

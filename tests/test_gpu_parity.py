@@ -272,7 +272,7 @@ def test_split_count_invariance(force):
 def test_trace_pages_match_oracle_gather(name, force):
     w = make_workload(name)
     plan = dv.plan_for(w, force_splits=force)
-    pl = oracle.plan(P=w.P, Hkv=w.Hkv, D=w.D, kv_fp8=w.kv == "fp8", seq_lens=w.seq_lens,
+    pl = oracle.plan(P=w.P, Hkv=w.Hkv, D=w.D, kv_fp8=w.kv == "fp8", kv=w.kv, seq_lens=w.seq_lens,
                      num_cus=_num_cus(), force_splits=force)
     np.testing.assert_array_equal(sw.small_w_attention_plan_export(plan),
                                   oracle.plan_export(pl, R=w.W * w.G))

@@ -512,8 +512,8 @@ def test_plan_partitions_every_request_into_balanced_splits():
         pl = oracle.plan(P=P, Hkv=Hkv, D=D, kv_fp8=fp8, seq_lens=seq, num_cus=256,
                          force_splits=force)
         assert pl["U"] == Hkv * sum(pl["splits"]) == len(pl["units"])
-        if force == 0 and P * Hkv <= 256:
-            assert pl["U"] <= 256 * (1 if D == 256 else 2)   # never a second round
+        if force == 0 and P * Hkv <= 256:                   # never a second round
+            assert pl["U"] <= 256 * (1 if D == 256 or fp8 else 2)
         k = 0
         for p in range(P):
             n, S = pl["n_pg"][p], pl["splits"][p]
@@ -551,6 +551,14 @@ def test_plan_at_the_long_context_shapes():
     # tiny: 17 pages, one head, 512 slots (D=64) -> the 8-page floor: floor(17/8) = 2
     pl = oracle.plan(P=1, Hkv=1, D=64, kv_fp8=False, seq_lens=[260], num_cus=256)
     assert pl["splits"] == [2] and [u[3:] for u in pl["units"]] == [(0, 8), (8, 17)]
+    # draft block at D = 128: a bf16 unit leaves room for a second on its CU, an
+    # e4m3 or MXFP4 one does not.  8 requests x 8 heads; with 1000 pages each the
+    # 8-page floor never binds, so the budget is spent evenly: 512 slots -> 64
+    # splits (8 a request), 256 slots -> 32 (4 a request)
+    for kv, S in (("bf16", 8), ("fp8", 4), ("mxfp4", 4)):
+        pl = oracle.plan(P=8, Hkv=8, D=128, kv_fp8=kv == "fp8", kv=kv, seq_lens=[16000] * 8,
+                         num_cus=256)
+        assert pl["splits"] == [S] * 8 and pl["U"] == 64 * S
 
 
 def test_plan_minimises_the_largest_split_by_brute_force():
@@ -619,10 +627,10 @@ def test_row_exact_plan_splits_at_fixed_page_multiples():
     # with a sliding window the first piece starts below the window's first page,
     # on the grid of the pages one arithmetic step groups: L = 1000, W = 4, causal,
     # window 700 -> row 0's first key 996 - 700 + 1 = 297, page 18; B = 20 -> k = 0.
-    # bf16 groups page pairs: piece 0 starts at 18; e4m3 groups 8 pages: at 16
-    for fp8, start in ((False, 18), (True, 16)):
-        pl = oracle.plan(P=1, Hkv=1, D=128, kv_fp8=fp8, seq_lens=[1000], num_cus=256,
-                         split_pages=20, W=4, causal=True, window_left=700)
+    # bf16 groups page pairs: piece 0 starts at 18; e4m3 and MXFP4 group 8 pages: at 16
+    for kv, start in (("bf16", 18), ("fp8", 16), ("mxfp4", 16)):
+        pl = oracle.plan(P=1, Hkv=1, D=128, kv_fp8=kv == "fp8", kv=kv, seq_lens=[1000],
+                         num_cus=256, split_pages=20, W=4, causal=True, window_left=700)
         assert pl["splits"] == [4] and pl["units"][0][3:] == (start, 20)
         assert [u[3:] for u in pl["units"][1:]] == [(20, 40), (40, 60), (60, 63)]
 
