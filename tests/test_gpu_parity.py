@@ -391,11 +391,10 @@ def test_mxfp4_edge_shapes(case, force):
     check(w, o, l, *oracle.attention(w))
 
 
-# Five or six row tiles (W*G in 65..96): two row-tile waves share SIMDs 0 and 1;
-# the MXFP4 V decode then runs only on the four waves of SIMDs 2 and 3 (the
-# row-tile waves among them after their chunk's PV).  The e4m3 cases check the
-# same shapes on the e4m3 sweep.  T = ceil(W*G / 16) noted per case.
-DECH_CASES = [
+# Five or six row tiles (W*G in 65..96): two row-tile waves share SIMDs 0 and 1,
+# and some waves hold no row tile but still stream and (MXFP4) decode.  The
+# e4m3 and MXFP4 sweeps on those shapes.  T = ceil(W*G / 16) noted per case.
+TILE56_CASES = [
     ("fp8", dict(P=2, Hq=5, Hkv=1, D=64, ctx=(37, 300), W=16, causal=True)),        # T = 5
     ("fp8", dict(P=1, Hq=12, Hkv=2, D=128, ctx=(1000,), W=16, causal=False)),      # T = 6
     ("fp8", dict(P=3, Hq=20, Hkv=4, D=256, ctx=(0, 90, 777), W=13, causal=True)),  # T = 5
@@ -405,10 +404,10 @@ DECH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(DECH_CASES)))
+@pytest.mark.parametrize("case", range(len(TILE56_CASES)))
 @pytest.mark.parametrize("force", [0, 3])
-def test_v_decode_on_simds_2_and_3(case, force):
-    kv, spec = DECH_CASES[case]
+def test_five_and_six_row_tiles(case, force):
+    kv, spec = TILE56_CASES[case]
     G = spec["Hq"] // spec["Hkv"]
     assert -(-spec["W"] * G // 16) in (5, 6)
     npg = sum(-(-(c + spec["W"]) // 16) for c in spec["ctx"])
