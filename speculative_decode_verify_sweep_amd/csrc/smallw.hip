@@ -18,7 +18,10 @@
 // In this orientation a lane's accumulator registers all belong to one query
 // row, so the online-softmax max/sum and the rescale factor are per-lane
 // scalars, and the S^T accumulator registers of two 16-token tiles are
-// exactly the B operand of the PV MFMA (no shuffle through LDS).
+// exactly the B operand of the PV MFMA (no shuffle through LDS).  That is the
+// bf16 sweep; e4m3 and MXFP4 pools have sweeps of their own (sweep8_kernel,
+// sweep4_kernel) with the same units, orientation and epilogue, 128-token
+// steps, and the scores on the scaled 16x16x128 MFMA straight from the codes.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
