@@ -244,21 +244,27 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     }
 }
 
-// Byte J of w (two E2M1 codes, the low nibble first) -> 2 bf16, each times
-// 2^(e-127) for the E8M0 byte e.  The convert takes only the exponent field of
-// its fp32 scale operand, which e << 23 sets, so this is exact for every byte
-// (0 gives 2^-127, 0xFF NaN).  The pair is moved as a whole word: reading an
-// element out of the convert's 2 x bf16 result can lose its upper half.
-template <int J>
-__device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t w, uint32_t e8) {
-    return __builtin_bit_cast(
-        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, __builtin_bit_cast(float, e8 << 23), J));
+// The convert's scale operand for E8M0 byte K of the word s.  The convert reads
+// only the exponent field (bits 23..30) of its fp32 scale operand (measured:
+// the sign and mantissa bits change nothing, and 0 gives 2^-127, 0xFF NaN), so
+// byte K shifted into that field is the scale 2^(e-127) exactly, whatever the
+// neighbouring bytes put around it: one shift per scale.
+template <int K>
+__device__ __forceinline__ float e8m0_operand(uint32_t s) {
+    return __builtin_bit_cast(float, K == 3 ? s >> 1 : s << (23 - 8 * K));
 }
-// byte J of w with its low code times 2^(e_lo-127) and its high code times
-// 2^(e_hi-127): both halves are converted with each scale and one of each kept
+// Byte J of w (two E2M1 codes, the low nibble first) -> 2 bf16, each times the
+// scale sc.  The pair is moved as a whole word: reading an element out of the
+// convert's 2 x bf16 result can lose its upper half.
 template <int J>
-__device__ __forceinline__ uint32_t e2m1x2_two_scales(uint32_t w, uint32_t e_lo, uint32_t e_hi) {
-    return (e2m1x2_to_bf16<J>(w, e_lo) & 0xFFFFu) | (e2m1x2_to_bf16<J>(w, e_hi) & 0xFFFF0000u);
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t w, float sc) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, J));
+}
+// byte J of w with its low code times sc_lo and its high code times sc_hi:
+// both halves are converted with each scale and one of each kept
+template <int J>
+__device__ __forceinline__ uint32_t e2m1x2_two_scales(uint32_t w, float sc_lo, float sc_hi) {
+    return (e2m1x2_to_bf16<J>(w, sc_lo) & 0xFFFFu) | (e2m1x2_to_bf16<J>(w, sc_hi) & 0xFFFF0000u);
 }
 
 // Epilogue of a work unit, on a wave that owns row tile w: normalise the
@@ -1372,52 +1378,70 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
         }
     };
 
-    // ---- decode of step j's V^T codes: item (chunk c, page pg, row d) is the
-    // row's 16 codes (8 bytes, the even token in the low nibble) and the 16
-    // tokens' E8M0 bytes of its 32-row block; each code byte is converted with
-    // each of its two tokens' scales and one half of each kept.  Tokens past
-    // the unit's keys (stale slots, pages past the end) are written as zeros.
+    // ---- decode of step j's V^T codes.  Item (chunk c, page pg, rows d and
+    // d + 16 of one 32-row block): the two rows' 16 codes each (8 bytes, the
+    // even token in the low nibble) and the 16 tokens' E8M0 bytes of their
+    // block, which both rows share.  The rows' nibbles are re-paired so that
+    // byte i of E (O) holds token 2i (2i + 1) of row d in its low nibble and of
+    // row d + 16 in its high one: both codes of a byte then take one token's
+    // scale, one convert per byte, and the two rows' values are sorted back
+    // into their rows by byte permutes.  Tokens past the unit's keys (stale
+    // slots, pages past the end) are written as zeros.
     auto decode = [&](int j, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        constexpr int NB = NDEC < 4 ? NDEC : 4;  // items whose reads are issued together
+        constexpr int NP = NDEC / 2;  // row pairs per thread and step
+        uint2 ca[NP], cb[NP];
+        u32x4 sv[NP];
 #pragma unroll
-        for (int n0 = 0; n0 < NDEC; n0 += NB) {
-            uint2 cw[NB];
-            u32x4 sv[NB];
+        for (int n = 0; n < NP; ++n) {
+            const int it = tid + kSweepThreads * n;
+            const int dl = it % (D / 2), pg = (it / (D / 2)) & 3, c = it / (2 * D);
+            const int d = 32 * (dl >> 4) + (dl & 15);
+            const uint8_t* src = ring + ((2 * j + c) % NR) * CHB;
+            ca[n] = *reinterpret_cast<const uint2*>(src + OFF_V + pg * PGB + d * 8);
+            cb[n] = *reinterpret_cast<const uint2*>(src + OFF_V + pg * PGB + (d + 16) * 8);
+            sv[n] = *reinterpret_cast<const u32x4*>(src + OFF_VS + pg * SPB + (d >> 5) * 16);
+        }
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                const int it = tid + kSweepThreads * (n0 + n);
-                const int d = it % D, pg = (it / D) & 3, c = it / (4 * D);
-                const uint8_t* src = ring + ((2 * j + c) % NR) * CHB;
-                cw[n] = *reinterpret_cast<const uint2*>(src + OFF_V + pg * PGB + d * 8);
-                sv[n] = *reinterpret_cast<const u32x4*>(src + OFF_VS + pg * SPB + (d >> 5) * 16);
-            }
+        for (int n = 0; n < NP; ++n) {
+            const int it = tid + kSweepThreads * n;
+            const int dl = it % (D / 2), pg = (it / (D / 2)) & 3, c = it / (2 * D);
+            const int d = 32 * (dl >> 4) + (dl & 15);
+            const u32x4 sc = sv[n];
+            const int vc = TAIL ? min(max(jend - (un.pb + 4 * (2 * j + c) + pg) * kPage, 0), 16) : 16;
+            // row d: pieces 2 (pg & 1) + h of block 2c + (pg >> 1); row d + 16 one
+            // d tile (1 KiB) further
+            uint8_t* dst = stg + (2 * c + (pg >> 1)) * BLK + (d >> 4) * 1024 + (pg & 1) * 512 +
+                           (d & 15) * 16;
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                const int it = tid + kSweepThreads * (n0 + n);
-                const int d = it % D, pg = (it / D) & 3, c = it / (4 * D);
-                const u32x4 s = sv[n];
-                u32x4 o0 = {e2m1x2_two_scales<0>(cw[n].x, s[0] & 0xFFu, (s[0] >> 8) & 0xFFu),
-                            e2m1x2_two_scales<1>(cw[n].x, (s[0] >> 16) & 0xFFu, s[0] >> 24),
-                            e2m1x2_two_scales<2>(cw[n].x, s[1] & 0xFFu, (s[1] >> 8) & 0xFFu),
-                            e2m1x2_two_scales<3>(cw[n].x, (s[1] >> 16) & 0xFFu, s[1] >> 24)};
-                u32x4 o1 = {e2m1x2_two_scales<0>(cw[n].y, s[2] & 0xFFu, (s[2] >> 8) & 0xFFu),
-                            e2m1x2_two_scales<1>(cw[n].y, (s[2] >> 16) & 0xFFu, s[2] >> 24),
-                            e2m1x2_two_scales<2>(cw[n].y, s[3] & 0xFFu, (s[3] >> 8) & 0xFFu),
-                            e2m1x2_two_scales<3>(cw[n].y, (s[3] >> 16) & 0xFFu, s[3] >> 24)};
-                if constexpr (TAIL) {
-                    const int vc = min(max(jend - (un.pb + 4 * (2 * j + c) + pg) * kPage, 0), 16);
-#pragma unroll
-                    for (int k2 = 0; k2 < 4; ++k2) {
-                        o0[k2] &= (2 * k2 + 1 < vc) ? 0xffffffffu : (2 * k2 < vc ? 0x0000ffffu : 0u);
-                        o1[k2] &= (2 * k2 + 9 < vc) ? 0xffffffffu : (2 * k2 + 8 < vc ? 0x0000ffffu : 0u);
+            for (int h = 0; h < 2; ++h) {  // tokens 8h .. 8h + 7
+                const uint32_t a = h ? ca[n].y : ca[n].x, b = h ? cb[n].y : cb[n].x;
+                const uint32_t E = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+                const uint32_t O = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+                u32x4 ra, rb;  // rows d and d + 16: word i = tokens 8h + 2i, 8h + 2i + 1
+                auto pair = [&](auto i_tag) {
+                    constexpr int i = decltype(i_tag)::value;
+                    // token 8h + 2i: scale byte 2i of word 2h + (i >> 1) of sc
+                    const uint32_t sw = sc[2 * h + (i >> 1)];
+                    const uint32_t te = e2m1x2_to_bf16<i>(E, e8m0_operand<2 * (i & 1)>(sw));
+                    const uint32_t to = e2m1x2_to_bf16<i>(O, e8m0_operand<2 * (i & 1) + 1>(sw));
+                    uint32_t wa = (te & 0xFFFFu) | (to << 16);
+                    uint32_t wb = (te >> 16) | (to & 0xFFFF0000u);
+                    if constexpr (TAIL) {
+                        const int t = 8 * h + 2 * i;
+                        const uint32_t m = t + 1 < vc ? 0xffffffffu : (t < vc ? 0x0000ffffu : 0u);
+                        wa &= m;
+                        wb &= m;
                     }
-                }
-                // pieces 2 (pg & 1) and 2 (pg & 1) + 1 of row d of block 2c + (pg >> 1)
-                uint8_t* dst = stg + (2 * c + (pg >> 1)) * BLK + (d >> 4) * 1024 + (pg & 1) * 512 +
-                               (d & 15) * 16;
-                *reinterpret_cast<u32x4*>(dst) = o0;
-                *reinterpret_cast<u32x4*>(dst + 256) = o1;
+                    ra[i] = wa;
+                    rb[i] = wb;
+                };
+                pair(std::integral_constant<int, 0>{});
+                pair(std::integral_constant<int, 1>{});
+                pair(std::integral_constant<int, 2>{});
+                pair(std::integral_constant<int, 3>{});
+                *reinterpret_cast<u32x4*>(dst + 256 * h) = ra;
+                *reinterpret_cast<u32x4*>(dst + 1024 + 256 * h) = rb;
             }
         }
     };
