@@ -580,7 +580,7 @@ def test_row_exact_mode_matches_oracle(name, B):
     check(w, o, l, *oracle.attention(w))
 
 
-@pytest.mark.parametrize("kv,B", [("bf16", 8), ("bf16", 100), ("fp8", 8)])
+@pytest.mark.parametrize("kv,B", [("bf16", 8), ("bf16", 100), ("fp8", 8), ("mxfp4", 8)])
 def test_row_exact_rows_do_not_depend_on_the_window(kv, B):
     """In row-exact mode, row i of a W-row causal call is bitwise the 1-row call
     at length L - W + i + 1 with the same query, pool and block table."""
@@ -673,11 +673,12 @@ def test_sliding_window_trace_pages_skip_the_early_pages():
     check(w, o, l, *oracle.attention(w))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "mxfp4"])
 def test_row_exact_with_window_rows_do_not_depend_on_the_window_rows(kv):
     """With a sliding window the first row-exact piece starts below row 0's
     window, aligned to the pages one arithmetic step groups (2 for bf16, 8 for
-    e4m3), so every row's pieces group their pages alike in every call."""
+    e4m3 and MXFP4), so every row's pieces group their pages alike in every
+    call."""
     w = make_workload(None, P=1, Hq=24, Hkv=4, D=256, ctx=(2000,), W=16, causal=True,
                       kv=kv, placement="permuted", pool_pages=140, seed=97, poison=False,
                       window_left=500)
