@@ -260,12 +260,6 @@ template <int J>
 __device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t w, float sc) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, J));
 }
-// byte J of w with its low code times sc_lo and its high code times sc_hi:
-// both halves are converted with each scale and one of each kept
-template <int J>
-__device__ __forceinline__ uint32_t e2m1x2_two_scales(uint32_t w, float sc_lo, float sc_hi) {
-    return (e2m1x2_to_bf16<J>(w, sc_lo) & 0xFFFFu) | (e2m1x2_to_bf16<J>(w, sc_hi) & 0xFFFF0000u);
-}
 
 // Epilogue of a work unit, on a wave that owns row tile w: normalise the
 // rows, then write the final bf16 output and LSE (an unsplit request) or the
