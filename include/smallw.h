@@ -259,6 +259,23 @@ int small_w_attention_trace_pages(const smallw_plan* plan, const int32_t* block_
                                   const int32_t* seq_lens, int32_t* pages_out,
                                   size_t max_unit_pages, void* stream);
 
+/*
+ * Input check for callers that cannot vouch for their tables: on `stream`,
+ * write bad_out[p] (device int32 [P]) = the number of block_table entries that
+ * a call with this plan reads for request p and that lie outside
+ * [0, num_pages), or -1 when seq_lens[p] breaks the device-length rules
+ * (L < 0, L > 16 * max_pages_per_req, or causal with 0 < L < W).  The entries
+ * read are those of the pages small_w_attention_trace_pages lists for p's
+ * units: logical pages from the first one a row attends (moved down to the
+ * row-exact grouping grid in row-exact mode with a sliding window) to
+ * ceil(L / 16).  A run does not fault on bad entries (they are clamped) but
+ * gives undefined numbers for that request; all zeros means every page the run
+ * reads is a pool page.  The plan is only read; nothing is allocated; bad_out
+ * is written by one kernel on `stream` (SMALLW_EDEVICE if the launch fails).
+ */
+int small_w_attention_check_pages(const smallw_plan* plan, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t* bad_out, void* stream);
+
 /* Largest page count of any work unit of the plan (host lengths). */
 size_t small_w_attention_plan_max_unit_pages(const smallw_plan* plan);
 

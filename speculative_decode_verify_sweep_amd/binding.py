@@ -77,6 +77,8 @@ def lib():
         L.small_w_attention_trace_pages.argtypes = [vp, vp, vp, vp, sz, vp]
         L.small_w_kv_append.argtypes = [vp] * 10
         L.small_w_attention_trace_pages.restype = ctypes.c_int
+        L.small_w_attention_check_pages.argtypes = [vp] * 5
+        L.small_w_attention_check_pages.restype = ctypes.c_int
         L.small_w_attention_plan_destroy.argtypes = [vp]
         L.small_w_attention_plan_destroy.restype = None
         L.small_w_stream_read.argtypes = [vp, sz, vp, vp, vp, vp]
@@ -281,6 +283,23 @@ def small_w_attention_trace_pages(plan: Plan, block_table, seq_lens, pages_out,
                                              _ptr(pages_out), maxp, _stream(stream))
     if rc != SMALLW_OK:
         raise SmallwError(rc, "small_w_attention_trace_pages")
+
+
+def small_w_attention_check_pages(plan: Plan, block_table, seq_lens, bad_out,
+                                  stream=None) -> None:
+    """Enqueue the table check: bad_out (device int32 [P]) receives, per
+    request, the count of block-table entries the call reads that lie outside
+    the pool, or -1 for a device length outside the rules."""
+    pr = plan.problem
+    dev = _current_device()
+    _check(block_table, "block_table", ("int32",), numel=pr.num_reqs * pr.max_pages_per_req,
+           device=dev)
+    _check(seq_lens, "seq_lens", ("int32",), numel=pr.num_reqs, device=dev)
+    _check(bad_out, "bad_out", ("int32",), numel=pr.num_reqs, device=dev)
+    rc = lib().small_w_attention_check_pages(plan.handle, _ptr(block_table), _ptr(seq_lens),
+                                             _ptr(bad_out), _stream(stream))
+    if rc != SMALLW_OK:
+        raise SmallwError(rc, "small_w_attention_check_pages")
 
 
 def small_w_kv_append(plan: Plan, k_new, v_new, k_pool, v_pool, k_scale, v_scale,

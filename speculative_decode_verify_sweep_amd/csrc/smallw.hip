@@ -1787,6 +1787,36 @@ __global__ void trace_kernel(Params a, int32_t* out, int64_t maxp) {
     for (; k < maxp; ++k) out[u * maxp + k] = -1;
 }
 
+// Table check, one workgroup per request p: how many of the block-table entries
+// a call reads for p (the pages from the first split's first page to the last
+// split's end, as decode_unit gives them to the sweep) lie outside
+// [0, num_pages); -1 when the device length breaks the rules the plan's host
+// lengths were checked against.  Integer work only; a fixed reduction order.
+__global__ __launch_bounds__(kThreads) void check_kernel(Params a, int32_t* bad) {
+    const int p = blockIdx.x;
+    const int L = a.seq[p];
+    if (L < 0 || L > a.bt_stride * kPage || (a.causal && L > 0 && L < a.W)) {
+        if (threadIdx.x == 0) bad[p] = -1;
+        return;
+    }
+    const int S = (a.unit_off[p + 1] - a.unit_off[p]) / a.Hkv;
+    const int pb = decode_unit(a, a.unit_off[p]).pb;
+    const int pe = decode_unit(a, a.unit_off[p] + S - 1).pe;
+    int cnt = 0;
+    for (int n = pb + int(threadIdx.x); n < pe; n += kThreads) {
+        const int pg = a.bt[int64_t(p) * a.bt_stride + n];
+        cnt += (pg < 0 || pg >= a.num_pages) ? 1 : 0;
+    }
+    __shared__ int part[kThreads];
+    part[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int h = kThreads / 2; h > 0; h >>= 1) {
+        if (int(threadIdx.x) < h) part[threadIdx.x] += part[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) bad[p] = part[0];
+}
+
 // ==== host side: launches, events, error text (device code ends above) ====
 thread_local char g_err[256] = "";
 
@@ -2039,6 +2069,19 @@ int small_w_attention_trace_pages(const smallw_plan* pl, const int32_t* block_ta
     hipLaunchKernelGGL(trace_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        a, pages_out, int64_t(max_unit_pages));
     return check_launch("trace kernel launch");
+}
+
+int small_w_attention_check_pages(const smallw_plan* pl, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t* bad_out, void* stream) {
+    if (!pl || !block_table || !seq_lens || !bad_out) return SMALLW_EINVAL;
+    Params a;
+    memset(&a, 0, sizeof a);
+    fill_params(a, pl);
+    a.bt = block_table;
+    a.seq = seq_lens;
+    hipLaunchKernelGGL(check_kernel, dim3(pl->prob.num_reqs), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a, bad_out);
+    return check_launch("check kernel launch");
 }
 
 const char* small_w_attention_strerror(int status) {

@@ -294,6 +294,70 @@ def _num_cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
+def _pages_read(w, force, split_pages):
+    """Per request, the logical pages the oracle's planner gives its units."""
+    pl = oracle.plan(P=w.P, Hkv=w.Hkv, D=w.D, kv_fp8=w.kv == "fp8", kv=w.kv, seq_lens=w.seq_lens,
+                     num_cus=_num_cus(), force_splits=force, split_pages=split_pages, W=w.W,
+                     causal=w.causal, window_left=w.window_left)
+    read = [set() for _ in range(w.P)]
+    for (p, _kvh, _s, pb, pe) in pl["units"]:
+        read[p].update(range(pb, pe))
+    return read
+
+
+@pytest.mark.parametrize("force,split_pages", [(0, 0), (3, 0), (0, 8)])
+def test_table_check_counts_the_bad_entries_a_call_reads(force, split_pages):
+    """small_w_attention_check_pages counts, per request, the block-table entries
+    outside the pool among the pages the call reads (the oracle planner's unit
+    ranges), and flags device lengths outside the rules with -1.  Entries the call
+    does not read (past the last page, below the window's first page) are not
+    counted, and changing them leaves the outputs bitwise unchanged."""
+    w = make_workload(None, P=4, Hq=8, Hkv=2, D=128, ctx=(700, 1500, 40, 333), W=8,
+                      causal=True, kv="bf16", placement="permuted", pool_pages=200, seed=131,
+                      max_pages=120, window_left=600)
+    plan = dv.plan_for(w, force_splits=force, split_pages=split_pages)
+    read = _pages_read(w, force, split_pages)
+    bt = w.block_table.copy()
+    rng = np.random.default_rng(9)
+    want = np.zeros(w.P, dtype=np.int32)
+    unread = []
+    for p in range(w.P):
+        rd = sorted(read[p])
+        assert rd, p
+        unread += [(p, n) for n in range(bt.shape[1]) if n not in read[p]]
+        for n in rng.choice(rd, size=min(3, len(rd)), replace=False):
+            bt[p, n] = rng.choice([-1, w.num_pages, 1 << 30])
+            want[p] += 1
+    # entries no unit reads: garbage that must change nothing
+    bt_unread = w.block_table.copy()
+    for p, n in unread:
+        bt_unread[p, n] = rng.choice([-7, w.num_pages + 3, -(1 << 30)])
+    dev_bt = torch.from_numpy(bt).cuda()
+    dev_sl = torch.from_numpy(w.seq_lens).cuda()
+    bad = torch.full((w.P,), -99, dtype=torch.int32, device="cuda")
+    announce(f"table check force={force} split_pages={split_pages}")
+    sw.small_w_attention_check_pages(plan, dev_bt, dev_sl, bad)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bad.cpu().numpy(), want)
+    # a clean table, the unread-garbage table: zero bad entries, bitwise equal runs
+    for table in (w.block_table, bt_unread):
+        sw.small_w_attention_check_pages(plan, torch.from_numpy(table).cuda(), dev_sl, bad)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bad.cpu().numpy(), np.zeros(w.P, np.int32))
+    o, l = gpu_run(w, force_splits=force, split_pages=split_pages)
+    o2, l2 = gpu_run(dataclasses.replace(w, block_table=bt_unread), force_splits=force,
+                     split_pages=split_pages)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(l2, l)
+    # device lengths outside the rules: negative, past the table row, causal 0 < L < W
+    sl = w.seq_lens.copy()
+    sl[0], sl[2], sl[3] = -3, w.block_table.shape[1] * 16 + 1, w.W - 1
+    sw.small_w_attention_check_pages(plan, torch.from_numpy(w.block_table).cuda(),
+                                     torch.from_numpy(sl).cuda(), bad)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bad.cpu().numpy(), np.array([-1, 0, -1, -1], np.int32))
+
+
 # ------------------------------------------------------------------ fp8-e4m3 KV
 def test_fp8_verify_batched_contexts():
     w = make_workload("fp8")
