@@ -80,7 +80,7 @@
  * exception crosses this interface.  All shape and range checks happen in
  * small_w_attention_plan on the host.  Block-table entries outside
  * [0, num_pages) are clamped on the device, so they cannot fault, but give
- * undefined numbers.
+ * undefined numbers; small_w_attention_check_pages counts them.
  */
 #ifndef SMALLW_H
 #define SMALLW_H
