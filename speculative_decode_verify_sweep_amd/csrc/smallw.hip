@@ -251,7 +251,8 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // neighbouring bytes put around it: one shift per scale.
 template <int K>
 __device__ __forceinline__ float e8m0_operand(uint32_t s) {
-    return __builtin_bit_cast(float, K == 3 ? s >> 1 : s << (23 - 8 * K));
+    if constexpr (K == 3) return __builtin_bit_cast(float, s >> 1);
+    else return __builtin_bit_cast(float, s << (23 - 8 * K));
 }
 // Byte J of w (two E2M1 codes, the low nibble first) -> 2 bf16, each times the
 // scale sc.  The pair is moved as a whole word: reading an element out of the
