@@ -6,11 +6,15 @@
 * the integer plan export is bit-exact against the oracle's restatement of
   the written split specification, over a seeded sweep of problems;
 * small_w_attention_run rejects null pointers and short or misaligned
-  workspaces before touching the device.
+  workspaces before touching the device;
+* the header serves a C11 caller: tests/c_abi_host.c builds with every
+  warning an error, links against the library and passes its host checks.
 """
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -27,6 +31,19 @@ def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(small_w_\w+)\s*\(", text)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_header_serves_a_c11_caller(tmp_path):
+    exe = str(tmp_path / "c_abi_host")
+    pkg = os.path.dirname(B.LIB_PATH)
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi_host.c"),
+           "-o", exe, "-L", pkg, "-lsmallw", f"-Wl,-rpath,{pkg}"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.stdout, run.stderr)
 
 
 def test_library_exports_every_declared_function():

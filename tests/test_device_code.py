@@ -63,7 +63,7 @@ def instructions(body):
 
 def test_every_kernel_is_present(asm):
     names = [n for n, _ in kernels(asm["smallw.hip"])]
-    for k in ("sweep_kernel", "combine_kernel", "trace_kernel"):
+    for k in ("sweep_kernel", "combine_kernel", "trace_kernel", "check_kernel"):
         assert any(k in n for n in names), (k, names)
     # bf16 sweeps at D = 64 / 128 / 256 for d-major and token-major value pages,
     # the e4m3 sweep at the three head dims, the MXFP4 sweep at D = 128 / 256
