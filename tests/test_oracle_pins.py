@@ -215,7 +215,7 @@ def test_oracle_matches_torch_sdpa_fp64(case):
     Q = q_f64(w)
     for p in range(w.P):
         L = int(w.seq_lens[p])
-        M = torch.from_numpy(mask_matrix(L, w.W, w.causal, K.shape[2], w.window_left))
+        M = torch.from_numpy(np.array(mask_matrix(L, w.W, w.causal, K.shape[2], w.window_left)))
         kk = torch.from_numpy(K[p]).repeat_interleave(w.G, dim=0)[None]     # [1][Hq][L][D]
         vv = torch.from_numpy(V[p]).repeat_interleave(w.G, dim=0)[None]
         qq = torch.from_numpy(Q[p]).permute(1, 0, 2)[None]                   # [1][Hq][W][D]
