@@ -784,26 +784,21 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
-    // ---- DMA work of this wave.  K: instructions w and w + 8 of a chunk's KI
-    // (page i / IPP), rows swizzled so that a lane's 16-byte slot sigma of row
-    // (page, token) sits at sigma ^ h, h = (page << 2 | token & 3) masked to the
-    // row: the 8 and 16 lanes of one operand read then hit distinct banks.
-    // Scales: wave 6 the chunk's K scales, wave 7 its V scales (lane l: page
-    // l >> 4, token l & 15).  V^T: instruction i of chunk q of a PV step is
-    // issued by wave (i + q KI) mod 8, a raw 1 KiB copy.
-    uint32_t koff[2];
-    int kpg[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int i = (w + 8 * j) % KI;
-        const int qc = 64 * (i % IPP) + l;
-        const int tr = qc / SPR, ps = qc % SPR;
-        const int pg = i / IPP;
-        const int h = ((pg << 2) | (tr & 3)) & (SPR - 1);
-        koff[j] = uint32_t(tr * D + 16 * (ps ^ h));
-        kpg[j] = pg;
-    }
-    const bool issues_scale = w >= 6;
+    // ---- DMA work.  The eight pages of a PV step (two chunks of four) are
+    // dealt to the issuing waves: the waves without a row tile when there are
+    // at least two of them, else all eight.  Issuer e takes pages e, e + NF,
+    // ... of the step; for each it reads the pool page id once and moves the
+    // page's K and V^T codes, IPP 1 KiB instructions each.  K rows are
+    // swizzled so that a lane's 16-byte slot sigma of row (page, token) sits
+    // at sigma ^ h, h = (page << 2 | token & 3) masked to the row: the 8 and 16
+    // lanes of one operand read then hit distinct banks.  V^T is a raw copy.
+    // A chunk's K scales go to issuer 2q mod NF and its V scales to issuer
+    // 2q + 1 mod NF (chunk q of the step; lane l: page l >> 4, token l & 15).
+    // Measured: a row-tile wave that also issued loads spent about a fifth of
+    // each step on them, one page-id read and wait per instruction.
+    const int n_free = 8 - T;
+    const int NF = n_free >= 2 ? n_free : 8;
+    const int e_iss = n_free >= 2 ? w - T : w;  // issuer index; negative: issues nothing
     const uint32_t kr_base = uint32_t(reinterpret_cast<uintptr_t>(kring));
     const uint32_t vr_base = uint32_t(reinterpret_cast<uintptr_t>(vring));
     const uint32_t scl_base = uint32_t(reinterpret_cast<uintptr_t>(&scl[0][0]));
@@ -811,57 +806,53 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
     const float* vscale = a.v_scale;
     asm volatile("" : "+s"(kscale), "+s"(vscale));
 
-    // pages past the unit's end are replaced by the chunk's first page (always
-    // present); their tokens are masked
-    auto issue_k = [&](int t) {
-        const int ks = t % NK;
-        const uint32_t slot = uint32_t(ks * CHB);
+    // chunk t, which is chunk q (0 or 1) of its PV step; pages past the
+    // unit's end are replaced by the chunk's first page (always present),
+    // their tokens are masked
+    auto issue_chunk = [&](int t, int q) {
+        if (e_iss < 0) return;
+        const uint32_t kslot = uint32_t((t % NK) * CHB), vslot = uint32_t((t % NV) * CHB);
+#pragma unroll 1
+        for (int p8 = e_iss; p8 < 4 * q + 4; p8 += NF) {
+            const int pg = p8 - 4 * q;
+            if (pg < 0) continue;
+            int n = 4 * t + pg;
+            if (n >= npages) n = 4 * t;
+            const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
+            const uint8_t* kp = a.k + (int64_t(phys) * a.Hkv + kvh) * PGB;
+            const uint8_t* vp = a.v + (int64_t(phys) * a.Hkv + kvh) * PGB;
+            // the lane offsets are recomputed per page from an opaque copy of the
+            // lane index: hoisted out of the loop they cost registers the row
+            // tiles need (the issuing waves have time to spare)
+            int lane = l;
+            asm volatile("" : "+v"(lane));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int i = w + 8 * j;
-            if (i < KI) {
-                int n = 4 * t + kpg[j];
-                if (n >= npages) n = 4 * t;
-                const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
-                dma16(a.k + (int64_t(phys) * a.Hkv + kvh) * PGB + koff[j],
-                      __builtin_amdgcn_readfirstlane(kr_base + slot + 1024u * uint32_t(i)));
+            for (int m = 0; m < IPP; ++m) {
+                const int i = pg * IPP + m;
+                const int qc = 64 * m + lane;
+                const int tr = qc / SPR, ps = qc % SPR;
+                const int h = ((pg << 2) | (tr & 3)) & (SPR - 1);
+                dma16(kp + tr * D + 16 * (ps ^ h),
+                      __builtin_amdgcn_readfirstlane(kr_base + kslot + 1024u * uint32_t(i)));
+                dma16(vp + 16 * qc,
+                      __builtin_amdgcn_readfirstlane(vr_base + vslot + 1024u * uint32_t(i)));
             }
         }
-        if (issues_scale) {
+        const bool ks_mine = e_iss == (2 * q) % NF, vs_mine = e_iss == (2 * q + 1) % NF;
+        if (ks_mine || vs_mine) {
             int n = 4 * t + (l >> 4);
             if (n >= npages) n = 4 * t;
-            const int phys = ptab[n - tbase];
-            const float* src = (w == 6 ? kscale : vscale) +
-                               (int64_t(phys) * a.Hkv + kvh) * kPage + (l & 15);
-            dma4(src, __builtin_amdgcn_readfirstlane(
-                          scl_base + uint32_t((ks * 128 + (w - 6) * 64) * 4)));
-        }
-    };
-    auto issue_v = [&](int gi) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int t = 2 * gi + q;
-            if (t >= nchunks) break;
-            const uint32_t slot = uint32_t((t % NV) * CHB);
-#pragma unroll
-            for (int m = 0; m < (KI + 7) / 8; ++m) {
-                const int i = ((w - q * KI) & 7) + 8 * m;
-                if (i < KI) {
-                    int n = 4 * t + i / IPP;
-                    if (n >= npages) n = 4 * t;
-                    const int phys = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
-                    dma16(a.v + (int64_t(phys) * a.Hkv + kvh) * PGB + 16 * (64 * (i % IPP) + l),
-                          __builtin_amdgcn_readfirstlane(vr_base + slot + 1024u * uint32_t(i)));
-                }
-            }
+            const int64_t off = (int64_t(ptab[n - tbase]) * a.Hkv + kvh) * kPage + (l & 15);
+            const uint32_t dst = scl_base + uint32_t((t % NK) * 128 * 4);
+            if (ks_mine) dma4(kscale + off, __builtin_amdgcn_readfirstlane(dst));
+            if (vs_mine) dma4(vscale + off, __builtin_amdgcn_readfirstlane(dst + 256u));
         }
     };
 
     // ---- prologue: step 0's K and V^T, then Q (one round trip for all of it).
     // Each step then issues the next step's loads right after its barrier, so
     // one step is in flight while the current one computes.
-    for (int t = 0; t < min(2, nchunks); ++t) issue_k(t);
-    if (nchunks > 0) issue_v(0);
+    for (int t = 0; t < min(2, nchunks); ++t) issue_chunk(t, t);
     // Q as two e4m3 parts (its loads overlap the DMA issued above)
     i32x8 qhi[KS4], qlo[KS4];
     uint32_t shi = 0, slo = 0;
@@ -1114,9 +1105,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 __syncthreads();
             }
-            issue_k(tn);
-            if (tn + 1 < nchunks) issue_k(tn + 1);
-            issue_v(j + 1);
+            issue_chunk(tn, 0);
+            if (tn + 1 < nchunks) issue_chunk(tn + 1, 1);
         }
     };
 
