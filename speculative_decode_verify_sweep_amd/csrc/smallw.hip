@@ -1207,7 +1207,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     constexpr int NR = 4;                      // ring slots: two steps
     constexpr int N16 = CHB / 16;              // 16-byte pieces of a chunk
     constexpr int NI = (N16 + 63) / 64;        // DMA instructions per chunk
-    constexpr int MI = (2 * NI + kSweepWaves - 1) / kSweepWaves;  // per wave and step, at most
+    constexpr int MI = (2 * NI + 5) / 6;       // per issuing wave and step, at most
     constexpr int BLK = 64 * D;                // staging bytes of one 32-token block
     constexpr int NDEC = 8 * D / kSweepThreads;  // decode items per thread and step
     // score tiles whose K operands are read together, (block, d tile) PV
@@ -1253,16 +1253,26 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
-    // ---- DMA work of this wave: instructions I = w + 8m of a step's 2 NI,
-    // I = NI c + i being instruction i of the step's chunk c.  Lane l of
+    // ---- DMA work.  The issuing waves take the instructions I = e + NF m of a
+    // step's 2 NI, issuer e of NF, I = NI c + i being instruction i of the
+    // step's chunk c.  With five or six row tiles the issuers are every wave
+    // but the second row-tile waves of SIMDs 0 and 1 (waves 4 and 5), which
+    // carry the longest chain of each step; otherwise all eight.  (Measured at
+    // 64K W = 16: those waves spent about a sixth of each step issuing; the
+    // call went from 53.9 to 51.9 us.  Leaving every load to the waves without
+    // a row tile was slower here: the gathered K instructions of one wave
+    // then queue behind each other.)  Lane l of
     // instruction i moves piece q = 64 i + l of the chunk; its source array
     // (0 K codes, 1 V^T codes, 2 K scales, 3 V scales), page of the chunk and
     // byte offset in that page-head are packed as off | pg << 12 | arr << 14,
     // bit 16 set for a piece inside the chunk.
+    const bool spare45 = T == 5 || T == 6;
+    const int NF = spare45 ? 12 - T : kSweepWaves;
+    const int e_iss = !spare45 ? w : (w < 4 ? w : (w >= T ? w - T + 4 : -1));  // -1: no loads
     uint32_t dsc[MI];
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
-        const int q = 64 * ((w + kSweepWaves * m) % NI) + l;
+        const int q = 64 * ((max(e_iss, 0) + NF * m) % NI) + l;
         int arr = 0, pg = 0, off = 0;
         if (q < 2 * D) {  // block (tt, k) = q >> 6, piece 16g + m = q & 63
             const int tt = (q >> 6) / KS4, k = (q >> 6) % KS4, gg = (q >> 4) & 3, m = q & 15;
@@ -1299,17 +1309,18 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     // so an LDS read placed between two of them would make the second wait
     // for the first's page id to arrive.
     auto issue_step = [&](int j) {
+        if (e_iss < 0) return;
         int phys[MI];
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
-            const int t = 2 * j + (w + kSweepWaves * m) / NI;
+            const int t = 2 * j + (e_iss + NF * m) / NI;
             int n = 4 * t + (int(dsc[m] >> 12) & 3);
             if (n >= npages) n = 4 * t;
             phys[m] = ptab[min(max(n - tbase, 0), kPtab - 1)];
         }
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
-            const int I = w + kSweepWaves * m;
+            const int I = e_iss + NF * m;
             if (I >= 2 * NI) break;  // wave-uniform
             const int c = I / NI, i = I % NI;
             const int t = 2 * j + c;
