@@ -717,8 +717,9 @@ __device__ __forceinline__ void load_split_q(const Params& a, int p, int kvh, bo
 // bf16 weights of the other paths).  Chunks are 64 tokens (4 pages); two
 // chunks (128 tokens, the MFMA's depth) make one PV step.
 //
-// K streams through a 4-chunk LDS ring (three chunks ahead), V^T through a
-// 2-step one (the next step ahead).
+// K and V^T each stream through a 4-chunk LDS ring (two PV steps): the next
+// step's chunks load while the current one computes, issued by the waves
+// that hold no row tile (by all eight when fewer than two are free).
 //
 // Token layout.  Score tile tt (16 tokens) of a chunk puts page g of the
 // chunk in MFMA rows 4g..4g+3 at tokens 4tt..4tt+3, so lane group g ends up
@@ -729,8 +730,8 @@ __device__ __forceinline__ void load_split_q(const Params& a, int p, int kvh, bo
 // two 16-byte LDS reads, the d-major page layout as stored in HBM.
 //
 // The running max only moves to whole numbers, so every rescale is an exact
-// power of two: pending weights shift their block exponent, and the output
-// accumulator is rescaled once per step, before that step's PV MFMAs.
+// power of two; the running sum and the output accumulator are rescaled once
+// per step, before that step's PV MFMAs.
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
