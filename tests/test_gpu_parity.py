@@ -482,6 +482,31 @@ def test_five_and_six_row_tiles(case, force):
     check(w, o, l, *oracle.attention(w))
 
 
+# Row-tile counts T that change which waves issue the loads: the e4m3 sweep
+# deals them to the 8 - T waves without a row tile (all eight when T >= 7), the
+# MXFP4 sweep spares waves 4 and 5 only when T is 5 or 6.
+ISSUER_CASES = [
+    ("fp8", dict(P=2, Hq=6, Hkv=1, D=256, ctx=(900, 33), W=1, causal=True)),       # T = 1
+    ("fp8", dict(P=2, Hq=16, Hkv=4, D=128, ctx=(1300, 700), W=9, causal=False)),   # T = 3
+    ("fp8", dict(P=2, Hq=8, Hkv=2, D=64, ctx=(2000, 150), W=16, causal=True)),     # T = 4
+    ("fp8", dict(P=2, Hq=16, Hkv=2, D=256, ctx=(400, 1800), W=14, causal=True)),   # T = 7
+    ("mxfp4", dict(P=2, Hq=24, Hkv=4, D=256, ctx=(1500, 61), W=4, causal=True)),   # T = 2
+    ("mxfp4", dict(P=2, Hq=16, Hkv=2, D=128, ctx=(700, 1900), W=14, causal=False)),  # T = 7
+]
+
+
+@pytest.mark.parametrize("case", range(len(ISSUER_CASES)))
+@pytest.mark.parametrize("force", [0, 5])
+def test_row_tile_counts_that_change_the_load_issuers(case, force):
+    kv, spec = ISSUER_CASES[case]
+    npg = sum(-(-(c + spec["W"]) // 16) for c in spec["ctx"])
+    w = make_workload(None, kv=kv, placement="permuted", pool_pages=npg + 9,
+                      seed=760 + case, **spec)
+    announce(f"{kv} load issuers, T = {-(-w.W * w.G // 16)}, {spec} force={force}")
+    o, l = gpu_run(w, force_splits=force)
+    check(w, o, l, *oracle.attention(w))
+
+
 def test_mxfp4_poison_and_determinism():
     kw = dict(P=2, Hq=24, Hkv=4, D=256, ctx=(501, 77), W=16, causal=True, kv="mxfp4",
               placement="permuted", pool_pages=60, seed=64)
