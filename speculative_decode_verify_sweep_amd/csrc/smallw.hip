@@ -1194,7 +1194,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep8_kernel(Params a) {
 // block b, row d = 16 dt + m.
 // ----------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool SPARE>
 __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     static_assert(D == 128 || D == 256, "MXFP4 serves D = 128 and 256");
     constexpr int KS4 = D / 128;               // 128-deep k-steps of the scores
@@ -1208,7 +1208,7 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     constexpr int NR = 4;                      // ring slots: two steps
     constexpr int N16 = CHB / 16;              // 16-byte pieces of a chunk
     constexpr int NI = (N16 + 63) / 64;        // DMA instructions per chunk
-    constexpr int MI = (2 * NI + 5) / 6;       // per issuing wave and step, at most
+    constexpr int MI = SPARE ? 1 : (2 * NI + kSweepWaves - 1) / kSweepWaves;  // per wave and step
     constexpr int BLK = 64 * D;                // staging bytes of one 32-token block
     constexpr int NDEC = 8 * D / kSweepThreads;  // decode items per thread and step
     // score tiles whose K operands are read together, (block, d tile) PV
@@ -1254,26 +1254,27 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
-    // ---- DMA work.  The issuing waves take the instructions I = e + NF m of a
-    // step's 2 NI, issuer e of NF, I = NI c + i being instruction i of the
-    // step's chunk c.  With five or six row tiles the issuers are every wave
-    // but the second row-tile waves of SIMDs 0 and 1 (waves 4 and 5), which
-    // carry the longest chain of each step; otherwise all eight.  (Measured at
-    // 64K W = 16: those waves spent about a sixth of each step issuing; the
-    // call went from 53.9 to 51.9 us.  Leaving every load to the waves without
-    // a row tile was slower here: the gathered K instructions of one wave
-    // then queue behind each other.)  Lane l of
+    // ---- DMA work.  Instruction i of a chunk (NI of them) moves pieces
+    // q = 64 i + l: K codes (placed operand-major, gathered from the chunk's
+    // four pages), then V^T codes, then K and V scales.
+    // SPARE (five or six row tiles, chosen at launch): the V^T code
+    // instructions come from waves 0..3, the K code and scale instructions
+    // from the waves without a row tile, and none from the second row-tile
+    // waves of SIMDs 0 and 1 (waves 4 and 5), whose chain is each step's
+    // longest.  Per-wave timestamps at 64K W = 16 showed every issuing wave
+    // spending 1500-2000 cycles of a ~9000-cycle step on its loads, most of it
+    // on the gathered K instructions; the waves without a row tile have that
+    // time to spare, the V^T copies are cheap.  64K W = 16: 53.9 -> 49.7 us.
+    // Otherwise every wave issues the instructions I = w + 8 m of a step's
+    // 2 NI, I = NI c + i being instruction i of the step's chunk c.  Lane l of
     // instruction i moves piece q = 64 i + l of the chunk; its source array
     // (0 K codes, 1 V^T codes, 2 K scales, 3 V scales), page of the chunk and
     // byte offset in that page-head are packed as off | pg << 12 | arr << 14,
     // bit 16 set for a piece inside the chunk.
-    const bool spare45 = T == 5 || T == 6;
-    const int NF = spare45 ? 12 - T : kSweepWaves;
-    const int e_iss = !spare45 ? w : (w < 4 ? w : (w >= T ? w - T + 4 : -1));  // -1: no loads
     uint32_t dsc[MI];
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
-        const int q = 64 * ((max(e_iss, 0) + NF * m) % NI) + l;
+        const int q = 64 * ((w + kSweepWaves * m) % NI) + l;
         int arr = 0, pg = 0, off = 0;
         if (q < 2 * D) {  // block (tt, k) = q >> 6, piece 16g + m = q & 63
             const int tt = (q >> 6) / KS4, k = (q >> 6) % KS4, gg = (q >> 4) & 3, m = q & 15;
@@ -1306,22 +1307,88 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
 
     // loads of step j: chunks 2j and 2j + 1, those that exist; pages past the
     // unit's end are replaced by the chunk's first page and masked later.
-    // Every page id is read first: a DMA statement carries a memory clobber,
-    // so an LDS read placed between two of them would make the second wait
-    // for the first's page id to arrive.
+    // SPARE: chunk c's K code and scale instructions are dealt over the 8 - T
+    // waves without a row tile, its V^T code instructions over waves 0..3;
+    // the four page ids of a chunk are read once, and each lane selects its
+    // page (the K pieces of one instruction come from all four pages).
+    auto issue_spare = [&](int j) {
+        const bool kiss = w >= T;
+        if (!kiss && w >= 4) return;
+        const int nk = 8 - T, ek = w - T;
+        constexpr int NKI = 2 * D / 64, NVI = 2 * D / 64, NSI = NI - NKI - NVI;
+        const int mm = l & 15, gg = (l >> 4) & 3;
+        const int lrow = 8 * (mm >> 2) + (mm & 3);
+#pragma unroll 1
+        for (int c = 0; c < 2; ++c) {
+            const int t = 2 * j + c;
+            if (t >= nchunks) break;
+            int pid[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int n = 4 * t + k < npages ? 4 * t + k : 4 * t;
+                pid[k] = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
+            }
+            const uint32_t slot = ring_base + uint32_t((t % NR) * CHB);
+            if (kiss) {
+#pragma unroll
+                for (int idx = 0; idx < NKI + NSI; ++idx) {
+                    const int n = c * (NKI + NSI) + idx;
+                    if (n % nk != ek) continue;
+                    if (idx < NKI) {
+                        const int tt = idx / KS4, k = idx % KS4;
+                        const int row = 32 * (tt >> 1) + 4 * (tt & 1) + lrow;
+                        const int pg = row >> 4;
+                        const int off = (row & 15) * (D / 2) + 16 * (4 * k + gg);
+                        const int phys = pg == 0 ? pid[0] : pg == 1 ? pid[1] : pg == 2 ? pid[2] : pid[3];
+                        const uint64_t src = kcb + uint64_t(int64_t(phys) * a.Hkv + kvh) * PGB + off;
+                        dma16(reinterpret_cast<const void*>(src),
+                              __builtin_amdgcn_readfirstlane(slot + 1024u * uint32_t(idx)));
+                    } else {
+                        const int i = NKI + NVI + (idx - NKI);
+                        const int q = 64 * i + l;
+                        const int o = 16 * (q - 4 * D);
+                        const int pg = (o % (4 * SPB)) / SPB;
+                        const int off = o % SPB;
+                        const int phys = pg == 0 ? pid[0] : pg == 1 ? pid[1] : pg == 2 ? pid[2] : pid[3];
+                        const uint64_t src = ksb + (o >= 4 * SPB ? vsd : 0) +
+                                             uint64_t(int64_t(phys) * a.Hkv + kvh) * SPB + off;
+                        if (q < N16)
+                            dma16(reinterpret_cast<const void*>(src),
+                                  __builtin_amdgcn_readfirstlane(slot + 1024u * uint32_t(i)));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int iv = 0; iv < NVI; ++iv) {
+                    if (((c * NVI + iv) & 3) != w) continue;
+                    const int pg = (1024 * iv) / PGB;
+                    const int off = (1024 * iv) % PGB + 16 * l;
+                    const uint64_t src = kcb + vcd + uint64_t(int64_t(pid[pg]) * a.Hkv + kvh) * PGB + off;
+                    dma16(reinterpret_cast<const void*>(src),
+                          __builtin_amdgcn_readfirstlane(slot + 1024u * uint32_t(NKI + iv)));
+                }
+            }
+        }
+    };
+    // otherwise: every page id of this wave's instructions is read first (a DMA
+    // statement carries a memory clobber, so an LDS read placed between two of
+    // them would make the second wait for the first's page id to arrive)
     auto issue_step = [&](int j) {
-        if (e_iss < 0) return;
+        if constexpr (SPARE) {
+            issue_spare(j);
+            return;
+        }
         int phys[MI];
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
-            const int t = 2 * j + (e_iss + NF * m) / NI;
+            const int t = 2 * j + (w + kSweepWaves * m) / NI;
             int n = 4 * t + (int(dsc[m] >> 12) & 3);
             if (n >= npages) n = 4 * t;
             phys[m] = ptab[min(max(n - tbase, 0), kPtab - 1)];
         }
 #pragma unroll
         for (int m = 0; m < MI; ++m) {
-            const int I = e_iss + NF * m;
+            const int I = w + kSweepWaves * m;
             if (I >= 2 * NI) break;  // wave-uniform
             const int c = I / NI, i = I % NI;
             const int t = 2 * j + c;
@@ -1925,8 +1992,14 @@ int launch_sweep(const smallw_plan* pl, const Params& a, hipStream_t st, void* e
     if (pl->prob.kv_dtype == SMALLW_KV_MXFP4) {
         if constexpr (D == 64) return SMALLW_EUNSUPPORTED;  // the planner rejects it first
         else
-            return launch(sweep4_kernel<D>, pl->U, kSweepThreads, a, st, ev0, ev1,
+        {
+            const int T = (pl->R + 15) / 16;
+            if (T == 5 || T == 6)
+                return launch(sweep4_kernel<D, true>, pl->U, kSweepThreads, a, st, ev0, ev1,
+                              "sweep kernel launch");
+            return launch(sweep4_kernel<D, false>, pl->U, kSweepThreads, a, st, ev0, ev1,
                           "sweep kernel launch");
+        }
     }
     if (pl->prob.v_layout == SMALLW_V_TOKEN_MAJOR)
         return launch(sweep_kernel<D, 4, true>, pl->U, kSweepThreads, a, st,
