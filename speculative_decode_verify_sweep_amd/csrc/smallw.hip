@@ -229,6 +229,12 @@ __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_addr) {
                  : "memory");
 }
 
+// The value among p0..p3 that a per-lane index k in [0, 4) selects (selects,
+// not an indexed array, which the compiler would put in private memory).
+__device__ __forceinline__ int pick4(int k, int p0, int p1, int p2, int p3) {
+    return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3;
+}
+
 // s_waitcnt vmcnt(n) for a run-time n in [0, 24]
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     switch (n) {
@@ -1312,8 +1318,8 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
     // the four page ids of a chunk are read once, and each lane selects its
     // page (the K pieces of one instruction come from all four pages).
     auto issue_spare = [&](int j) {
-        const bool kiss = w >= T;
-        if (!kiss && w >= 4) return;
+        const bool k_issuer = w >= T;  // a wave without a row tile
+        if (!k_issuer && w >= 4) return;
         const int nk = 8 - T, ek = w - T;
         constexpr int NKI = 2 * D / 64, NVI = 2 * D / 64, NSI = NI - NKI - NVI;
         const int mm = l & 15, gg = (l >> 4) & 3;
@@ -1329,29 +1335,26 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
                 pid[k] = __builtin_amdgcn_readfirstlane(ptab[n - tbase]);
             }
             const uint32_t slot = ring_base + uint32_t((t % NR) * CHB);
-            if (kiss) {
+            if (k_issuer) {
 #pragma unroll
                 for (int idx = 0; idx < NKI + NSI; ++idx) {
                     const int n = c * (NKI + NSI) + idx;
                     if (n % nk != ek) continue;
-                    if (idx < NKI) {
+                    if (idx < NKI) {  // K codes: operand block (tt, k)
                         const int tt = idx / KS4, k = idx % KS4;
                         const int row = 32 * (tt >> 1) + 4 * (tt & 1) + lrow;
-                        const int pg = row >> 4;
                         const int off = (row & 15) * (D / 2) + 16 * (4 * k + gg);
-                        const int phys = pg == 0 ? pid[0] : pg == 1 ? pid[1] : pg == 2 ? pid[2] : pid[3];
-                        const uint64_t src = kcb + uint64_t(int64_t(phys) * a.Hkv + kvh) * PGB + off;
+                        const int ph = pick4(row >> 4, pid[0], pid[1], pid[2], pid[3]);
+                        const uint64_t src = kcb + uint64_t(int64_t(ph) * a.Hkv + kvh) * PGB + off;
                         dma16(reinterpret_cast<const void*>(src),
                               __builtin_amdgcn_readfirstlane(slot + 1024u * uint32_t(idx)));
-                    } else {
+                    } else {  // K scales, then V scales
                         const int i = NKI + NVI + (idx - NKI);
                         const int q = 64 * i + l;
                         const int o = 16 * (q - 4 * D);
-                        const int pg = (o % (4 * SPB)) / SPB;
-                        const int off = o % SPB;
-                        const int phys = pg == 0 ? pid[0] : pg == 1 ? pid[1] : pg == 2 ? pid[2] : pid[3];
+                        const int ph = pick4((o % (4 * SPB)) / SPB, pid[0], pid[1], pid[2], pid[3]);
                         const uint64_t src = ksb + (o >= 4 * SPB ? vsd : 0) +
-                                             uint64_t(int64_t(phys) * a.Hkv + kvh) * SPB + off;
+                                             uint64_t(int64_t(ph) * a.Hkv + kvh) * SPB + o % SPB;
                         if (q < N16)
                             dma16(reinterpret_cast<const void*>(src),
                                   __builtin_amdgcn_readfirstlane(slot + 1024u * uint32_t(i)));
@@ -1359,11 +1362,11 @@ __global__ __launch_bounds__(kSweepThreads, 1) void sweep4_kernel(Params a) {
                 }
             } else {
 #pragma unroll
-                for (int iv = 0; iv < NVI; ++iv) {
+                for (int iv = 0; iv < NVI; ++iv) {  // V^T codes, 1 KiB of one page each
                     if (((c * NVI + iv) & 3) != w) continue;
                     const int pg = (1024 * iv) / PGB;
-                    const int off = (1024 * iv) % PGB + 16 * l;
-                    const uint64_t src = kcb + vcd + uint64_t(int64_t(pid[pg]) * a.Hkv + kvh) * PGB + off;
+                    const uint64_t src = kcb + vcd + uint64_t(int64_t(pid[pg]) * a.Hkv + kvh) * PGB +
+                                         (1024 * iv) % PGB + 16 * l;
                     dma16(reinterpret_cast<const void*>(src),
                           __builtin_amdgcn_readfirstlane(slot + 1024u * uint32_t(NKI + iv)));
                 }
