@@ -305,15 +305,16 @@ def _pages_read(w, force, split_pages):
     return read
 
 
-@pytest.mark.parametrize("force,split_pages", [(0, 0), (3, 0), (0, 8)])
-def test_table_check_counts_the_bad_entries_a_call_reads(force, split_pages):
+@pytest.mark.parametrize("kv,force,split_pages", [("bf16", 0, 0), ("bf16", 3, 0), ("bf16", 0, 8),
+                                                  ("fp8", 0, 8), ("mxfp4", 0, 8), ("mxfp4", 0, 0)])
+def test_table_check_counts_the_bad_entries_a_call_reads(kv, force, split_pages):
     """small_w_attention_check_pages counts, per request, the block-table entries
     outside the pool among the pages the call reads (the oracle planner's unit
     ranges), and flags device lengths outside the rules with -1.  Entries the call
     does not read (past the last page, below the window's first page) are not
     counted, and changing them leaves the outputs bitwise unchanged."""
     w = make_workload(None, P=4, Hq=8, Hkv=2, D=128, ctx=(700, 1500, 40, 333), W=8,
-                      causal=True, kv="bf16", placement="permuted", pool_pages=200, seed=131,
+                      causal=True, kv=kv, placement="permuted", pool_pages=200, seed=131,
                       max_pages=120, window_left=600)
     plan = dv.plan_for(w, force_splits=force, split_pages=split_pages)
     read = _pages_read(w, force, split_pages)
@@ -335,7 +336,7 @@ def test_table_check_counts_the_bad_entries_a_call_reads(force, split_pages):
     dev_bt = torch.from_numpy(bt).cuda()
     dev_sl = torch.from_numpy(w.seq_lens).cuda()
     bad = torch.full((w.P,), -99, dtype=torch.int32, device="cuda")
-    announce(f"table check force={force} split_pages={split_pages}")
+    announce(f"table check {kv} force={force} split_pages={split_pages}")
     sw.small_w_attention_check_pages(plan, dev_bt, dev_sl, bad)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bad.cpu().numpy(), want)
